@@ -1,0 +1,226 @@
+// gdn_api.cpp -- the C ABI of libgdn.so (declared in include/gdn.h).
+//
+// Every entry point validates its arguments on the host first and returns a
+// status without touching the HIP runtime when they are invalid, so the
+// error paths are testable on a machine without a GPU. Valid calls enqueue
+// kernels on the caller's stream and return without synchronising.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "gdn_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool valid_dtype(int d) { return d == GDN_F32 || d == GDN_BF16; }
+size_t dsize(int d) { return d == GDN_BF16 ? 2 : 4; }
+
+// Shared checks of the two delta-rule entry points.
+int check_core(const char* fn, const void* q, const void* k, const void* v, int in_dtype, int64_t& qs,
+               int64_t& ks, int64_t& vs, const float* g, const float* beta, int n_seqs, int64_t T, int nk, int nv,
+               int dk, int dv, const void* o, int o_dtype) {
+  if (!valid_dtype(in_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: in_dtype %d is not f32/bf16", fn, in_dtype);
+  if (!valid_dtype(o_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: o_dtype %d is not f32/bf16", fn, o_dtype);
+  if (n_seqs <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: n_seqs must be >= 1 (got %d)", fn, n_seqs);
+  if (T < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: T_tot must be >= 0", fn);
+  if (nk <= 0 || nv <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: head counts must be positive", fn);
+  if (nv % nk != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: nv (%d) must be a multiple of nk (%d)", fn, nv, nk);
+  if (dk <= 0 || dv <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: head dims must be positive", fn);
+  if (dk != 128 || dv != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: only dk = dv = 128 is built (got %d, %d)", fn, dk, dv);
+  if (T > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: T_tot above 2^31-1", fn);
+  if (qs == 0) qs = static_cast<int64_t>(nk) * dk;
+  if (ks == 0) ks = static_cast<int64_t>(nk) * dk;
+  if (vs == 0) vs = static_cast<int64_t>(nv) * dv;
+  if (qs < static_cast<int64_t>(nk) * dk || ks < static_cast<int64_t>(nk) * dk || vs < static_cast<int64_t>(nv) * dv)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a token stride is smaller than one token's row", fn);
+  if (T > 0) {
+    if (!q || !k || !v || !g || !beta || !o)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, g, beta and o are required", fn);
+    if (qs % 8 || ks % 8 || vs % 8)
+      return fail(GDN_ERR_UNSUPPORTED, "%s: token strides must be multiples of 8 elements", fn);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+      return fail(GDN_ERR_UNSUPPORTED, "%s: q, k, v, o must be 16-byte aligned", fn);
+  }
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
+    case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH";
+    default: return "GDN_ERR_UNKNOWN";
+  }
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_gating(const void* a, const void* b, int ab_dtype, const float* A_log, const float* dt_bias, int64_t T_tot,
+               int nv, float* g, float* beta, void* stream) {
+  if (!valid_dtype(ab_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_gating: ab_dtype %d is not f32/bf16", ab_dtype);
+  if (T_tot < 0 || nv <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_gating: need T_tot >= 0 and nv > 0");
+  if (!A_log || !dt_bias) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_gating: A_log and dt_bias are required");
+  if (T_tot > 0 && (!a || !b || !g || !beta))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_gating: a, b, g and beta are required");
+  if (T_tot == 0) return ok();
+  return launched(gdn::launch_gating(a, b, ab_dtype == GDN_BF16, A_log, dt_bias, T_tot, nv, g, beta,
+                                     static_cast<hipStream_t>(stream)),
+                  "gdn_gating");
+}
+
+size_t gdn_chunk_fwd_workspace_size(int64_t T_tot, int n_seqs, int nk, int nv, int dk, int dv, int in_dtype) {
+  (void)nk; (void)dk; (void)dv; (void)in_dtype;
+  if (T_tot < 0 || n_seqs <= 0 || nv <= 0) return 0;
+  return gdn::chunk_workspace_bytes(T_tot, n_seqs, nv);
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype, int64_t q_tok_stride,
+                  int64_t k_tok_stride, int64_t v_tok_stride, const float* g, const float* beta,
+                  const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv, float scale,
+                  int qk_l2norm, const float* initial_state, float* final_state, void* o, int o_dtype,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_chunk_fwd";
+  int64_t qs = q_tok_stride, ks = k_tok_stride, vs = v_tok_stride;
+  const int st = check_core(fn, q, k, v, in_dtype, qs, ks, vs, g, beta, n_seqs, T_tot, nk, nv, dk, dv, o, o_dtype);
+  if (st != GDN_OK) return st;
+  if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
+  if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nv);
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
+  return launched(gdn::launch_chunk_fwd(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, g, beta, cu_seqlens, n_seqs, T_tot,
+                                        nk, nv, scale, qk_l2norm != 0, initial_state, final_state, o,
+                                        o_dtype == GDN_BF16, workspace, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype, int64_t q_tok_stride,
+                      int64_t k_tok_stride, int64_t v_tok_stride, const float* g, const float* beta,
+                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv,
+                      float scale, int qk_l2norm, float* state, void* o, int o_dtype, void* stream) {
+  const char* fn = "gdn_recurrent_fwd";
+  int64_t qs = q_tok_stride, ks = k_tok_stride, vs = v_tok_stride;
+  const int st = check_core(fn, q, k, v, in_dtype, qs, ks, vs, g, beta, n_seqs, T_tot, nk, nv, dk, dv, o, o_dtype);
+  if (st != GDN_OK) return st;
+  if (!state) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state is required", fn);
+  if (!aligned(state, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: state must be 16-byte aligned", fn);
+  if (!cu_seqlens && T_tot != n_seqs)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: without cu_seqlens T_tot must equal n_seqs (one token each)", fn);
+  if (static_cast<int64_t>(n_seqs) * nv > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: too many (seq, head) units", fn);
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
+  return launched(gdn::launch_recurrent(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, g, beta, cu_seqlens, n_seqs, T_tot, nk,
+                                        nv, scale, qk_l2norm != 0, state, o, o_dtype == GDN_BF16,
+                                        static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int gdn_causal_conv1d(const void* x, int dtype, int64_t x_tok_stride, const float* weight, const float* bias,
+                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int conv_dim, int K,
+                      const void* conv_state_in, void* conv_state_out, int state_len, int silu, void* y,
+                      void* stream) {
+  const char* fn = "gdn_causal_conv1d";
+  if (!valid_dtype(dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not f32/bf16", fn, dtype);
+  if (n_seqs <= 0 || T_tot < 0 || conv_dim <= 0 || K <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: need n_seqs >= 1, T_tot >= 0, conv_dim > 0, K > 0", fn);
+  if (state_len < K - 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_len (%d) < K - 1", fn, state_len);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: only K = 4 is built (got %d)", fn, K);
+  if (conv_dim % 8) return fail(GDN_ERR_UNSUPPORTED, "%s: conv_dim must be a multiple of 8", fn);
+  if (T_tot > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: T_tot above 2^31-1", fn);
+  if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
+  if (!weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: weight is required", fn);
+  if (x_tok_stride == 0) x_tok_stride = conv_dim;
+  if (x_tok_stride < conv_dim) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x token stride smaller than conv_dim", fn);
+  if (T_tot > 0) {
+    if (!x || !y) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x and y are required", fn);
+    if (x_tok_stride % 8) return fail(GDN_ERR_UNSUPPORTED, "%s: x token stride must be a multiple of 8", fn);
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: x and y must be 16-byte aligned", fn);
+  }
+  if (conv_state_in && conv_state_out) {
+    const size_t bytes = static_cast<size_t>(n_seqs) * conv_dim * state_len * dsize(dtype);
+    const char* a0 = static_cast<const char*>(conv_state_in);
+    const char* b0 = static_cast<const char*>(conv_state_out);
+    if (a0 < b0 + bytes && b0 < a0 + bytes)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: conv_state_out must not overlap conv_state_in", fn);
+  }
+  return launched(gdn::launch_causal_conv1d(x, dtype == GDN_BF16, x_tok_stride, weight, bias, cu_seqlens, n_seqs,
+                                            T_tot, conv_dim, conv_state_in, conv_state_out, state_len, silu != 0, y,
+                                            static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int gdn_causal_conv1d_update(const void* x, int dtype, void* conv_state, int state_len, const float* weight,
+                             const float* bias, int n_seqs, int conv_dim, int K, int silu, void* y, void* stream) {
+  const char* fn = "gdn_causal_conv1d_update";
+  if (!valid_dtype(dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not f32/bf16", fn, dtype);
+  if (n_seqs < 0 || conv_dim <= 0 || K <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: need n_seqs >= 0, conv_dim > 0, K > 0", fn);
+  if (state_len < K - 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_len (%d) < K - 1", fn, state_len);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: only K = 4 is built (got %d)", fn, K);
+  if (!weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: weight is required", fn);
+  if (n_seqs == 0) return ok();
+  if (!x || !conv_state || !y) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, conv_state and y are required", fn);
+  return launched(gdn::launch_causal_conv1d_update(x, dtype == GDN_BF16, conv_state, state_len, weight, bias, n_seqs,
+                                                   conv_dim, silu != 0, y, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int gdn_gated_rmsnorm(const void* x, int x_dtype, const void* z, int z_dtype, const float* weight, int64_t rows,
+                      int D, float eps, void* y, int y_dtype, void* stream) {
+  const char* fn = "gdn_gated_rmsnorm";
+  if (!valid_dtype(x_dtype) || !valid_dtype(z_dtype) || !valid_dtype(y_dtype))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dtypes must be f32/bf16", fn);
+  if (rows < 0 || D <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: need rows >= 0 and D > 0", fn);
+  if (!(eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: eps must be >= 0", fn);
+  if (D % 4 || D > 4096) return fail(GDN_ERR_UNSUPPORTED, "%s: D must be a multiple of 4 and <= 4096", fn);
+  if (!weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: weight is required", fn);
+  if (rows == 0) return ok();
+  if (!x || !z || !y) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, z and y are required", fn);
+  if (rows > static_cast<int64_t>(UINT32_MAX) * 8) return fail(GDN_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  return launched(gdn::launch_gated_rmsnorm(x, x_dtype == GDN_BF16, z, z_dtype == GDN_BF16, weight, rows, D, eps, y,
+                                            y_dtype == GDN_BF16, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+}  // extern "C"

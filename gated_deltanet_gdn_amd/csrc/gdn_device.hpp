@@ -1,0 +1,150 @@
+// gdn_device.hpp -- device helpers shared by the gfx950 kernels of libgdn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+// bf16 is stored as raw 16-bit words in global memory. Widening is exact;
+// narrowing rounds to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ static __forceinline__ void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32) as fp32.
+__device__ __forceinline__ void load8(const uint16_t* p, float (&out)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&out)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+// log(1 + e^s) without overflow: max(s, 0) + log1p(e^{-|s|}).
+__device__ __forceinline__ float softplusf_(float s) { return fmaxf(s, 0.0f) + log1pf(expf(-fabsf(s))); }
+__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
+
+// ---------------------------------------------------------------- wave helpers (wave64)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- MFMA fragments
+// v_mfma_f32_16x16x32_bf16 (gfx950): per lane, A holds 8 bf16 of one row
+// (row = lane % 16, k-slots 8*(lane/16) .. +7), B holds 8 bf16 of one column
+// (col = lane % 16, same k-slots), D holds 4 fp32 (rows 4*(lane/16) + i,
+// col = lane % 16). v_mfma_f32_16x16x4_f32 uses the same row/col mapping with
+// one k-slot per lane (k = lane / 16).
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&v)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(v[i]);
+  return r;
+}
+// x = hi + lo + O(2^-17 |x|): hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = static_cast<__bf16>(v[i]);
+    hi[i] = h;
+    lo[i] = static_cast<__bf16>(v[i] - static_cast<float>(h));
+  }
+}
+
+// Accumulate A(16 x KS) * B(KS x 16) for one k-step, given per-lane operand
+// values (KPL = 8 slots for bf16 MFMA, 1 slot for fp32 MFMA). EXACT_A / EXACT_B
+// say whether that operand's values are exactly representable in bf16 (raw bf16
+// inputs); other operands are split into hi + lo, giving 1, 2 or 3 MFMA passes.
+template <bool BF16, bool EXACT_A, bool EXACT_B> struct Mma;
+
+template <bool EA, bool EB> struct Mma<false, EA, EB> {
+  static constexpr int KS = 4, KPL = 1;
+  __device__ static __forceinline__ void run(f32x4& acc, const float (&a)[1], const float (&b)[1]) {
+    acc = mfma_f32(a[0], b[0], acc);
+  }
+};
+template <bool EA, bool EB> struct Mma<true, EA, EB> {
+  static constexpr int KS = 32, KPL = 8;
+  __device__ static __forceinline__ void run(f32x4& acc, const float (&a)[8], const float (&b)[8]) {
+    if constexpr (EA && EB) {
+      acc = mfma_bf16(to_bf16x8(a), to_bf16x8(b), acc);
+    } else if constexpr (EA) {
+      bf16x8 bh, bl;
+      split_bf16x8(b, bh, bl);
+      const bf16x8 aa = to_bf16x8(a);
+      acc = mfma_bf16(aa, bl, acc);
+      acc = mfma_bf16(aa, bh, acc);
+    } else if constexpr (EB) {
+      bf16x8 ah, al;
+      split_bf16x8(a, ah, al);
+      const bf16x8 bb = to_bf16x8(b);
+      acc = mfma_bf16(al, bb, acc);
+      acc = mfma_bf16(ah, bb, acc);
+    } else {
+      bf16x8 ah, al, bh, bl;
+      split_bf16x8(a, ah, al);
+      split_bf16x8(b, bh, bl);
+      acc = mfma_bf16(al, bh, acc);
+      acc = mfma_bf16(ah, bl, acc);
+      acc = mfma_bf16(ah, bh, acc);
+    }
+  }
+};
+
+// ---------------------------------------------------------------- packed sequences
+// Token range [b, e) of sequence n, clamped into [0, T] so that a malformed
+// cu_seqlens can give wrong results but never an out-of-range token index.
+// cu == nullptr means one sequence of T tokens.
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int64_t T, int64_t& b, int64_t& e) {
+  if (!cu) { b = 0; e = T; return; }
+  b = min(max(static_cast<int64_t>(cu[n]), int64_t(0)), T);
+  e = min(max(static_cast<int64_t>(cu[n + 1]), b), T);
+}
+
+// ---------------------------------------------------------------- XCD-aware block order
+// Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
+// Remap so that logically consecutive work items land on the same XCD and
+// share its L2. Identity when the grid is not a multiple of 8.
+__device__ __forceinline__ int xcd_swizzle(int b, int nblocks) {
+  if (nblocks % 8 != 0) return b;
+  const int per = nblocks / 8;
+  return (b % 8) * per + b / 8;
+}
+
+}  // namespace gdn

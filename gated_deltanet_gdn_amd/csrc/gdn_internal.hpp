@@ -1,0 +1,43 @@
+// gdn_internal.hpp -- launchers shared between the C-ABI layer and the kernel files.
+// All arguments have been validated by the caller (gdn_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+hipError_t launch_gating(const void* a, const void* b, int bf16, const float* A_log,
+                         const float* dt_bias, int64_t T, int nv, float* g, float* beta,
+                         hipStream_t s);
+
+hipError_t launch_gated_rmsnorm(const void* x, int x_bf16, const void* z, int z_bf16,
+                                const float* w, int64_t rows, int D, float eps, void* y,
+                                int y_bf16, hipStream_t s);
+
+hipError_t launch_causal_conv1d(const void* x, int bf16, int64_t x_stride, const float* w,
+                                const float* bias, const int32_t* cu, int n_seqs, int64_t T,
+                                int C, const void* st_in, void* st_out, int state_len, int silu,
+                                void* y, hipStream_t s);
+
+hipError_t launch_causal_conv1d_update(const void* x, int bf16, void* state, int state_len,
+                                       const float* w, const float* bias, int n_seqs, int C,
+                                       int silu, void* y, hipStream_t s);
+
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf16,
+                            int64_t qs, int64_t ks, int64_t vs, const float* g, const float* beta,
+                            const int32_t* cu, int n_seqs, int64_t T, int nk, int nv, float scale, int l2,
+                            float* state, void* o, int o_bf16, hipStream_t s);
+
+// Chunked path. The workspace holds, per chunk and value head, the packed
+// 64x64 tile [T strictly lower | P^T on and above the diagonal] and the
+// per-token scalars; see k_chunk.hip.
+size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nv);
+hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf16,
+                            int64_t qs, int64_t ks, int64_t vs, const float* g, const float* beta,
+                            const int32_t* cu, int n_seqs, int64_t T, int nk, int nv, float scale,
+                            int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
+                            hipStream_t s);
+
+}  // namespace gdn

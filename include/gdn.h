@@ -1,0 +1,189 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the Gated DeltaNet core for AMD MI355X (gfx950).
+ *
+ * The operations are those of a Gated DeltaNet token mixer as published in
+ * "Qwen3.5 Dense Model Architecture" (blog), section "Linear Attention"
+ * (mechanism list, minimal forward example, cache table) and in "Qwen3.5
+ * Simulation Support Design Document" (msmodeling RFC), sections 1.1, 2.2
+ * (decomposed op flow: causal conv / conv update, gating, chunk and recurrent
+ * gated delta rule, gated RMSNorm), 2.3 (chunk vs recurrent path selection)
+ * and 2.4 (conv body vs conv state update).
+ *
+ * General conventions (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer unless stated otherwise. The
+ *     caller allocates and owns every buffer, including workspaces; the
+ *     library never allocates, frees or synchronises on these paths.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream). Return value GDN_OK only means the work was enqueued.
+ *   - Arguments are validated on the host before any HIP call; a non-OK
+ *     return enqueues nothing and leaves outputs untouched. gdn_last_error()
+ *     then describes the failure (thread-local string).
+ *   - Data-dependent preconditions that the host cannot see (cu_seqlens
+ *     monotone, starting at 0 and ending at T_tot; finite inputs; g within
+ *     [-1e4, 0]) are the caller's responsibility; violating them gives
+ *     unspecified output, never an out-of-bounds access of any buffer whose
+ *     documented size is respected.
+ *   - Layouts are row-major with the last index contiguous. A "token stride"
+ *     is the distance in elements between consecutive tokens (0 = dense),
+ *     which lets q/k/v be zero-copy views into a packed [T, conv_dim] tensor.
+ *   - dtype codes: GDN_F32 = 0, GDN_BF16 = 1. Parameters (A_log, dt_bias,
+ *     conv weight/bias, norm weight) are always fp32. Recurrent states are
+ *     always fp32; conv states use the activation dtype.
+ *   - Results are deterministic: the kernels use no atomics.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1, /* null required pointer, bad size, nv % nk != 0, ...   */
+  GDN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. dk != 128, K != 4)  */
+  GDN_ERR_WORKSPACE_TOO_SMALL = 3,
+  GDN_ERR_LAUNCH = 4            /* a HIP launch or runtime call failed                */
+};
+
+enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
+
+int gdn_abi_version(void);
+const char* gdn_status_string(int status);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* gdn_last_error(void);
+
+/*
+ * Gating ("Qwen3.5 Dense Model Architecture", Linear Attention, the beta and g
+ * lines of the minimal example; computed in fp32 as the page notes, to keep
+ * A_log from overflowing in low precision):
+ *   beta[t,h] = sigmoid(b[t,h])
+ *   g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ * a, b : [T_tot, nv] of ab_dtype, dense.  A_log, dt_bias : [nv] fp32.
+ * g, beta : [T_tot, nv] fp32 outputs.  T_tot = 0 is a no-op.
+ */
+int gdn_gating(const void* a, const void* b, int ab_dtype,
+               const float* A_log, const float* dt_bias,
+               int64_t T_tot, int nv, float* g, float* beta, void* stream);
+
+/*
+ * Chunked gated delta rule, the prefill path ("Qwen3.5 Simulation Support
+ * Design Document", 2.2 op 4 and Appendix B: the sequence is split into
+ * chunks of 64 for intra-chunk attention plus an inter-chunk recurrence;
+ * "Qwen3.5 Dense Model Architecture", Linear Attention: prefill calls the
+ * chunk kernel and writes the final state back to the cache).
+ *
+ * Per packed sequence n (tokens [cu[n], cu[n+1])) and value head h, with key
+ * head hk = h / (nv / nk) (repeat_interleave), the result equals the token
+ * recurrence
+ *   qh = q[t,hk] / sqrt(|q|^2 + 1e-6) * scale,  kh = k[t,hk] / sqrt(|k|^2 + 1e-6)
+ *   S <- exp(g[t,h]) S ;  S <- S + beta[t,h] kh (v[t,h] - S^T kh)^T ;  o[t,h] = S^T qh
+ * (the L2 norms are skipped when qk_l2norm == 0), evaluated chunk-parallel.
+ *
+ *   q, k   : [T_tot, nk, dk] of in_dtype, token stride q_tok_stride / k_tok_stride
+ *   v      : [T_tot, nv, dv] of in_dtype, token stride v_tok_stride
+ *            (heads are contiguous inside a token in all three)
+ *   g, beta: [T_tot, nv] fp32 dense (gdn_gating output; g must lie in [-1e4, 0])
+ *   cu_seqlens : device int32 [n_seqs + 1], or NULL for one sequence of T_tot
+ *   scale  : <= 0 selects dk^-1/2
+ *   initial_state : [n_seqs, nv, dk, dv] fp32 or NULL (zero state)
+ *   final_state   : same shape, or NULL (not written); may alias initial_state
+ *   o      : [T_tot, nv, dv], o_dtype (fp32 recommended; bf16 rounds once)
+ *   workspace : device buffer of at least gdn_chunk_fwd_workspace_size(...) bytes,
+ *            256-byte aligned; its contents on entry are ignored.
+ * Supported: dk = dv = 128; in_dtype f32 or bf16; nv % nk == 0.
+ */
+size_t gdn_chunk_fwd_workspace_size(int64_t T_tot, int n_seqs, int nk, int nv,
+                                    int dk, int dv, int in_dtype);
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                  int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                  const float* g, const float* beta,
+                  const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                  int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                  const float* initial_state, float* final_state,
+                  void* o, int o_dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Recurrent gated delta rule, the decode path ("Qwen3.5 Simulation Support
+ * Design Document", 2.2 op 5 and 2.3: decode batches, including multi-token
+ * MTP decode, take the token-by-token path; "Qwen3.5 Dense Model
+ * Architecture", cache table: decode updates the recurrent state in place).
+ * Same recurrence and argument meaning as gdn_chunk_fwd, except:
+ *   cu_seqlens : device int32 [n_seqs + 1], or NULL for exactly one token per
+ *                sequence (then T_tot must equal n_seqs)
+ *   state      : [n_seqs, nv, dk, dv] fp32, read and then overwritten in place
+ *                with the state after each sequence's last token.
+ * Supported: dk = dv = 128; in_dtype f32 or bf16.
+ */
+int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                      int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                      const float* g, const float* beta,
+                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                      int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                      float* state, void* o, int o_dtype, void* stream);
+
+/*
+ * Causal depthwise conv1d with optional SiLU over packed sequences, the
+ * prefill conv body ("Qwen3.5 Simulation Support Design Document", 2.4;
+ * "Qwen3.5 Dense Model Architecture", Linear Attention: depthwise Conv1d of
+ * kernel size linear_conv_kernel_dim over the packed QKV, then SiLU; a cached
+ * conv state is prepended when present):
+ *   y[t,c] = act(bias[c] + sum_{j<K} w[c,j] * x[t-(K-1)+j, c])
+ * where inputs before a sequence's first token come from the last K-1 entries
+ * of conv_state_in[n,c,:] (zeros when conv_state_in is NULL).
+ *   x, y          : [T_tot, conv_dim] of dtype; x token stride x_tok_stride
+ *                   (0 = dense); y is dense
+ *   weight        : [conv_dim, K] fp32;  bias : [conv_dim] fp32 or NULL
+ *   conv_state_in : [n_seqs, conv_dim, state_len] of dtype, or NULL
+ *   conv_state_out: same shape or NULL: the last state_len entries of
+ *                   concat(conv_state_in[n,c,:] or zeros, x[seq n, c]).
+ *                   Must not overlap conv_state_in.
+ * Supported: K = 4, state_len >= K - 1, conv_dim % 8 == 0, dtype f32 or bf16.
+ */
+int gdn_causal_conv1d(const void* x, int dtype, int64_t x_tok_stride,
+                      const float* weight, const float* bias,
+                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                      int conv_dim, int K,
+                      const void* conv_state_in, void* conv_state_out, int state_len,
+                      int silu, void* y, void* stream);
+
+/*
+ * One decode step of the causal conv ("Qwen3.5 Simulation Support Design
+ * Document", 2.4 state update; "Qwen3.5 Dense Model Architecture", decode
+ * branch of the minimal example): window = [conv_state[n,c,-(K-1):], x[n,c]],
+ *   y[n,c] = act(bias[c] + sum_j w[c,j] window[j]),
+ * then conv_state[n,c,:] <- [conv_state[n,c,1:], x[n,c]] in place.
+ *   x, y : [n_seqs, conv_dim] of dtype, dense.
+ *   conv_state : [n_seqs, conv_dim, state_len] of dtype, updated in place.
+ * Supported: K = 4, state_len >= K - 1, dtype f32 or bf16.
+ */
+int gdn_causal_conv1d_update(const void* x, int dtype, void* conv_state, int state_len,
+                             const float* weight, const float* bias,
+                             int n_seqs, int conv_dim, int K, int silu,
+                             void* y, void* stream);
+
+/*
+ * Gated RMSNorm epilogue ("Qwen3.5 Simulation Support Design Document", 1.1
+ * and Appendix B: RMSNorm whose output is scaled by 1 + weight, with the
+ * SiLU(z) gate of 2.2 op 6; "Qwen3.5 Dense Model Architecture", minimal
+ * example: norm(core_output, z) over rows of Dv):
+ *   y[r,:] = x[r,:] * (mean(x[r,:]^2) + eps)^(-1/2) * (1 + weight) * z[r,:] * sigmoid(z[r,:])
+ *   x : [rows, D] of x_dtype;  z : [rows, D] of z_dtype;  weight : [D] fp32;
+ *   y : [rows, D] of y_dtype. All dense.
+ * Supported: D % 4 == 0 and D <= 4096.
+ */
+int gdn_gated_rmsnorm(const void* x, int x_dtype, const void* z, int z_dtype,
+                      const float* weight, int64_t rows, int D, float eps,
+                      void* y, int y_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,182 @@
+"""C-ABI contract of libgdn.so, checked without a GPU.
+
+Every argument error is detected on the host before any HIP call, so these
+tests pass arbitrary non-null "device" addresses and expect the documented
+status. No compute entry point is called with valid arguments here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_gdn_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, LAUNCH = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(0x100000)      # a fake, 256-byte aligned "device" address (never dereferenced)
+P2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100002)    # misaligned
+NULL = None
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return gdn.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert "gdn_chunk_fwd" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"libgdn.so does not export {n}"
+
+
+def test_version_and_status_strings(L):
+    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_status_string(OK) == "GDN_OK"
+    assert gdn.gdn_status_string(INVALID) == "GDN_ERR_INVALID_ARGUMENT"
+    assert gdn.gdn_status_string(UNSUPPORTED) == "GDN_ERR_UNSUPPORTED"
+    assert gdn.gdn_status_string(WS_SMALL) == "GDN_ERR_WORKSPACE_TOO_SMALL"
+    assert gdn.gdn_status_string(LAUNCH) == "GDN_ERR_LAUNCH"
+    assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
+
+
+def _chunk(L, **kw):
+    a = dict(q=P, k=P, v=P, in_dtype=1, qs=0, ks=0, vs=0, g=P, beta=P, cu=NULL, n=1, T=256, nk=1, nv=2, dk=128,
+             dv=128, scale=0.0, l2=1, s0=NULL, st=NULL, o=P, o_dtype=0, ws=P2, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return L.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["qs"], a["ks"], a["vs"], a["g"], a["beta"],
+                           a["cu"], a["n"], a["T"], a["nk"], a["nv"], a["dk"], a["dv"], a["scale"], a["l2"],
+                           a["s0"], a["st"], a["o"], a["o_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nk=3, nv=4), INVALID),            # nv % nk != 0 (the pages' head-divisibility error)
+    (dict(nk=0), INVALID),
+    (dict(n=0), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(in_dtype=7), INVALID),
+    (dict(o_dtype=5), INVALID),
+    (dict(q=NULL), INVALID),
+    (dict(beta=NULL), INVALID),
+    (dict(o=NULL), INVALID),
+    (dict(n=2), INVALID),                   # several sequences need cu_seqlens
+    (dict(qs=100), INVALID),                # token stride smaller than a row (nk*dk = 128)
+    (dict(ws=NULL), INVALID),
+    (dict(ws=MIS), INVALID),
+    (dict(ws_bytes=16), WS_SMALL),
+    (dict(dk=64), UNSUPPORTED),
+    (dict(dv=256), UNSUPPORTED),
+    (dict(qs=132), UNSUPPORTED),            # not a multiple of 8 elements
+    (dict(q=MIS), UNSUPPORTED),
+    (dict(T=1 << 32), UNSUPPORTED),
+])
+def test_chunk_fwd_argument_errors(L, kw, status):
+    assert _chunk(L, **kw) == status
+    assert gdn.gdn_last_error().startswith("gdn_chunk_fwd")
+
+
+def test_workspace_size_is_monotone_and_positive(L):
+    s1 = gdn.gdn_chunk_fwd_workspace_size(8192, 1, 16, 32)
+    s2 = gdn.gdn_chunk_fwd_workspace_size(8192 + 64, 1, 16, 32)
+    s3 = gdn.gdn_chunk_fwd_workspace_size(8192, 8, 16, 32)
+    assert 0 < s1 < s2 and s1 < s3
+    assert s1 % 256 == 0
+    # per chunk and value head: a 64x64 fp32 tile, 64 float4 scalars, one float
+    assert s1 >= (8192 // 64) * 32 * (64 * 64 * 4 + 64 * 16 + 4)
+    assert gdn.gdn_chunk_fwd_workspace_size(-1, 1, 16, 32) == 0
+
+
+def _rec(L, **kw):
+    a = dict(q=P, k=P, v=P, in_dtype=1, qs=0, ks=0, vs=0, g=P, beta=P, cu=NULL, n=4, T=4, nk=2, nv=4, dk=128,
+             dv=128, scale=0.0, l2=1, state=P2, o=P, o_dtype=0, stream=NULL)
+    a.update(kw)
+    return L.gdn_recurrent_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["qs"], a["ks"], a["vs"], a["g"], a["beta"],
+                               a["cu"], a["n"], a["T"], a["nk"], a["nv"], a["dk"], a["dv"], a["scale"], a["l2"],
+                               a["state"], a["o"], a["o_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nk=3), INVALID),
+    (dict(state=NULL), INVALID),
+    (dict(T=5), INVALID),                   # one token per sequence without cu_seqlens
+    (dict(v=NULL), INVALID),
+    (dict(dk=96), UNSUPPORTED),
+    (dict(state=MIS), UNSUPPORTED),
+])
+def test_recurrent_fwd_argument_errors(L, kw, status):
+    assert _rec(L, **kw) == status
+
+
+def _conv(L, **kw):
+    a = dict(x=P, dtype=1, xs=0, w=P, b=NULL, cu=NULL, n=1, T=10, C=64, K=4, si=NULL, so=NULL, sl=3, silu=1, y=P2,
+             stream=NULL)
+    a.update(kw)
+    return L.gdn_causal_conv1d(a["x"], a["dtype"], a["xs"], a["w"], a["b"], a["cu"], a["n"], a["T"], a["C"], a["K"],
+                               a["si"], a["so"], a["sl"], a["silu"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sl=2), INVALID),                  # state_len < K - 1
+    (dict(K=0), INVALID),
+    (dict(n=2), INVALID),                   # missing cu_seqlens
+    (dict(w=NULL), INVALID),
+    (dict(x=NULL), INVALID),
+    (dict(xs=32), INVALID),                 # stride < conv_dim
+    (dict(si=P, so=ctypes.c_void_p(0x100000 + 64)), INVALID),   # overlapping states
+    (dict(K=3, sl=3), UNSUPPORTED),
+    (dict(C=60), UNSUPPORTED),
+    (dict(xs=68), UNSUPPORTED),
+    (dict(dtype=3), INVALID),
+])
+def test_causal_conv1d_argument_errors(L, kw, status):
+    assert _conv(L, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, 1, P2, 2, P, NULL, 4, 64, 4, 1, P, NULL), INVALID),      # state_len 2 < 3
+    ((P, 1, P2, 3, NULL, NULL, 4, 64, 4, 1, P, NULL), INVALID),   # no weight
+    ((NULL, 1, P2, 3, P, NULL, 4, 64, 4, 1, P, NULL), INVALID),   # no x
+    ((P, 1, P2, 3, P, NULL, 4, 64, 2, 1, P, NULL), UNSUPPORTED),  # K = 2
+    ((P, 1, P2, 3, P, NULL, 0, 64, 4, 1, P, NULL), OK),           # zero sequences: no-op, no HIP call
+])
+def test_conv_update_argument_errors(L, args, status):
+    assert L.gdn_causal_conv1d_update(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, 0, P, 1, P, 10, 130, 1e-6, P2, 0, NULL), UNSUPPORTED),   # D % 4
+    ((P, 0, P, 1, P, 10, 8192, 1e-6, P2, 0, NULL), UNSUPPORTED),  # D too large
+    ((P, 0, P, 1, NULL, 10, 128, 1e-6, P2, 0, NULL), INVALID),
+    ((P, 0, P, 1, P, 10, 128, -1.0, P2, 0, NULL), INVALID),
+    ((P, 2, P, 1, P, 10, 128, 1e-6, P2, 0, NULL), INVALID),
+    ((P, 0, P, 1, P, 0, 128, 1e-6, P2, 0, NULL), OK),            # zero rows: no-op
+])
+def test_gated_rmsnorm_argument_errors(L, args, status):
+    assert L.gdn_gated_rmsnorm(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, P, 1, P, P, 10, 0, P, P, NULL), INVALID),      # nv = 0
+    ((P, P, 1, NULL, P, 10, 4, P, P, NULL), INVALID),   # no A_log
+    ((P, NULL, 1, P, P, 10, 4, P, P, NULL), INVALID),
+    ((P, P, 9, P, P, 10, 4, P, P, NULL), INVALID),
+    ((NULL, NULL, 1, P, P, 0, 4, NULL, NULL, NULL), OK),  # T = 0: no-op
+])
+def test_gating_argument_errors(L, args, status):
+    assert L.gdn_gating(*args) == status
+
+
+def test_python_binding_requires_device_tensors():
+    import torch
+    x = torch.zeros(4, 2)
+    with pytest.raises(ValueError):
+        gdn.gdn_gating(x, x, torch.zeros(2), torch.zeros(2))

@@ -1,0 +1,292 @@
+"""GPU parity of every libgdn entry point against the fp64 CPU oracle (small inputs).
+
+Sizes span several 64-token chunks with ragged tails, several sequences
+(including empty and one-token ones), both input dtypes and grouped heads.
+Each test prints the case it runs before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_gdn_amd as gdn
+import oracle
+import workloads as W
+from gpu_common import TOL, assert_close, bf16_ulp_diff, dev, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _inputs(dtype, lengths, nk, nv, s0_std=0.0, seed=7):
+    wl = W.Workload("t", seed, "chunk", dtype, nk=nk, nv=nv, s0_std=s0_std)
+    return W.chunk_inputs(wl, lengths=lengths)
+
+
+def _to(d, device):
+    return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+# ------------------------------------------------------------------ gating
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gating(dtype):
+    _say("gating", dtype)
+    x = _inputs(dtype, [300], 2, 6)
+    d = _to(x, dev())
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    # fp32 evaluation of exp / log1p / sigmoid: a few ulps of the result
+    np.testing.assert_allclose(f64(g), g_ref, rtol=4e-6, atol=0)
+    np.testing.assert_allclose(f64(beta), b_ref, rtol=4e-6, atol=0)
+
+
+def test_gating_odd_head_count():
+    _say("gating nv=3")
+    x = _inputs("bf16", [77], 1, 3)
+    d = _to(x, dev())
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    np.testing.assert_allclose(f64(g), g_ref, rtol=4e-6)
+    np.testing.assert_allclose(f64(beta), b_ref, rtol=4e-6)
+
+
+# ------------------------------------------------------------------ gated RMSNorm
+
+@pytest.mark.parametrize("xd,zd,yd", [("f32", "f32", "f32"), ("f32", "bf16", "f32"), ("bf16", "bf16", "bf16")])
+def test_gated_rmsnorm(xd, zd, yd):
+    _say("rmsnorm", xd, zd, yd)
+    rows, D = 777, 128
+    x = W.randn((rows, D), 3, 1, xd)
+    z = W.randn((rows, D), 3, 2, zd)
+    w = W.randn((D,), 3, 3, "f32", std=0.1)
+    y = gdn.gdn_gated_rmsnorm(x.to(dev()), z.to(dev()), w.to(dev()), eps=1e-6, y_dtype=W.TORCH_DTYPE[yd])
+    ref = oracle.gated_rmsnorm(f64(x), f64(z), f64(w), eps=1e-6)
+    if yd == "f32":
+        assert_close(y, ref, 1e-6, "rmsnorm")
+    else:
+        assert int(bf16_ulp_diff(y, ref).max()) <= 1
+
+
+def test_gated_rmsnorm_wide_rows():
+    _say("rmsnorm D=512")
+    x = W.randn((33, 512), 4, 1); z = W.randn((33, 512), 4, 2); w = W.randn((512,), 4, 3, std=0.1)
+    y = gdn.gdn_gated_rmsnorm(x.to(dev()), z.to(dev()), w.to(dev()))
+    assert_close(y, oracle.gated_rmsnorm(f64(x), f64(z), f64(w)), 1e-6, "rmsnorm D=512")
+
+
+# ------------------------------------------------------------------ causal conv
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_causal_conv1d_varlen(dtype, with_state):
+    _say("conv", dtype, with_state)
+    lengths = [70, 0, 1, 130, 2, 200]
+    C, K, SL = 96, 4, 3
+    cu = W.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    x = W.randn((T, C), 5, 1, dtype)
+    w = W.uniform((C, K), 5, 2, -0.5, 0.5)
+    b = W.randn((C,), 5, 3, "f32")
+    st = W.randn((len(lengths), C, SL), 5, 4, dtype) if with_state else None
+    d = dev()
+    y, so = gdn.gdn_causal_conv1d(x.to(d), w.to(d), b.to(d), cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=d),
+                                  conv_state_in=None if st is None else st.to(d), state_len=SL)
+    y_ref, so_ref = oracle.causal_conv1d(f64(x), f64(w), f64(b), cu_seqlens=cu,
+                                         conv_state=None if st is None else f64(st), state_len=SL)
+    if dtype == "bf16":
+        ulps = bf16_ulp_diff(y, y_ref)
+        assert int(ulps.max()) <= 1, f"conv output off by {int(ulps.max())} bf16 ulps"
+    else:
+        assert_close(y, y_ref, 1e-6, "conv f32")
+    np.testing.assert_array_equal(f64(so), so_ref)   # the state is a copy of inputs: exact
+
+
+def test_causal_conv1d_strided_view_and_long_state():
+    _say("conv strided view, state_len 4")
+    T, Cfull, C, SL = 150, 160, 64, 4
+    xfull = W.randn((T, Cfull), 6, 1, "bf16")
+    x = xfull[:, 32:32 + C]                     # token stride 160
+    w = W.uniform((C, 4), 6, 2, -0.5, 0.5)
+    st = W.randn((1, C, SL), 6, 3, "bf16")
+    d = dev()
+    y, so = gdn.gdn_causal_conv1d(xfull.to(d)[:, 32:32 + C], w.to(d), conv_state_in=st.to(d))
+    y_ref, so_ref = oracle.causal_conv1d(f64(x), f64(w), conv_state=f64(st))
+    assert int(bf16_ulp_diff(y, y_ref).max()) <= 1
+    np.testing.assert_array_equal(f64(so), so_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("state_len", [3, 4])
+def test_causal_conv1d_update(dtype, state_len):
+    _say("conv update", dtype, state_len)
+    n, C = 37, 200
+    x = W.randn((n, C), 8, 1, dtype)
+    st = W.randn((n, C, state_len), 8, 2, dtype)
+    w = W.uniform((C, 4), 8, 3, -0.5, 0.5)
+    b = W.randn((C,), 8, 4)
+    d = dev()
+    st_d = st.to(d)
+    y = gdn.gdn_causal_conv1d_update(x.to(d), st_d, w.to(d), b.to(d))
+    y_ref, st_ref = oracle.causal_conv1d_update(f64(x), f64(st), f64(w), f64(b))
+    if dtype == "bf16":
+        assert int(bf16_ulp_diff(y, y_ref).max()) <= 1
+    else:
+        assert_close(y, y_ref, 1e-6, "conv update")
+    np.testing.assert_array_equal(f64(st_d), st_ref)
+
+
+# ------------------------------------------------------------------ recurrent (decode)
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_recurrent_one_token_per_sequence(dtype):
+    _say("recurrent 1 token", dtype)
+    n, nk, nv = 40, 2, 4
+    x = _inputs(dtype, [1] * n, nk, nv, s0_std=0.5)
+    d = _to(x, dev())
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    state = d["S0"].clone()
+    o = gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], g, beta, state)
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    o_ref, S_ref = oracle.delta_rule(f64(x["q"]), f64(x["k"]), f64(x["v"]), g_ref, b_ref,
+                                     cu_seqlens=np.arange(n + 1), initial_state=f64(x["S0"]))
+    assert_close(o, o_ref, TOL[dtype], "recurrent o")
+    assert_close(state, S_ref, TOL[dtype], "recurrent state")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_recurrent_multi_token_varlen(dtype):
+    _say("recurrent varlen", dtype)
+    lengths = [4, 0, 1, 9, 3]
+    x = _inputs(dtype, lengths, 1, 2, s0_std=0.5)
+    d = _to(x, dev())
+    cu = x["cu_seqlens"]
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    state = d["S0"].clone()
+    o = gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], g, beta, state, cu_seqlens=d["cu_seqlens"])
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    o_ref, S_ref = oracle.delta_rule(f64(x["q"]), f64(x["k"]), f64(x["v"]), g_ref, b_ref,
+                                     cu_seqlens=cu.numpy(), initial_state=f64(x["S0"]))
+    assert_close(o, o_ref, TOL[dtype], "recurrent varlen o")
+    assert_close(state, S_ref, TOL[dtype], "recurrent varlen state")
+
+
+# ------------------------------------------------------------------ chunk (prefill)
+
+def _run_chunk(x, dtype, with_s0=True, alias=False, o_dtype=torch.float32):
+    d = _to(x, dev())
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    s0 = d["S0"] if with_s0 else None
+    if alias:
+        st = s0.clone()
+        o, fs = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, cu_seqlens=d["cu_seqlens"], initial_state=st,
+                                  final_state=st, o_dtype=o_dtype)
+    else:
+        o, fs = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, cu_seqlens=d["cu_seqlens"], initial_state=s0,
+                                  o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    o_ref, S_ref = oracle.delta_rule(f64(x["q"]), f64(x["k"]), f64(x["v"]), g_ref, b_ref,
+                                     cu_seqlens=x["cu_seqlens"].numpy(),
+                                     initial_state=None if s0 is None else f64(x["S0"]))
+    return o, fs, o_ref, S_ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lengths,nk,nv", [
+    ([256], 1, 2),                       # whole chunks, grouped heads
+    ([200], 2, 4),                       # ragged tail
+    ([1, 63, 64, 65, 130, 0, 7], 1, 2),  # varlen incl. empty and one-token sequences
+    ([300], 1, 4),                       # 4 value heads per key head
+])
+def test_chunk_small(dtype, lengths, nk, nv):
+    _say("chunk", dtype, lengths, nk, nv)
+    x = _inputs(dtype, lengths, nk, nv, s0_std=0.3)
+    o, fs, o_ref, S_ref = _run_chunk(x, dtype)
+    assert_close(o, o_ref, TOL[dtype], "chunk o")
+    assert_close(fs, S_ref, TOL[dtype], "chunk final state")
+
+
+def test_chunk_zero_initial_state_and_alias():
+    _say("chunk zero S0 / aliased state")
+    x = _inputs("bf16", [190, 70], 1, 2, s0_std=0.3)
+    o, fs, o_ref, S_ref = _run_chunk(x, "bf16", with_s0=False)
+    assert_close(o, o_ref, TOL["bf16"], "chunk o (S0 = 0)")
+    assert_close(fs, S_ref, TOL["bf16"], "chunk state (S0 = 0)")
+    o2, fs2, o_ref2, S_ref2 = _run_chunk(x, "bf16", alias=True)
+    assert_close(o2, o_ref2, TOL["bf16"], "chunk o (aliased)")
+    assert_close(fs2, S_ref2, TOL["bf16"], "chunk state (aliased)")
+
+
+def test_chunk_slow_decay_stress():
+    """A_log = 0 and a ~ N(-4, 1): g ~ -0.02, the carried state dominates the output."""
+    _say("chunk slow decay")
+    x = _inputs("bf16", [640], 1, 2, s0_std=0.3)
+    x["A_log"] = torch.zeros_like(x["A_log"])
+    x["a"] = (x["a"].float() - 4.0).to(torch.bfloat16)
+    o, fs, o_ref, S_ref = _run_chunk(x, "bf16")
+    assert_close(o, o_ref, TOL["bf16"], "slow decay o")
+    assert_close(fs, S_ref, TOL["bf16"], "slow decay state")
+
+
+def test_chunk_matches_recurrent_path():
+    """Chunked and recurrent forms of the same sequence agree (both against the oracle and each other)."""
+    _say("chunk vs recurrent")
+    x = _inputs("bf16", [150], 1, 2, s0_std=0.3)
+    d = _to(x, dev())
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    o_c, s_c = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, initial_state=d["S0"])
+    st = d["S0"].clone()
+    o_r = gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], g, beta, st, cu_seqlens=d["cu_seqlens"])
+    assert_close(o_c, f64(o_r), 2 * TOL["bf16"], "chunk vs recurrent o")
+    assert_close(s_c, f64(st), 2 * TOL["bf16"], "chunk vs recurrent state")
+
+
+def test_chunk_bf16_output():
+    _say("chunk bf16 output")
+    x = _inputs("bf16", [200], 1, 2, s0_std=0.3)
+    o, fs, o_ref, S_ref = _run_chunk(x, "bf16", o_dtype=torch.bfloat16)
+    # one rounding of the output on top of the fp32 bar: 2e-3 RMS + half a bf16 ulp of |ref|
+    err = np.abs(f64(o) - o_ref)
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    assert np.all(err <= 2e-3 * rms + np.abs(o_ref) * 2.0 ** -8 + 1e-30)
+
+
+# ------------------------------------------------------------------ closed forms through the GPU
+
+def test_chunk_beta_zero_is_pure_decay():
+    _say("chunk beta = 0")
+    x = _inputs("bf16", [130], 1, 1, s0_std=0.5)
+    d = _to(x, dev())
+    g, _ = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    g = g * 0.01                       # slow decay so the state stays visible
+    beta = torch.zeros_like(g)
+    o, fs = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, initial_state=d["S0"])
+    G = np.cumsum(f64(g)[:, 0])
+    q = f64(x["q"])[:, 0]
+    qh = q / np.sqrt((q * q).sum(1, keepdims=True) + 1e-6) / math.sqrt(128)
+    S0 = f64(x["S0"])[0, 0]
+    o_ref = np.exp(G)[:, None] * (qh @ S0)
+    assert_close(o[:, 0], o_ref, TOL["bf16"], "beta=0 o")
+    assert_close(fs[0, 0], np.exp(G[-1]) * S0, TOL["bf16"], "beta=0 state")
+
+
+def test_chunk_reset_and_orthonormal_keys():
+    _say("chunk orthonormal keys, beta = 1, g = 0, no l2norm")
+    T = 100
+    rng = np.random.default_rng(3)
+    Qm, _ = np.linalg.qr(rng.standard_normal((128, 128)))
+    keys = torch.from_numpy(Qm[:T]).float()[:, None, :]     # fp32 inputs: exact keys
+    v = torch.randn(T, 1, 128, generator=torch.Generator().manual_seed(5))
+    S0 = torch.randn(1, 1, 128, 128, generator=torch.Generator().manual_seed(6))
+    d = dev()
+    g = torch.zeros(T, 1, device=d); beta = torch.ones(T, 1, device=d)
+    o, fs = gdn.gdn_chunk_fwd(keys.to(d), keys.to(d), v.to(d), g, beta, initial_state=S0.to(d), scale=1.0,
+                              qk_l2norm=False)
+    assert_close(o[:, 0], f64(v)[:, 0], TOL["f32"], "orthonormal read-back")
+    assert_close(keys[:, 0].double().numpy() @ f64(fs)[0, 0], f64(v)[:, 0], TOL["f32"], "values retrievable")
