@@ -1,7 +1,8 @@
 """Compile the fp64 CPU oracle (test infrastructure only) into a shared library.
 
-Plain g++ with OpenMP; no fast-math, so floating-point order is exactly the
-order written in gdn_oracle.cpp.
+Plain g++ with OpenMP; no fast-math and no contraction into fused
+multiply-adds, so every floating-point operation is the one written in
+gdn_oracle.cpp, in the order written there.
 """
 import os
 import subprocess
@@ -13,7 +14,7 @@ LIB = os.path.join(HERE, "liboracle_gdn.so")
 
 def build(verbose: bool = False) -> str:
     cmd = [
-        "g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared",
+        "g++", "-std=c++17", "-O3", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
         "-Wall", "-Wextra",
         os.path.join(HERE, "gdn_oracle.cpp"),
         "-o", LIB + ".tmp",

@@ -81,7 +81,7 @@ extern "C" int oracle_delta_rule(int64_t T_tot, int n_seqs, const int64_t* cu_se
       const double* src = S0 + unit * dk * dv;
       for (int64_t e = 0; e < static_cast<int64_t>(dk) * dv; ++e) S[e] = src[e];
     }
-    std::vector<double> qh(dk), kh(dk), u(dv);
+    std::vector<double> qh(dk), kh(dk), u(dv), acc(dv);
     const int64_t t0 = seq_begin(cu_seqlens, n, T_tot), t1 = seq_end(cu_seqlens, n, T_tot);
     for (int64_t t = t0; t < t1; ++t) {
       const double* qt = q + (t * nk + hk) * dk;
@@ -98,22 +98,22 @@ extern "C" int oracle_delta_rule(int64_t T_tot, int n_seqs, const int64_t* cu_se
       // decay
       const double decay = std::exp(g[t * nv + h]);
       for (auto& s : S) s *= decay;
-      // delta update on the decayed state: u = v - S^T kh ; S += beta kh u^T
-      for (int j = 0; j < dv; ++j) {
-        double acc = 0.0;
-        for (int i = 0; i < dk; ++i) acc += S[static_cast<size_t>(i) * dv + j] * kh[i];
-        u[j] = vt[j] - acc;
-      }
+      // delta update on the decayed state: u = v - S^T kh ; S += beta kh u^T.
+      // (S^T kh)_j = sum_i S_ij kh_i, summed over i in increasing order for
+      // every j; the i-outer loop only interleaves the independent j sums.
+      for (int j = 0; j < dv; ++j) acc[j] = 0.0;
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) acc[j] += S[static_cast<size_t>(i) * dv + j] * kh[i];
+      for (int j = 0; j < dv; ++j) u[j] = vt[j] - acc[j];
       const double bt = beta[t * nv + h];
       for (int i = 0; i < dk; ++i)
         for (int j = 0; j < dv; ++j) S[static_cast<size_t>(i) * dv + j] += bt * kh[i] * u[j];
-      // read-out after the update: o = S^T qh
+      // read-out after the update: o = S^T qh (same summation order)
       double* ot = o + (t * nv + h) * dv;
-      for (int j = 0; j < dv; ++j) {
-        double acc = 0.0;
-        for (int i = 0; i < dk; ++i) acc += S[static_cast<size_t>(i) * dv + j] * qh[i];
-        ot[j] = acc;
-      }
+      for (int j = 0; j < dv; ++j) acc[j] = 0.0;
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) acc[j] += S[static_cast<size_t>(i) * dv + j] * qh[i];
+      for (int j = 0; j < dv; ++j) ot[j] = acc[j];
     }
     if (ST) {
       double* dst = ST + unit * dk * dv;

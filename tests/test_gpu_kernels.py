@@ -68,7 +68,7 @@ def test_gated_rmsnorm(xd, zd, yd):
     y = gdn.gdn_gated_rmsnorm(x.to(dev()), z.to(dev()), w.to(dev()), eps=1e-6, y_dtype=W.TORCH_DTYPE[yd])
     ref = oracle.gated_rmsnorm(f64(x), f64(z), f64(w), eps=1e-6)
     if yd == "f32":
-        assert_close(y, ref, 1e-6, "rmsnorm")
+        assert_close(y, ref, TOL["f32"], "rmsnorm")
     else:
         assert int(bf16_ulp_diff(y, ref).max()) <= 1
 
@@ -77,7 +77,7 @@ def test_gated_rmsnorm_wide_rows():
     _say("rmsnorm D=512")
     x = W.randn((33, 512), 4, 1); z = W.randn((33, 512), 4, 2); w = W.randn((512,), 4, 3, std=0.1)
     y = gdn.gdn_gated_rmsnorm(x.to(dev()), z.to(dev()), w.to(dev()))
-    assert_close(y, oracle.gated_rmsnorm(f64(x), f64(z), f64(w)), 1e-6, "rmsnorm D=512")
+    assert_close(y, oracle.gated_rmsnorm(f64(x), f64(z), f64(w)), TOL["f32"], "rmsnorm D=512")
 
 
 # ------------------------------------------------------------------ causal conv
@@ -103,7 +103,7 @@ def test_causal_conv1d_varlen(dtype, with_state):
         ulps = bf16_ulp_diff(y, y_ref)
         assert int(ulps.max()) <= 1, f"conv output off by {int(ulps.max())} bf16 ulps"
     else:
-        assert_close(y, y_ref, 1e-6, "conv f32")
+        assert_close(y, y_ref, TOL["f32"], "conv f32")
     np.testing.assert_array_equal(f64(so), so_ref)   # the state is a copy of inputs: exact
 
 
@@ -137,7 +137,7 @@ def test_causal_conv1d_update(dtype, state_len):
     if dtype == "bf16":
         assert int(bf16_ulp_diff(y, y_ref).max()) <= 1
     else:
-        assert_close(y, y_ref, 1e-6, "conv update")
+        assert_close(y, y_ref, TOL["f32"], "conv update")
     np.testing.assert_array_equal(f64(st_d), st_ref)
 
 
