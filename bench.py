@@ -1,0 +1,220 @@
+"""Benchmark: Gated DeltaNet prefill tokens/s (T=8192, bf16) + decode state-update HBM GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu-baseline]
+
+One step = one pass of the prefill hot path over the T=8192 workload
+(B=1, 16 key heads repeated to 32 value heads, Dk=Dv=128, bf16 q/k/v/a/b,
+fp32 g/beta/state/output): gdn_gating then gdn_chunk_fwd (chunk table,
+per-chunk prep, per-sequence state recurrence). Inputs are resident in HBM
+before timing starts. W untimed warmup steps, then exactly K timed steps
+bracketed by torch.cuda.synchronize(); HIP events on the launch stream time
+every chunk_fwd call for the roofline figure.
+
+The decode figure runs one decode step of the 256-sequence workload (conv
+update, gating, recurrent update of the 512 MiB fp32 state in place) and
+reports the recurrent kernel's algorithmic bytes / its event-timed duration.
+
+The CPU baseline times the fp64 oracle (gating + token recurrence) on the
+whole prefill workload on the host (threads stated); it is a reported
+baseline, not a target.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def chunk_flops_per_token_head(C=64, dk=128, dv=128, r=2):
+    """Algorithmic flops of the chunked rule per token per value head.
+
+    Grams Q K^T and K K^T (shared by r value heads), W = T K, U = T V and the
+    intra-chunk P U product (C x C x D each per chunk), and the three state
+    products W S, Q S, K^T U (Dk x Dv per token). Triangular products are
+    counted dense; hi/lo precision passes are not counted.
+    """
+    return 2 * ((2 / r) * C * dk + C * (dk + 2 * dv) + 3 * dk * dv)
+
+
+def chunk_bytes(T, nk, nv, dk=128, dv=128, n_seqs=1, in_bytes=2, o_bytes=4, state_in=False):
+    """Algorithmic HBM bytes of one chunk_fwd call (inputs read once, outputs written once)."""
+    b = T * nk * dk * in_bytes * 2 + T * nv * dv * in_bytes      # q, k, v
+    b += T * nv * 4 * 2                                          # g, beta
+    b += T * nv * dv * o_bytes                                   # o
+    b += n_seqs * nv * dk * dv * 4 * (2 if state_in else 1)      # final (+ initial) state
+    return b
+
+
+def recurrent_bytes(n, nk, nv, dk=128, dv=128, in_bytes=2):
+    b = 2 * n * nv * dk * dv * 4                                 # state read + write
+    b += n * nk * dk * in_bytes * 2 + n * nv * dv * in_bytes      # q, k, v
+    b += n * nv * 4 * 2 + n * nv * dv * 4                        # g, beta, o
+    return b
+
+
+def cpu_baseline(x, threads):
+    import numpy as np
+    import oracle
+    f = lambda t: t.detach().to("cpu").double().numpy()
+    a, b, A, dt = f(x["a"]), f(x["b"]), f(x["A_log"]), f(x["dt_bias"])
+    q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
+    T = q.shape[0]
+    reps, t0 = 0, time.perf_counter()
+    while True:   # repeat the whole workload until ~10 s of wall time
+        g, beta = oracle.gating(a, b, A, dt)
+        oracle.delta_rule(q, k, v, g, beta, threads=threads)
+        reps += 1
+        dt_s = time.perf_counter() - t0
+        if dt_s >= 10.0 or reps >= 1000:
+            break
+    return dict(value=reps * T / dt_s, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"whole prefill workload (T={T}, 32 value heads), fp64 gating + token recurrence, "
+                       f"{reps} repetitions in {dt_s:.1f} s wall on {threads} threads")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GDN core shards by head or sequence with no "
+              "collective, so there is no multi-GPU step to time (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_gdn_amd as gdn
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- prefill step
+    wl = W.WORKLOADS["prefill_chunk_t8k"]
+    x = W.chunk_inputs(wl)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    T = wl.T
+    g = torch.empty((T, wl.nv), device=dev, dtype=torch.float32)
+    beta = torch.empty_like(g)
+    o = torch.empty((T, wl.nv, wl.dv), device=dev, dtype=torch.float32)
+    st = torch.empty((1, wl.nv, wl.dk, wl.dv), device=dev, dtype=torch.float32)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(T, 1, wl.nk, wl.nv), device=dev, dtype=torch.uint8)
+
+    def step(ev=None):
+        gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], g=g, beta=beta, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, final_state=st, o=o, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_step = elapsed * 1e3 / args.steps
+    chunk_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    r = wl.nv // wl.nk
+    flops = chunk_flops_per_token_head(r=r) * T * wl.nv
+    cbytes = chunk_bytes(T, wl.nk, wl.nv)
+    achieved_tflops = flops / (chunk_ms * 1e-3) / 1e12
+    roofline = dict(bound="mfma", kernel="gdn_chunk_fwd (chunk_offsets + chunk_prep + chunk_state launches)",
+                    achieved=round(achieved_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    avg_ms=round(chunk_ms, 4), algorithmic_flops=flops, algorithmic_bytes=cbytes,
+                    hbm_gbps_algorithmic=round(cbytes / (chunk_ms * 1e-3) / 1e9, 1))
+
+    # ---------------------------------------------------------------- decode step
+    decode = None
+    if not args.skip_decode:
+        dw = W.WORKLOADS["decode_256seq"]
+        dx = {k: v.to(dev) for k, v in W.decode_inputs(dw).items()}
+        n = dw.n_seqs
+        kd = dw.nk * dw.dk
+        y = torch.empty_like(dx["x"])
+        dg = torch.empty((n, dw.nv), device=dev, dtype=torch.float32)
+        db = torch.empty_like(dg)
+        do = torch.empty((n, dw.nv, dw.dv), device=dev, dtype=torch.float32)
+        qv = y[:, :kd].view(n, dw.nk, dw.dk)
+        kv = y[:, kd:2 * kd].view(n, dw.nk, dw.dk)
+        vv = y[:, 2 * kd:].view(n, dw.nv, dw.dv)
+
+        def dstep(ev=None):
+            gdn.gdn_causal_conv1d_update(dx["x"], dx["conv_state"], dx["conv_w"], y=y, stream=stream)
+            gdn.gdn_gating(dx["a"], dx["b"], dx["A_log"], dx["dt_bias"], g=dg, beta=db, stream=stream)
+            if ev is not None:
+                ev[0].record(stream)
+            gdn.gdn_recurrent_fwd(qv, kv, vv, dg, db, dx["state"], o=do, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            dstep(devs[i])
+        torch.cuda.synchronize()
+        dstep_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        rec_ms = sum(a.elapsed_time(b) for a, b in devs) / args.steps
+        rbytes = recurrent_bytes(n, dw.nk, dw.nv)
+        gbps = rbytes / (rec_ms * 1e-3) / 1e9
+        decode = dict(workload="decode_256seq: 256 seqs x 1 token, 16->32 heads, 512 MiB fp32 state in place",
+                      step_ms=round(dstep_ms, 4),
+                      roofline=dict(bound="hbm", kernel="recurrent_kernel", achieved=round(gbps, 1),
+                                    peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
+                                    traffic=None, avg_ms=round(rec_ms,4), algorithmic_bytes=rbytes))
+
+    cpu = None
+    if not args.skip_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(x, threads)
+        cpu["value"] = round(cpu["value"], 1)
+
+    out = {
+        "metric": "GDN prefill tokens/s (T=8K, bf16) + decode state-update HBM GB/s",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k,v,a,b ~ N(0,1) bf16, A_log = log U[1,16], dt_bias ~ N(0,0.1))",
+        "config": {"workload": "prefill_chunk_t8k: B=1, T=8192, 16 key heads -> 32 value heads, Dk=Dv=128, "
+                               "chunk 64, zero initial state, fp32 output + final state",
+                   "global_batch": 1, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

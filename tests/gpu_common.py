@@ -39,3 +39,33 @@ def bf16_ulp_diff(gpu_bf16, ref_f64):
     a = torch.where(a < 0, -(a & 0x7FFF), a)
     b = torch.where(b < 0, -(b & 0x7FFF), b)
     return (a - b).abs()
+
+
+def conv_abs_sum(xe, w):
+    """sum_j |w[c,j]| |xe[t+j, c]| for every output of a K-tap causal conv over xe = [history(K-1) + tokens, C]."""
+    xe = np.abs(np.asarray(xe, dtype=np.float64))
+    w = np.abs(np.asarray(w, dtype=np.float64))
+    K = w.shape[1]
+    T = xe.shape[0] - (K - 1)
+    return sum(w[None, :, j] * xe[j:j + T] for j in range(K))
+
+
+def assert_conv_close(y_gpu, y_ref, s_abs, what=""):
+    """bf16 conv output vs the fp64 reference.
+
+    The kernel accumulates K products in fp32 (each fused multiply-add rounds
+    once: error <= K * 2^-24 * sum|w x|), applies SiLU in fp32 and rounds once
+    to bf16 (<= half a bf16 ulp). Allowed: one bf16 ulp of |ref| plus twice
+    the accumulation bound. Near-zero outputs of cancelling sums may differ by
+    several bf16 ulps of their own tiny magnitude; that is still inside it.
+    """
+    y = f64(y_gpu)
+    ref = np.asarray(y_ref, dtype=np.float64)
+    K = 4
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    bound = ulp + 2 * K * 2.0 ** -24 * np.asarray(s_abs)
+    err = np.abs(y - ref)
+    ulps = bf16_ulp_diff(y_gpu, ref)
+    print(f"[parity] {what}: max ulps {int(ulps.max())}, flips {float((ulps > 0).float().mean()):.2e}, "
+          f"max err/bound {float(np.max(err / bound)):.3f}", flush=True)
+    assert np.all(err <= bound), f"{what}: conv output outside the fp32-accumulation + bf16-rounding bound"

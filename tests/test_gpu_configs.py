@@ -1,0 +1,176 @@
+"""Full-size parity of the five workloads against the fp64 CPU oracle.
+
+Each workload runs on the GPU exactly as the benchmark launches it (the
+binding's defaults). Checks:
+  * tiny chunk fp32 (T=256, 1->2 heads) and prefill T=8192 (16->32 heads):
+    every output and final state against the oracle;
+  * varlen packed prefill (8 sequences, nonzero initial states): every head
+    of every sequence;
+  * decode step (256 sequences, 512 MiB state in place): stage-wise --
+    conv update (fp32-accumulation + one bf16 rounding bound, state exact),
+    then gating + recurrent update
+    from the GPU's own bf16 conv output, every unit;
+  * long fused prefill (T=262144, 16->64 heads): stage-wise on samples the
+    oracle can compute -- conv on three token windows of all channels, gating
+    on every 61st token, the core on two value heads over the full sequence
+    (outputs and final state), gated RMSNorm on sampled rows.
+Parity bar: max-abs <= 2e-3 * RMS for bf16 inputs, 1e-5 * RMS for fp32.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_gdn_amd as gdn
+import oracle
+import workloads as W
+from gpu_common import TOL, assert_close, assert_conv_close, conv_abs_sum, dev, f64
+
+pytestmark = pytest.mark.gpu
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _chunk_config(name):
+    wl = W.WORKLOADS[name]
+    _say(name, "generate")
+    x = W.chunk_inputs(wl)
+    d = {k: (v.to(dev()) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    _say(name, "gpu", "T =", int(x["cu_seqlens"][-1]))
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    o, st = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta,
+                              cu_seqlens=d["cu_seqlens"] if wl.len_range else None, initial_state=d["S0"])
+    torch.cuda.synchronize()
+    _say(name, "oracle")
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    o_ref, s_ref = oracle.delta_rule(f64(x["q"]), f64(x["k"]), f64(x["v"]), g_ref, b_ref,
+                                     cu_seqlens=x["cu_seqlens"].numpy(),
+                                     initial_state=None if x["S0"] is None else f64(x["S0"]), threads=THREADS)
+    return wl, o, st, o_ref, s_ref
+
+
+@pytest.mark.parametrize("name", ["tiny_chunk_f32", "prefill_chunk_t8k", "varlen_prefill_8seq"])
+def test_chunk_workload(name):
+    wl, o, st, o_ref, s_ref = _chunk_config(name)
+    tol = TOL[wl.dtype]
+    assert_close(o, o_ref, tol, f"{name} o")
+    assert_close(st, s_ref, tol, f"{name} final state")
+    # worst head, for the log
+    per_head = [np.max(np.abs(f64(o[:, h]) - o_ref[:, h])) / np.sqrt(np.mean(o_ref[:, h] ** 2))
+                for h in range(o.shape[1])]
+    print(f"[parity] {name} worst head ratio {max(per_head):.3e} (head {int(np.argmax(per_head))})", flush=True)
+
+
+def test_decode_step_workload():
+    wl = W.WORKLOADS["decode_256seq"]
+    _say(wl.name, "generate")
+    x = W.decode_inputs(wl)
+    d = {k: v.to(dev()) for k, v in x.items()}
+    n, C = x["x"].shape
+    kd = wl.nk * wl.dk
+    _say(wl.name, "gpu")
+    conv_state = d["conv_state"].clone()
+    y = gdn.gdn_causal_conv1d_update(d["x"], conv_state, d["conv_w"])
+    q = y[:, :kd].view(n, wl.nk, wl.dk)
+    k = y[:, kd:2 * kd].view(n, wl.nk, wl.dk)
+    v = y[:, 2 * kd:].view(n, wl.nv, wl.dv)
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    state = d["state"].clone()
+    o = gdn.gdn_recurrent_fwd(q, k, v, g, beta, state)
+    torch.cuda.synchronize()
+
+    _say(wl.name, "oracle: conv update")
+    y_ref, cs_ref = oracle.causal_conv1d_update(f64(x["x"]), f64(x["conv_state"]), f64(x["conv_w"]))
+    win = np.concatenate([f64(x["conv_state"]), f64(x["x"])[:, :, None]], axis=2)     # [n, C, 4]
+    s_abs = np.sum(np.abs(win) * np.abs(f64(x["conv_w"]))[None], axis=2)
+    assert_conv_close(y, y_ref, s_abs, "decode conv update")
+    np.testing.assert_array_equal(f64(conv_state), cs_ref)
+
+    _say(wl.name, "oracle: recurrent on the GPU's conv output")
+    yg = f64(y)
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    o_ref, s_ref = oracle.delta_rule(yg[:, :kd].reshape(n, wl.nk, wl.dk), yg[:, kd:2 * kd].reshape(n, wl.nk, wl.dk),
+                                     yg[:, 2 * kd:].reshape(n, wl.nv, wl.dv), g_ref, b_ref,
+                                     cu_seqlens=np.arange(n + 1), initial_state=f64(x["state"]), threads=THREADS)
+    assert_close(o, o_ref, TOL["bf16"], "decode o")
+    assert_close(state, s_ref, TOL["bf16"], "decode state")
+
+
+# ------------------------------------------------------------------ long fused prefill
+
+@pytest.fixture(scope="module")
+def long_run():
+    wl = W.WORKLOADS["long_fused_t256k"]
+    D = dev()
+    _say(wl.name, "generate on the GPU")
+    x = W.fused_inputs(wl, device=D)
+    T, C = x["x"].shape
+    kd = wl.nk * wl.dk
+    _say(wl.name, "gpu pipeline")
+    y, cs = gdn.gdn_causal_conv1d(x["x"], x["conv_w"], state_len=wl.state_len)
+    q = y[:, :kd].view(T, wl.nk, wl.dk)
+    k = y[:, kd:2 * kd].view(T, wl.nk, wl.dk)
+    v = y[:, 2 * kd:].view(T, wl.nv, wl.dv)
+    g, beta = gdn.gdn_gating(x["a"], x["b"], x["A_log"], x["dt_bias"])
+    o, st = gdn.gdn_chunk_fwd(q, k, v, g, beta)
+    out = gdn.gdn_gated_rmsnorm(o, x["z"], x["norm_w"], eps=1e-6)
+    torch.cuda.synchronize()
+    return dict(wl=wl, x=x, y=y, cs=cs, g=g, beta=beta, o=o, st=st, out=out, T=T, C=C, kd=kd)
+
+
+def test_long_conv_windows(long_run):
+    r = long_run
+    T = r["T"]
+    for t0, t1 in ((0, 2048), (T // 2 - 1000, T // 2 + 1048), (T - 2048, T)):
+        _say("long conv window", t0, t1)
+        lo = max(t0 - 3, 0)
+        xs = f64(r["x"]["x"][lo:t1])
+        y_ref, _ = oracle.causal_conv1d(xs, f64(r["x"]["conv_w"]))
+        xe = np.concatenate([np.zeros((3 - (t0 - lo), xs.shape[1])), xs])
+        s_abs = conv_abs_sum(xe, f64(r["x"]["conv_w"]))          # outputs for tokens t0 .. t1-1
+        assert_conv_close(r["y"][t0:t1], y_ref[t0 - lo:], s_abs, f"long conv [{t0},{t1})")
+    np.testing.assert_array_equal(f64(r["cs"][0]), f64(r["x"]["x"][T - 3:]).T)
+
+
+def test_long_gating_sampled(long_run):
+    r = long_run
+    idx = torch.arange(0, r["T"], 61, device=r["g"].device)
+    g_ref, b_ref = oracle.gating(f64(r["x"]["a"][idx]), f64(r["x"]["b"][idx]), f64(r["x"]["A_log"]),
+                                 f64(r["x"]["dt_bias"]))
+    np.testing.assert_allclose(f64(r["g"][idx]), g_ref, rtol=4e-6)
+    np.testing.assert_allclose(f64(r["beta"][idx]), b_ref, rtol=4e-6)
+
+
+@pytest.mark.timeout(300)
+def test_long_core_two_heads_full_sequence(long_run):
+    r = long_run
+    wl = r["wl"]
+    rr = wl.nv // wl.nk
+    heads = [0, 37]
+    khs = [h // rr for h in heads]
+    _say("long core heads", heads, "key heads", khs)
+    yg = r["y"]
+    kd = r["kd"]
+    q = torch.stack([yg[:, hk * 128:(hk + 1) * 128] for hk in khs], 1)
+    k = torch.stack([yg[:, kd + hk * 128:kd + (hk + 1) * 128] for hk in khs], 1)
+    v = torch.stack([yg[:, 2 * kd + h * 128:2 * kd + (h + 1) * 128] for h in heads], 1)
+    hs = torch.tensor(heads, device=yg.device)
+    g_ref, b_ref = oracle.gating(f64(r["x"]["a"][:, hs]), f64(r["x"]["b"][:, hs]), f64(r["x"]["A_log"][hs]),
+                                 f64(r["x"]["dt_bias"][hs]))
+    o_ref, s_ref = oracle.delta_rule(f64(q), f64(k), f64(v), g_ref, b_ref, threads=THREADS)
+    for i, h in enumerate(heads):
+        assert_close(r["o"][:, h], o_ref[:, i], TOL["bf16"], f"long o head {h}")
+        assert_close(r["st"][0, h], s_ref[0, i], TOL["bf16"], f"long final state head {h}")
+
+
+def test_long_rmsnorm_sampled_rows(long_run):
+    r = long_run
+    rows = torch.arange(0, r["T"], 257, device=r["o"].device)
+    x = r["o"][rows]              # [rows, 64, 128] fp32 from the GPU core (stage-wise)
+    z = r["x"]["z"][rows]
+    ref = oracle.gated_rmsnorm(f64(x), f64(z), f64(r["x"]["norm_w"]), eps=1e-6)
+    assert_close(r["out"][rows], ref, TOL["f32"], "long gated rmsnorm (fp32 x)")
