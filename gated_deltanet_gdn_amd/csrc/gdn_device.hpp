@@ -137,6 +137,42 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int64_t T, 
   e = min(max(static_cast<int64_t>(cu[n + 1]), b), T);
 }
 
+// Contractions of length 16 (the blocked triangular inverse): bf16 uses
+// v_mfma_f32_16x16x16_bf16 (4 k-slots per lane: 4*(lane/16) .. +3), fp32
+// uses v_mfma_f32_16x16x4_f32 four times. Operands split into hi + lo as above.
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+template <bool BF16, bool EXACT_A, bool EXACT_B> struct Mma16;
+template <bool EA, bool EB> struct Mma16<false, EA, EB> : Mma<false, EA, EB> {};
+template <bool EA, bool EB> struct Mma16<true, EA, EB> {
+  static constexpr int KS = 16, KPL = 4;
+  __device__ static __forceinline__ void split4(const float (&v)[4], bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 h = static_cast<__bf16>(v[i]);
+      hi[i] = h;
+      lo[i] = static_cast<__bf16>(v[i] - static_cast<float>(h));
+    }
+  }
+  __device__ static __forceinline__ void run(f32x4& acc, const float (&a)[4], const float (&b)[4]) {
+    bf16x4 ah, al, bh, bl;
+    split4(a, ah, al);
+    split4(b, bh, bl);
+    if constexpr (EA && EB) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    } else if constexpr (EA) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    } else if constexpr (EB) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    } else {
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    }
+  }
+};
+
 // ---------------------------------------------------------------- XCD-aware block order
 // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
 // Remap so that logically consecutive work items land on the same XCD and

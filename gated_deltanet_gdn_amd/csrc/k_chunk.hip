@@ -22,15 +22,25 @@
 // Kernels:
 //   chunk_offsets : exclusive prefix of ceil(len/64) over sequences (varlen
 //                   chunk table on the device; no host synchronisation).
-//   chunk_prep    : one workgroup per (chunk, key head), fully parallel. Grams
+//   chunk_prep    : one wave per (chunk, value head), fully parallel. Grams
 //                   K K^T and Q K^T on MFMA from the raw inputs (exact
-//                   operands), then per value head: fp64 cumsum of g, A, the
-//                   forward substitution for T, P, and the per-token scalars.
-//                   Writes a packed 64x64 fp32 tile per (chunk, value head):
-//                   T strictly below the diagonal, P^T on and above it.
-//   chunk_state   : one wave per (sequence, value head, 16 value columns),
-//                   sequential over the sequence's chunks, S (128 x 16) held
-//                   in MFMA accumulator registers for the whole sequence.
+//                   operands, kept in registers), fp64 cumsum of g, A, the
+//                   blocked inverse T (16x16 diagonal blocks by substitution,
+//                   off-diagonal blocks on MFMA), P and per-token scalars.
+//                   Output per (chunk, value head): one packed 64x64 fp32
+//                   tile X with X[i][j] = T[i][j] for j < i and
+//                   X[63-i][63-j] = P[i][j] for j <= i (P turned by 180
+//                   degrees into the upper triangle), so rows of both T and
+//                   P are contiguous; plus 64 float4 scalars and exp(G_C).
+//   chunk_state   : sequential over a sequence's chunks. bf16 inputs: four
+//                   waves per (sequence, value head, 16 value columns); wave
+//                   w holds rows 32w..32w+31 of S (128 x 16, fp32) in MFMA
+//                   accumulators and computes token rows 16w..16w+15 of the
+//                   chunk; S is exchanged through LDS once per chunk. Q, T,
+//                   P and V operands are loaded straight into registers in
+//                   MFMA fragment layout one chunk ahead; K is staged in LDS
+//                   (double-buffered) because the state update reads it
+//                   transposed. fp32 inputs use a simple one-wave variant.
 //                   Products with an fp32 operand split it into bf16 hi + lo.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
@@ -40,18 +50,13 @@ namespace {
 
 constexpr int CH = 64;     // chunk length
 constexpr int D = 128;     // dk = dv
-constexpr int KP = 136;    // LDS row pitch (floats) of 64 x 128 K/Q tiles
-constexpr int GP = 65;     // LDS pitch of 64 x 64 Gram tiles
-constexpr int AP = 68;     // LDS pitch of 64 x 64 A / T|P tiles (16-byte rows)
-constexpr int RP = 18;     // LDS pitch of the per-wave 64 x 16 R / U tiles
+constexpr int AP = 68;     // LDS pitch (floats) of 64 x 64 fp32 tiles (16-byte rows)
 constexpr float kEps = 1e-6f;
-
-__device__ __forceinline__ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
   size_t off_chunk_off, off_tp, off_sc, off_egc, total;
 };
-__host__ __device__ inline WsLayout ws_layout(int64_t T, int n_seqs, int nv) {
+inline WsLayout ws_layout(int64_t T, int n_seqs, int nv) {
   const int64_t nch = T / CH + n_seqs;   // >= sum_n ceil(len_n / 64)
   WsLayout w{};
   size_t o = 0;
@@ -104,52 +109,89 @@ __device__ __forceinline__ int find_le(const int32_t* a, int n, int64_t x) {
   return lo;
 }
 
-template <typename TIn>
-__device__ __forceinline__ void load_row8(const TIn* p, float* dst) {
-  float v[8];
-  load8(p, v);
-  *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+// Raw copies of 8 input elements (16 bytes of bf16 or 32 bytes of fp32).
+__device__ __forceinline__ void copy8(const uint16_t* src, uint16_t* dst) {
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
 }
+__device__ __forceinline__ void copy8(const float* src, float* dst) {
+  *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+  *reinterpret_cast<float4*>(dst + 4) = *reinterpret_cast<const float4*>(src + 4);
+}
+__device__ __forceinline__ uint4 zero_if(bool z, uint4 u) {
+  return z ? make_uint4(0, 0, 0, 0) : u;
+}
+__device__ __forceinline__ float4 zero_if(bool z, float4 u) {
+  return z ? make_float4(0.f, 0.f, 0.f, 0.f) : u;
+}
+__device__ __forceinline__ void copy8_or_zero(const uint16_t* src, uint16_t* dst, bool z) {
+  *reinterpret_cast<uint4*>(dst) = zero_if(z, *reinterpret_cast<const uint4*>(src));
+}
+__device__ __forceinline__ void copy8_or_zero(const float* src, float* dst, bool z) {
+  *reinterpret_cast<float4*>(dst) = zero_if(z, *reinterpret_cast<const float4*>(src));
+  *reinterpret_cast<float4*>(dst + 4) = zero_if(z, *reinterpret_cast<const float4*>(src + 4));
+}
+__device__ __forceinline__ float tof(uint16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ float tof(float x) { return x; }
 
-// Cooperative load of a 64 x 128 tile (rows >= L zero) into LDS with pitch KP.
-template <typename TIn>
-__device__ __forceinline__ void load_tile_64x128(const TIn* __restrict__ base, int64_t tok_stride, int L,
-                                                 float* __restrict__ dst, int tid, int nthreads) {
-  for (int idx = tid; idx < CH * (D / 8); idx += nthreads) {
-    const int row = idx >> 4, seg = idx & 15;
-    float* d = dst + row * KP + seg * 8;
-    if (row < L) {
-      load_row8(base + row * tok_stride + seg * 8, d);
-    } else {
-      *reinterpret_cast<float4*>(d) = make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4*>(d + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+// lower 16x16 tiles of a 64x64 matrix, p = 0..9 -> (mi, mj), mi >= mj
+__device__ __forceinline__ int tile_mi(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
+__device__ __forceinline__ int tile_mj(int p) { const int mi = tile_mi(p); return p - mi * (mi + 1) / 2; }
+
+// acc += A(16x16) * B(16x16), both fp32 in LDS (row pitches lda, ldb).
+template <bool BF>
+__device__ __forceinline__ void mm16(f32x4& acc, const float* A, int lda, const float* B, int ldb, int lr, int lg) {
+  using M = Mma16<BF, false, false>;
+#pragma unroll
+  for (int s = 0; s < 16 / M::KS; ++s) {
+    float a[M::KPL], b[M::KPL];
+#pragma unroll
+    for (int j = 0; j < M::KPL; ++j) {
+      const int kk = s * M::KS + M::KPL * lg + j;
+      a[j] = A[lr * lda + kk];
+      b[j] = B[kk * ldb + lr];
     }
+    M::run(acc, a, b);
   }
 }
 
 // ------------------------------------------------------------------ prep
 template <typename TIn>
-__global__ void __launch_bounds__(256) chunk_prep_kernel(
+constexpr int prep_pitch() { return sizeof(TIn) == 2 ? 136 : 132; }   // 16-byte rows
+template <typename TIn>
+constexpr size_t prep_lds_bytes() {
+  constexpr size_t tiles = 2 * CH * prep_pitch<TIn>() * sizeof(TIn);
+  constexpr size_t at = 2 * CH * AP * sizeof(float);
+  return (tiles > at ? tiles : at) + CH * sizeof(double) + 4 * CH * sizeof(float) + 16 * 20 * sizeof(float);
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(64) chunk_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t qs, int64_t ks,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int n_seqs, int64_t T, int nk, int nv, float scale, int l2, const int32_t* __restrict__ chunk_off,
     float* __restrict__ tp, float4* __restrict__ sc, float* __restrict__ egc) {
   constexpr bool BF = sizeof(TIn) == 2;
-  using M = Mma<BF, true, true>;
-  constexpr int KS = M::KS, KPL = M::KPL;
+  constexpr int EP = prep_pitch<TIn>();
+  using MG = Mma<BF, true, true>;
+  constexpr int KS = MG::KS, KPL = MG::KPL;
+  constexpr size_t tiles = 2 * CH * EP * sizeof(TIn);
+  constexpr size_t at = 2 * CH * AP * sizeof(float);
+  constexpr size_t head = tiles > at ? tiles : at;
 
-  extern __shared__ float smem[];
-  float* Ks = smem;                       // [64][KP]
-  float* Qs = Ks + CH * KP;               // [64][KP]
-  float* Gkk = Qs + CH * KP;              // [64][GP]
-  float* Gqk = Gkk + CH * GP;             // [64][GP]
-  float* rk_s = Gqk + CH * GP;            // [64]
-  float* rq_s = rk_s + CH;                // [64]
-  float* Aw_all = Ks;                     // after the Grams: 4 x [64][AP] (aliases Ks/Qs)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  TIn* Ks = reinterpret_cast<TIn*>(smem);          // [64][EP]   (input tiles)
+  TIn* Qs = Ks + CH * EP;                          // [64][EP]
+  float* Aw = reinterpret_cast<float*>(smem);      // [64][AP]   (after the Grams)
+  float* Tw = Aw + CH * AP;                        // [64][AP]
+  double* Gs = reinterpret_cast<double*>(smem + head);
+  float* rk_s = reinterpret_cast<float*>(Gs + CH);
+  float* rq_s = rk_s + CH;
+  float* b_s = rq_s + CH;
+  float* scr = b_s + 2 * CH;                       // [16][20] scratch
 
   const int c = blockIdx.x;
-  const int hk = blockIdx.y;
+  const int h = blockIdx.y;
+  const int hk = h / (nv / nk);
   const int total = chunk_off[n_seqs];
   if (c >= total) return;
   const int n = find_le(chunk_off, n_seqs, c);
@@ -157,121 +199,421 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(
   seq_bounds(cu, n, T, s_begin, s_end);
   const int64_t t0 = s_begin + static_cast<int64_t>(c - chunk_off[n]) * CH;
   const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = nv / nk;
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
 
-  load_tile_64x128(k + t0 * ks + static_cast<int64_t>(hk) * D, ks, L, Ks, tid, 256);
-  load_tile_64x128(q + t0 * qs + static_cast<int64_t>(hk) * D, qs, L, Qs, tid, 256);
-  __syncthreads();
-
-  {  // row norms: 4 lanes per row, 32 elements each
-    const int row = tid >> 2, part = tid & 3;
-    float sk = 0.f, sq = 0.f;
-#pragma unroll 8
-    for (int e = 0; e < 32; ++e) {
-      const float kv = Ks[row * KP + part * 32 + e];
-      const float qv = Qs[row * KP + part * 32 + e];
-      sk = fmaf(kv, kv, sk);
-      sq = fmaf(qv, qv, sq);
-    }
-    sk += __shfl_xor(sk, 1, 64); sk += __shfl_xor(sk, 2, 64);
-    sq += __shfl_xor(sq, 1, 64); sq += __shfl_xor(sq, 2, 64);
-    if (part == 0) {
-      const bool valid = row < L;
-      rk_s[row] = valid ? (l2 ? 1.0f / sqrtf(sk + kEps) : 1.0f) : 0.0f;
-      rq_s[row] = valid ? (l2 ? 1.0f / sqrtf(sq + kEps) : 1.0f) : 0.0f;
-    }
-  }
-
-  // Grams on the lower 16x16 tiles: 10 of K K^T and 10 of Q K^T, 5 per wave.
+  // 1. K and Q tiles into LDS (rows >= L zero); 4 rows per instruction
   {
-    const int lr = lane & 15, lg = lane >> 4;
-    for (int p = wave; p < 20; p += 4) {
-      const int pp = p % 10;
-      const int mi = pp >= 6 ? 3 : pp >= 3 ? 2 : pp >= 1 ? 1 : 0;
-      const int mj = pp - mi * (mi + 1) / 2;
-      const float* X = p < 10 ? Ks : Qs;
-      float* G = p < 10 ? Gkk : Gqk;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const TIn* kb = k + t0 * ks + static_cast<int64_t>(hk) * D;
+    const TIn* qb = q + t0 * qs + static_cast<int64_t>(hk) * D;
 #pragma unroll
-      for (int s = 0; s < D / KS; ++s) {
-        float a[KPL], b[KPL];
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const int kk = s * KS + KPL * lg + j;
-          a[j] = X[(16 * mi + lr) * KP + kk];
-          b[j] = Ks[(16 * mj + lr) * KP + kk];
-        }
-        M::run(acc, a, b);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) G[(16 * mi + 4 * lg + i) * GP + 16 * mj + lr] = acc[i];
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane, row = idx >> 4, seg = idx & 15;
+      const int rr = min(row, L - 1);   // clamped read, zeroed below: no branch around the load
+      copy8_or_zero(kb + rr * ks + seg * 8, Ks + row * EP + seg * 8, row >= L);
+      copy8_or_zero(qb + rr * qs + seg * 8, Qs + row * EP + seg * 8, row >= L);
     }
   }
   __syncthreads();
 
-  // Per value head: one wave each.
-  for (int jj = wave; jj < r; jj += 4) {
-    const int h = hk * r + jj;
-    float* Aw = Aw_all + wave * CH * AP;
-    const size_t tile = static_cast<size_t>(c) * nv + h;
-    float* X = tp + tile * CH * CH;
-
-    const bool valid = lane < L;
-    const float gi = valid ? g[(t0 + lane) * nv + h] : 0.0f;
-    const float bi = valid ? beta[(t0 + lane) * nv + h] : 0.0f;
-    double G = gi;                      // chunk-local cumulative decay, fp64
+  // 2. |q_i|^2 (lane = row)
+  float sqq = 0.f;
+#pragma unroll 8
+  for (int e = 0; e < D; ++e) {
+    const float x = tof(Qs[lane * EP + e]);
+    sqq = fmaf(x, x, sqq);
+  }
+  // 3. Grams on the lower 16x16 tiles, kept in registers
+  f32x4 gkk[10], gqk[10];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(G, off, 64);
-      if (lane >= off) G += y;
-    }
-    const double GC = __shfl(G, 63, 64);
-    const float rk_i = rk_s[lane], rq_i = rq_s[lane];
-
-    // A, column-oriented (lane = column j); row i broadcast via shuffles
-    for (int i = 0; i < CH; ++i) {
-      const double Gi = __shfl(G, i, 64);
-      const float bi_ = __shfl(bi, i, 64);
-      float a = 0.0f;
-      if (lane < i) a = bi_ * rk_s[i] * rk_i * expf(static_cast<float>(Gi - G)) * Gkk[i * GP + lane];
-      Aw[i * AP + lane] = a;
-    }
-    // (wave-private LDS: the writes above precede the reads below in program order)
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-
-    // forward substitution: T[i][j] = delta_ij - sum_{m<i} A[i][m] T[m][j]; lane = j
-    float tcol[CH];
+  for (int p = 0; p < 10; ++p) {
+    const int mi = tile_mi(p), mj = tile_mj(p);
+    gkk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gqk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      float acc = (lane == i) ? 1.0f : 0.0f;
-      const float* Ar = Aw + i * AP;
+    for (int s = 0; s < D / KS; ++s) {
+      float ak[KPL], aq[KPL], bk[KPL];
 #pragma unroll
-      for (int m = 0; m < i; ++m) acc = fmaf(-Ar[m], tcol[m], acc);
-      tcol[i] = acc;
-      if (lane < i) X[i * CH + lane] = acc;     // strictly lower part of T
+      for (int j = 0; j < KPL; ++j) {
+        const int kk = s * KS + KPL * lg + j;
+        ak[j] = tof(Ks[(16 * mi + lr) * EP + kk]);
+        aq[j] = tof(Qs[(16 * mi + lr) * EP + kk]);
+        bk[j] = tof(Ks[(16 * mj + lr) * EP + kk]);
+      }
+      MG::run(gkk[p], ak, bk);
+      MG::run(gqk[p], aq, bk);
     }
+  }
+  // 4. norms: |k_i|^2 from the Gram diagonal (diagonal tiles p = 0, 2, 5, 9)
+  if (lr >= 4 * lg && lr < 4 * lg + 4) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int p = m * (m + 1) / 2 + m;
+      const int row = 16 * m + lr;
+      const float skk = gkk[p][lr - 4 * lg];
+      rk_s[row] = row < L ? (l2 ? 1.0f / sqrtf(skk + kEps) : 1.0f) : 0.0f;
+    }
+  }
+  rq_s[lane] = lane < L ? (l2 ? 1.0f / sqrtf(sqq + kEps) : 1.0f) : 0.0f;
+  // 5. chunk-local cumulative decay in fp64
+  const bool valid = lane < L;
+  const float g_ld = g[(t0 + min(lane, L - 1)) * nv + h];
+  const float b_ld = beta[(t0 + min(lane, L - 1)) * nv + h];
+  const float gi = valid ? g_ld : 0.0f;
+  const float bi = valid ? b_ld : 0.0f;
+  double G = gi;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(G, off, 64);
+    if (lane >= off) G += y;
+  }
+  const double GC = __shfl(G, 63, 64);
+  Gs[lane] = G;
+  b_s[lane] = bi;
+  __syncthreads();   // norms, G, beta visible; K/Q tiles no longer read
 
-    // P (row-oriented, lane = i), stored transposed: X[j][i] = P[i][j], j <= i
-    for (int j = 0; j < CH; ++j) {
-      const double Gj = __shfl(G, j, 64);
-      if (j <= lane) {
-        const float pij = scale * rq_i * rk_s[j] * expf(static_cast<float>(G - Gj)) * Gqk[lane * GP + j];
-        X[j * CH + lane] = pij;
+  // 6. A (into LDS) and P (kept in registers, in place of the QK^T Gram)
+  {
+    double Gc[4];
+    float rkc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { Gc[m] = Gs[16 * m + lr]; rkc[m] = rk_s[16 * m + lr]; }
+#pragma unroll
+    for (int p = 0; p < 10; ++p) {
+      const int mi = tile_mi(p), mj = tile_mj(p);
+      const int j = 16 * mj + lr;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * mi + 4 * lg + ii;
+        const double Gi = Gs[i];
+        const float dec = (j <= i) ? expf(static_cast<float>(Gi - Gc[mj])) : 0.0f;
+        const float rki = rk_s[i];
+        Aw[i * AP + j] = (j < i) ? b_s[i] * rki * rkc[mj] * dec * gkk[p][ii] : 0.0f;
+        gqk[p][ii] = (j <= i) ? scale * rq_s[i] * rkc[mj] * dec * gqk[p][ii] : 0.0f;
       }
     }
-    // per-token scalars: a = scale rq e^G, b = beta rk e^G, c = rk e^{G_C - G}, beta
-    const float eG = expf(static_cast<float>(G));
-    sc[tile * CH + lane] = make_float4(scale * rq_i * eG, bi * rk_i * eG,
-                                       rk_i * expf(static_cast<float>(GC - G)), bi);
-    if (lane == 0) egc[tile] = expf(static_cast<float>(GC));
+  }
+  __syncthreads();
+
+  // 7. T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
+  //    (lane = (block lg, column lr)), then the off-diagonal blocks
+  //    T_IJ = -T_II * sum_{M=J}^{I-1} A_IM T_MJ on MFMA, one level at a time.
+  {
+    const int I = lg, jc = lr;
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* Ar = Aw + (16 * I + i) * AP + 16 * I;
+      float a0 = (i == jc) ? 1.0f : 0.0f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) {
+        const float prod = Ar[m] * t[m];
+        if ((m & 3) == 0) a0 -= prod; else if ((m & 3) == 1) a1 -= prod; else if ((m & 3) == 2) a2 -= prod; else a3 -= prod;
+      }
+      t[i] = (a0 + a1) + (a2 + a3);
+      Tw[(16 * I + i) * AP + 16 * I + jc] = t[i];
+    }
+  }
+  __syncthreads();
+  constexpr int SP = 20;
+#pragma unroll
+  for (int lvl = 1; lvl <= 3; ++lvl) {
+#pragma unroll
+    for (int I = lvl; I <= 3; ++I) {
+      const int J = I - lvl;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int Mb = J; Mb < I; ++Mb)
+        mm16<BF>(acc, Aw + 16 * I * AP + 16 * Mb, AP, Tw + 16 * Mb * AP + 16 * J, AP, lr, lg);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) scr[(4 * lg + ii) * SP + lr] = acc[ii];
+      __syncthreads();
+      f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+      mm16<BF>(acc2, Tw + 16 * I * AP + 16 * I, AP, scr, SP, lr, lg);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) Tw[(16 * I + 4 * lg + ii) * AP + 16 * J + lr] = -acc2[ii];
+      __syncthreads();
+    }
+  }
+
+  // 8. P into the upper triangle turned by 180 degrees: X[63-i][63-j] = P[i][j], j <= i
+#pragma unroll
+  for (int p = 0; p < 10; ++p) {
+    const int mi = tile_mi(p), mj = tile_mj(p);
+    const int j = 16 * mj + lr;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 16 * mi + 4 * lg + ii;
+      if (j <= i) Tw[(63 - i) * AP + (63 - j)] = gqk[p][ii];
+    }
+  }
+  __syncthreads();
+
+  // 9. packed tile and scalars to the workspace
+  const size_t tile = static_cast<size_t>(c) * nv + h;
+  float* X = tp + tile * CH * CH;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int idx = it * 64 + lane, row = idx >> 4, c4 = (idx & 15) * 4;
+    *reinterpret_cast<float4*>(X + row * CH + c4) = *reinterpret_cast<const float4*>(Tw + row * AP + c4);
+  }
+  const float eG = expf(static_cast<float>(G));
+  const float rk_i = rk_s[lane], rq_i = rq_s[lane];
+  sc[tile * CH + lane] = make_float4(scale * rq_i * eG, bi * rk_i * eG, rk_i * expf(static_cast<float>(GC - G)), bi);
+  if (lane == 0) egc[tile] = expf(static_cast<float>(GC));
+}
+
+// ------------------------------------------------------------------ state: bf16 inputs, 4 waves per 16 columns
+constexpr int KB = 136;   // LDS pitch (bf16) of the K tile
+constexpr int SPT = 132;  // LDS pitch (floats) of S^T [16 columns][128 rows]
+constexpr int UP = 20;    // LDS pitch (floats) of the R / U tiles [64][16]
+
+struct Prefetch {
+  uint4 kt[4];      // this thread's share of the K tile (for the LDS copy)
+  uint4 qf[4];      // Q A-fragments of this wave's token tile (4 k-steps)
+  float4 tf[4];     // T fragments (2 k-steps x 8 floats)
+  float4 pf[4];     // P fragments (2 k-steps x 8 floats, reversed order)
+  float vv[4];      // V values of this lane's 4 accumulator rows
+  float sx, sy, sz, sw;   // per-token scalars of token tid % 64
+  float eg;         // exp(G_C)
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+template <typename TO>
+__global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t qs,
+    int64_t ks, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk, int nv,
+    const int32_t* __restrict__ chunk_off, const float* __restrict__ tp, const float4* __restrict__ sc,
+    const float* __restrict__ egc, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][CH * KB];
+  __shared__ __attribute__((aligned(16))) float St[16 * SPT];
+  __shared__ __attribute__((aligned(16))) float Rs[CH * UP];
+  __shared__ __attribute__((aligned(16))) float Us[CH * UP];
+  __shared__ float4 SCs[2][CH];
+  __shared__ float egcs[2];
+
+  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int slice = bid & 7;
+  const int unit = bid >> 3;               // n * nv + h
+  const int n = unit / nv, h = unit % nv;
+  const int hk = h / (nv / nk);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int col = slice * 16 + lr;
+  const int row = 16 * w + lr;             // this lane's token row as an A-operand row
+  const int nks = (16 * w + 15) / 32 + 1;  // k-steps of the triangular products
+
+  int64_t s_begin, s_end;
+  seq_bounds(cu, n, T, s_begin, s_end);
+  const int cbase = chunk_off[n];
+  const int nchunks = chunk_off[n + 1] - cbase;
+
+  f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (S0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[t][i] = S0[(static_cast<int64_t>(unit) * D + 32 * w + 16 * t + 4 * lg + i) * D + col];
+  }
+
+  auto load_chunk = [&](int cc, Prefetch& pf) {
+    const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+    const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+    const size_t tile = static_cast<size_t>(cbase + cc) * nv + h;
+    // rows past the sequence end read the last valid row and are zeroed by a
+    // select: no branch around a load, so all loads stay in flight together
+    const uint16_t* kb = k + t0 * ks + static_cast<int64_t>(hk) * D;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 256 + tid, r = idx >> 4, seg = idx & 15;
+      pf.kt[it] = zero_if(r >= L, *reinterpret_cast<const uint4*>(kb + min(r, L - 1) * ks + seg * 8));
+    }
+    const uint16_t* qb = q + (t0 + min(row, L - 1)) * qs + static_cast<int64_t>(hk) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pf.qf[s] = zero_if(row >= L, *reinterpret_cast<const uint4*>(qb + 32 * s));
+    const float* X = tp + tile * CH * CH;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {   // (waves 0, 1 only use k-step 0; the rest is masked)
+      pf.tf[2 * s] = *reinterpret_cast<const float4*>(X + row * CH + 32 * s + 8 * lg);
+      pf.tf[2 * s + 1] = *reinterpret_cast<const float4*>(X + row * CH + 32 * s + 8 * lg + 4);
+      const int base = 56 - 32 * s - 8 * lg;
+      pf.pf[2 * s] = *reinterpret_cast<const float4*>(X + (63 - row) * CH + base);
+      pf.pf[2 * s + 1] = *reinterpret_cast<const float4*>(X + (63 - row) * CH + base + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 16 * w + 4 * lg + i;
+      const float vx = bf16_to_f32(v[(t0 + min(tok, L - 1)) * vs + static_cast<int64_t>(h) * D + col]);
+      pf.vv[i] = tok < L ? vx : 0.0f;
+    }
+    const float4 s4 = sc[tile * CH + (tid & (CH - 1))];
+    pf.sx = s4.x; pf.sy = s4.y; pf.sz = s4.z; pf.sw = s4.w;
+    pf.eg = egc[tile];
+  };
+  auto commit = [&](const Prefetch& pf, int buf) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 256 + tid, r = idx >> 4, seg = idx & 15;
+      *reinterpret_cast<uint4*>(&Kt[buf][r * KB + seg * 8]) = pf.kt[it];
+    }
+    if (tid < CH) SCs[buf][tid] = make_float4(pf.sx, pf.sy, pf.sz, pf.sw);
+    if (tid == 0) egcs[buf] = pf.eg;
+  };
+
+  Prefetch cur;
+  if (nchunks > 0) {
+    load_chunk(0, cur);
+    commit(cur, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(&St[lr * SPT + 32 * w + 16 * t + 4 * lg]) = S[t];
+  __syncthreads();
+
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const int buf = cc & 1;
+    // operands of the next chunk (the last iteration re-reads its own chunk:
+    // unconditional, so the prefetch stays in registers)
+    Prefetch nxt;
+    load_chunk(min(cc + 1, nchunks - 1), nxt);
+    const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+    const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+
+    // S (all 128 rows) as B fragments, split into bf16 hi + lo
+    bf16x8 bh[4], bl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float f[8];
+      const float4 u0 = *reinterpret_cast<const float4*>(&St[lr * SPT + 32 * s + 8 * lg]);
+      const float4 u1 = *reinterpret_cast<const float4*>(&St[lr * SPT + 32 * s + 8 * lg + 4]);
+      f[0] = u0.x; f[1] = u0.y; f[2] = u0.z; f[3] = u0.w; f[4] = u1.x; f[5] = u1.y; f[6] = u1.z; f[7] = u1.w;
+      split_bf16x8(f, bh[s], bl[s]);
+    }
+    // X = K S, Y = Q S for token rows 16w..16w+15
+    f32x4 Xa = {0.f, 0.f, 0.f, 0.f}, Ya = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[buf][row * KB + 32 * s + 8 * lg]));
+      const bf16x8 aq = as_bf16x8(cur.qf[s]);
+      Xa = mfma_bf16(ak, bl[s], Xa);
+      Ya = mfma_bf16(aq, bl[s], Ya);
+      Xa = mfma_bf16(ak, bh[s], Xa);
+      Ya = mfma_bf16(aq, bh[s], Ya);
+    }
+    // R = beta v - b X
+    f32x4 Ra;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 16 * w + 4 * lg + i;
+      const float4 s4 = SCs[buf][tok];
+      Ra[i] = s4.w * cur.vv[i] - s4.y * Xa[i];
+      Rs[tok * UP + lr] = Ra[i];
+    }
+    __syncthreads();
+
+    // U = R + T_strict R
+    f32x4 Ua = Ra;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nks) {
+        float a[8], b[8];
+        const float tv[8] = {cur.tf[2 * s].x, cur.tf[2 * s].y, cur.tf[2 * s].z, cur.tf[2 * s].w,
+                             cur.tf[2 * s + 1].x, cur.tf[2 * s + 1].y, cur.tf[2 * s + 1].z, cur.tf[2 * s + 1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kk = 32 * s + 8 * lg + j;
+          a[j] = kk < row ? tv[j] : 0.0f;
+          b[j] = Rs[kk * UP + lr];
+        }
+        Mma<true, false, false>::run(Ua, a, b);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Us[(16 * w + 4 * lg + i) * UP + lr] = Ua[i];
+    __syncthreads();
+
+    // O = a Y + P U
+    f32x4 Oa;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Oa[i] = SCs[buf][16 * w + 4 * lg + i].x * Ya[i];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nks) {
+        float a[8], b[8];
+        const float pv[8] = {cur.pf[2 * s].x, cur.pf[2 * s].y, cur.pf[2 * s].z, cur.pf[2 * s].w,
+                             cur.pf[2 * s + 1].x, cur.pf[2 * s + 1].y, cur.pf[2 * s + 1].z, cur.pf[2 * s + 1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kk = 32 * s + 8 * lg + j;
+          a[j] = kk <= row ? pv[7 - j] : 0.0f;
+          b[j] = Us[kk * UP + lr];
+        }
+        Mma<true, false, false>::run(Oa, a, b);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 16 * w + 4 * lg + i;
+      if (tok < L) Elem<TO>::store(o, ((t0 + tok) * nv + h) * static_cast<int64_t>(D) + col, Oa[i]);
+    }
+
+    // S_w = e^{G_C} S_w + K[:, rows of w]^T (c U)
+    const float eGC = egcs[buf];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[t][i] *= eGC;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        float a[8], b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kk = 32 * s + 8 * lg + j;
+          a[j] = bf16_to_f32(Kt[buf][kk * KB + 32 * w + 16 * t + lr]);
+          b[j] = SCs[buf][kk].z * Us[kk * UP + lr];
+        }
+        Mma<true, true, false>::run(S[t], a, b);
+      }
+    }
+    // publish S for the next chunk (every wave has read St before the barriers above)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(&St[lr * SPT + 32 * w + 16 * t + 4 * lg]) = S[t];
+    commit(nxt, buf ^ 1);
+    cur = nxt;
+    __syncthreads();
+  }
+
+  if (ST) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ST[(static_cast<int64_t>(unit) * D + 32 * w + 16 * t + 4 * lg + i) * D + col] = S[t][i];
   }
 }
 
-// ------------------------------------------------------------------ state recurrence
-template <typename TIn, typename TO, int W>
-__global__ void __launch_bounds__(64 * W) chunk_state_kernel(
+// ------------------------------------------------------------------ state: generic (fp32 inputs), one wave per 16 columns
+constexpr int KP = 132;    // LDS pitch (floats) of 64 x 128 K/Q tiles
+constexpr int RP = 18;     // LDS pitch of the 64 x 16 R / U tiles
+
+template <typename TIn>
+__device__ __forceinline__ void load_tile_64x128(const TIn* __restrict__ base, int64_t tok_stride, int L,
+                                                 float* __restrict__ dst, int tid, int nthreads) {
+  for (int idx = tid; idx < CH * (D / 8); idx += nthreads) {
+    const int row = idx >> 4, seg = idx & 15;
+    float* d = dst + row * KP + seg * 8;
+    if (row < L) {
+      float vals[8];
+      load8(base + row * tok_stride + seg * 8, vals);
+      *reinterpret_cast<float4*>(d) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(vals[4], vals[5], vals[6], vals[7]);
+    } else {
+      *reinterpret_cast<float4*>(d) = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+template <typename TIn, typename TO>
+__global__ void __launch_bounds__(64) chunk_state_generic_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, int64_t qs,
     int64_t ks, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk, int nv,
     const int32_t* __restrict__ chunk_off, const float* __restrict__ tp, const float4* __restrict__ sc,
@@ -279,35 +621,28 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
     TO* __restrict__ o) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int KS = Mma<BF, true, true>::KS, KPL = Mma<BF, true, true>::KPL;
-  constexpr int NT = 64 * W;
-  constexpr int VW = 16 * W;           // value columns per workgroup
-  constexpr int VP = VW + 4;           // LDS pitch of the V tile
 
-  extern __shared__ float smem[];
-  float* Ks = smem;                    // [64][KP]
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  float* Ks = smem_f;                  // [64][KP]
   float* Qs = Ks + CH * KP;            // [64][KP]
-  float* Ts = Qs + CH * KP;            // [64][AP]  packed T | P^T
-  float* Vs = Ts + CH * AP;            // [64][VP]
-  float4* SCs = reinterpret_cast<float4*>(Vs + CH * VP);   // [64]
-  float* Rall = reinterpret_cast<float*>(SCs + CH);        // W x [64][RP]
+  float* Ts = Qs + CH * KP;            // [64][AP]  packed T | rotated P
+  float* Vs = Ts + CH * AP;            // [64][16]
+  float4* SCs = reinterpret_cast<float4*>(Vs + CH * 16);   // [64]
+  float* Rw = reinterpret_cast<float*>(SCs + CH);           // [64][RP]
 
-  const int nblk = D / VW;
   const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int nb = bid % nblk;
-  const int unit = bid / nblk;         // n * nv + h
+  const int nb = bid & 7;
+  const int unit = bid >> 3;
   const int n = unit / nv, h = unit % nv;
   const int hk = h / (nv / nk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int lr = lane & 15, lg = lane >> 4;
-  const int col = nb * VW + wave * 16 + lr;   // this lane's value column
-  float* Rw = Rall + wave * CH * RP;
+  const int col = nb * 16 + lr;
 
   int64_t s_begin, s_end;
   seq_bounds(cu, n, T, s_begin, s_end);
   const int nchunks = chunk_off[n + 1] - chunk_off[n];
 
-  // S in accumulator layout: tile t covers dk rows 16t..16t+15; lane holds
-  // rows 16t + 4*lg + i, column `col`.
   f32x4 S[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
@@ -319,31 +654,21 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
     const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
     const size_t tile = static_cast<size_t>(chunk_off[n] + cc) * nv + h;
-
-    __syncthreads();   // previous chunk's LDS reads are complete
-    load_tile_64x128(k + t0 * ks + static_cast<int64_t>(hk) * D, ks, L, Ks, tid, NT);
-    load_tile_64x128(q + t0 * qs + static_cast<int64_t>(hk) * D, qs, L, Qs, tid, NT);
-    for (int idx = tid; idx < CH * CH / 4; idx += NT) {
-      const int row = idx >> 4, c4 = (idx & 15) * 4;
-      *reinterpret_cast<float4*>(Ts + row * AP + c4) =
-          *reinterpret_cast<const float4*>(tp + tile * CH * CH + row * CH + c4);
+    __syncthreads();
+    load_tile_64x128(k + t0 * ks + static_cast<int64_t>(hk) * D, ks, L, Ks, lane, 64);
+    load_tile_64x128(q + t0 * qs + static_cast<int64_t>(hk) * D, qs, L, Qs, lane, 64);
+    for (int idx = lane; idx < CH * CH / 4; idx += 64) {
+      const int r = idx >> 4, c4 = (idx & 15) * 4;
+      *reinterpret_cast<float4*>(Ts + r * AP + c4) = *reinterpret_cast<const float4*>(tp + tile * CH * CH + r * CH + c4);
     }
-    for (int idx = tid; idx < CH * (VW / 8); idx += NT) {
-      const int row = idx / (VW / 8), seg = idx % (VW / 8);
-      float* d = Vs + row * VP + seg * 8;
-      if (row < L) {
-        load_row8(v + (t0 + row) * vs + static_cast<int64_t>(h) * D + nb * VW + seg * 8, d);
-      } else {
-        *reinterpret_cast<float4*>(d) = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(d + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+    for (int idx = lane; idx < CH * 16; idx += 64) {
+      const int r = idx >> 4, cidx = idx & 15;
+      Vs[idx] = r < L ? Elem<TIn>::load(v, (t0 + r) * vs + static_cast<int64_t>(h) * D + nb * 16 + cidx) : 0.0f;
     }
-    for (int idx = tid; idx < CH; idx += NT) SCs[idx] = sc[tile * CH + idx];
+    SCs[lane] = sc[tile * CH + lane];
     const float eGC = egc[tile];
     __syncthreads();
 
-    // X = K S, Y = Q S (64 x 16 per wave); S is the B operand with the
-    // contraction index ordered as the accumulator holds it.
     f32x4 Xa[4], Ya[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -364,8 +689,6 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
         Mma<BF, true, false>::run(Ya[mt], aq, bs);
       }
     }
-
-    // R = beta v - b X  (accumulator layout), to this wave's LDS tile
     f32x4 Ra[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -373,13 +696,10 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
       for (int i = 0; i < 4; ++i) {
         const int tau = 16 * mt + 4 * lg + i;
         const float4 s4 = SCs[tau];
-        const float rv = s4.w * Vs[tau * VP + wave * 16 + lr] - s4.y * Xa[mt][i];
-        Ra[mt][i] = rv;
-        Rw[tau * RP + lr] = rv;
+        Ra[mt][i] = s4.w * Vs[tau * 16 + lr] - s4.y * Xa[mt][i];
+        Rw[tau * RP + lr] = Ra[mt][i];
       }
     __syncthreads();
-
-    // U = R + T_strict R
     f32x4 Ua[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -403,8 +723,6 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) Rw[(16 * mt + 4 * lg + i) * RP + lr] = Ua[mt][i];
     __syncthreads();
-
-    // O = a Y + P U  (P[i][j] stored at Ts[j][i])
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       f32x4 Oa;
@@ -417,7 +735,7 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
 #pragma unroll
         for (int j = 0; j < KPL; ++j) {
           const int kk = s * KS + KPL * lg + j;
-          a[j] = kk <= row ? Ts[kk * AP + row] : 0.0f;
+          a[j] = kk <= row ? Ts[(63 - row) * AP + (63 - kk)] : 0.0f;
           b[j] = Rw[kk * RP + lr];
         }
         Mma<BF, false, false>::run(Oa, a, b);
@@ -425,12 +743,9 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tau = 16 * mt + 4 * lg + i;
-        if (tau < L)
-          Elem<TO>::store(o, ((t0 + tau) * nv + h) * static_cast<int64_t>(D) + col, Oa[i]);
+        if (tau < L) Elem<TO>::store(o, ((t0 + tau) * nv + h) * static_cast<int64_t>(D) + col, Oa[i]);
       }
     }
-
-    // S = e^{G_C} S + K^T (c U)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
@@ -448,40 +763,17 @@ __global__ void __launch_bounds__(64 * W) chunk_state_kernel(
       }
     }
   }
-
   if (ST) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ST[(static_cast<int64_t>(unit) * D + 16 * t + 4 * lg + i) * D + col] = S[t][i];
+      for (int i = 0; i < 4; ++i)
+        ST[(static_cast<int64_t>(unit) * D + 16 * t + 4 * lg + i) * D + col] = S[t][i];
   }
 }
 
-constexpr size_t prep_lds_bytes() {
-  return (2 * CH * KP + 2 * CH * GP + 2 * CH) * sizeof(float);
-}
-template <int W>
-constexpr size_t state_lds_bytes() {
-  return (2 * CH * KP + CH * AP + CH * (16 * W + 4)) * sizeof(float) + CH * sizeof(float4) +
-         W * CH * RP * sizeof(float);
-}
-static_assert(4 * CH * AP <= 2 * CH * KP, "A tiles must fit in the K/Q region");
-
-template <typename TIn, typename TO, int W>
-hipError_t launch_state(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
-                        const int32_t* cu, int n_seqs, int64_t T, int nk, int nv, const int32_t* chunk_off,
-                        const float* tp, const float4* sc, const float* egc, const float* S0, float* ST,
-                        void* o, hipStream_t s) {
-  auto kern = chunk_state_kernel<TIn, TO, W>;
-  const size_t lds = state_lds_bytes<W>();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  const unsigned grid = static_cast<unsigned>(n_seqs) * nv * (D / (16 * W));
-  kern<<<grid, 64 * W, lds, s>>>(static_cast<const TIn*>(q), static_cast<const TIn*>(k),
-                                 static_cast<const TIn*>(v), qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc,
-                                 egc, S0, ST, static_cast<TO*>(o));
-  return hipGetLastError();
+constexpr size_t generic_lds_bytes() {
+  return (2 * CH * KP + CH * AP + CH * 16) * sizeof(float) + CH * sizeof(float4) + CH * RP * sizeof(float);
 }
 
 template <typename TIn>
@@ -500,32 +792,42 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   chunk_offsets_kernel<<<1, 256, 0, s>>>(cu, n_seqs, T, static_cast<int32_t>(nch), chunk_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-
   {
     auto kern = chunk_prep_kernel<TIn>;
-    const size_t lds = prep_lds_bytes();
+    const size_t lds = prep_lds_bytes<TIn>();
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    kern<<<dim3(static_cast<unsigned>(nch), static_cast<unsigned>(nk)), 256, lds, s>>>(
+    kern<<<dim3(static_cast<unsigned>(nch), static_cast<unsigned>(nv)), 64, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, g, beta, cu, n_seqs, T, nk, nv, scale, l2,
         chunk_off, tp, sc, egc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // 16 value columns per wave; 4 waves per workgroup when there are enough
-  // (sequence, head) units to fill the GPU, else 1 so more CUs share the work.
-  const int64_t units = static_cast<int64_t>(n_seqs) * nv;
-  const bool wide = units * 2 >= 256;
-  if (o_bf16)
-    return wide ? launch_state<TIn, uint16_t, 4>(q, k, v, qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc,
-                                                 egc, S0, ST, o, s)
-                : launch_state<TIn, uint16_t, 1>(q, k, v, qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc,
-                                                 egc, S0, ST, o, s);
-  return wide ? launch_state<TIn, float, 4>(q, k, v, qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc,
-                                            S0, ST, o, s)
-              : launch_state<TIn, float, 1>(q, k, v, qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc,
-                                            S0, ST, o, s);
+  const unsigned grid = static_cast<unsigned>(n_seqs) * nv * (D / 16);
+  if constexpr (sizeof(TIn) == 2) {
+    if (o_bf16)
+      chunk_state_bf16_kernel<uint16_t><<<grid, 256, 0, s>>>(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qs, ks,
+          vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, static_cast<uint16_t*>(o));
+    else
+      chunk_state_bf16_kernel<float><<<grid, 256, 0, s>>>(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qs, ks,
+          vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, static_cast<float*>(o));
+    return hipGetLastError();
+  } else {
+    const size_t lds = generic_lds_bytes();
+    auto launch = [&](auto kern, auto* optr) {
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (err != hipSuccess) return err;
+      kern<<<grid, 64, lds, s>>>(static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
+                                 qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, optr);
+      return hipGetLastError();
+    };
+    if (o_bf16) return launch(chunk_state_generic_kernel<TIn, uint16_t>, static_cast<uint16_t*>(o));
+    return launch(chunk_state_generic_kernel<TIn, float>, static_cast<float*>(o));
+  }
 }
 
 }  // namespace
