@@ -173,6 +173,28 @@ template <bool EA, bool EB> struct Mma16<true, EA, EB> {
   }
 };
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer loads: a 128-bit resource in SGPRs plus a 32-bit VGPR offset per
+// lane. Loads past num_records bytes return 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint16_t bload2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void bstore4(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore2(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- XCD-aware block order
 // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
 // Remap so that logically consecutive work items land on the same XCD and

@@ -133,6 +133,22 @@ __device__ __forceinline__ void copy8_or_zero(const float* src, float* dst, bool
 __device__ __forceinline__ float tof(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float tof(float x) { return x; }
 
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi); four values packed into
+// two dwords per plane (element 0 in the low half of the first dword).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(f32x2v x, uint32_t& hi, uint32_t& lo) {
+  const bf16x2v h = __builtin_convertvector(x, bf16x2v);
+  const f32x2v hf = __builtin_convertvector(h, f32x2v);
+  const f32x2v r = {x.x - hf.x, x.y - hf.y};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
+}
+__device__ __forceinline__ void split4_packed(float4 x, uint2& hi, uint2& lo) {
+  split2(f32x2v{x.x, x.y}, hi.x, lo.x);
+  split2(f32x2v{x.z, x.w}, hi.y, lo.y);
+}
+
 // lower 16x16 tiles of a 64x64 matrix, p = 0..9 -> (mi, mj), mi >= mj
 __device__ __forceinline__ int tile_mi(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
 __device__ __forceinline__ int tile_mj(int p) { const int mi = tile_mi(p); return p - mi * (mi + 1) / 2; }
@@ -208,9 +224,11 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int idx = it * 64 + lane, row = idx >> 4, seg = idx & 15;
-      const int rr = min(row, L - 1);   // clamped read, zeroed below: no branch around the load
-      copy8_or_zero(kb + rr * ks + seg * 8, Ks + row * EP + seg * 8, row >= L);
-      copy8_or_zero(qb + rr * qs + seg * 8, Qs + row * EP + seg * 8, row >= L);
+      // rows past the sequence end re-read the last valid row: their norms
+      // are forced to 0 below, so they contribute nothing to A, P or scalars
+      const int rr = min(row, L - 1);
+      copy8(kb + rr * ks + seg * 8, Ks + row * EP + seg * 8);
+      copy8(qb + rr * qs + seg * 8, Qs + row * EP + seg * 8);
     }
   }
   __syncthreads();
@@ -231,16 +249,25 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
     gqk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / KS; ++s) {
-      float ak[KPL], aq[KPL], bk[KPL];
+      if constexpr (BF) {   // raw bf16 fragments, one 16-byte LDS read each
+        const int kk = s * KS + KPL * lg;
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + (16 * mi + lr) * EP + kk);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + (16 * mi + lr) * EP + kk);
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Ks + (16 * mj + lr) * EP + kk);
+        gkk[p] = mfma_bf16(ak, bk, gkk[p]);
+        gqk[p] = mfma_bf16(aq, bk, gqk[p]);
+      } else {
+        float ak[KPL], aq[KPL], bk[KPL];
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const int kk = s * KS + KPL * lg + j;
-        ak[j] = tof(Ks[(16 * mi + lr) * EP + kk]);
-        aq[j] = tof(Qs[(16 * mi + lr) * EP + kk]);
-        bk[j] = tof(Ks[(16 * mj + lr) * EP + kk]);
+        for (int j = 0; j < KPL; ++j) {
+          const int kk = s * KS + KPL * lg + j;
+          ak[j] = tof(Ks[(16 * mi + lr) * EP + kk]);
+          aq[j] = tof(Qs[(16 * mi + lr) * EP + kk]);
+          bk[j] = tof(Ks[(16 * mj + lr) * EP + kk]);
+        }
+        MG::run(gkk[p], ak, bk);
+        MG::run(gqk[p], aq, bk);
       }
-      MG::run(gkk[p], ak, bk);
-      MG::run(gqk[p], aq, bk);
     }
   }
   // 4. norms: |k_i|^2 from the Gram diagonal (diagonal tiles p = 0, 2, 5, 9)
@@ -353,7 +380,19 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int idx = it * 64 + lane, row = idx >> 4, c4 = (idx & 15) * 4;
-    *reinterpret_cast<float4*>(X + row * CH + c4) = *reinterpret_cast<const float4*>(Tw + row * AP + c4);
+    const float4 x = *reinterpret_cast<const float4*>(Tw + row * AP + c4);
+    if constexpr (BF) {
+      // bf16 inputs: the tile is stored as two bf16 planes, hi = bf16(x) and
+      // lo = bf16(x - hi), each 64 x 64, in the same 16 KB
+      uint16_t* Xh = reinterpret_cast<uint16_t*>(X);
+      uint16_t* Xl = Xh + CH * CH;
+      uint2 hi, lo;
+      split4_packed(x, hi, lo);
+      *reinterpret_cast<uint2*>(Xh + row * CH + c4) = hi;
+      *reinterpret_cast<uint2*>(Xl + row * CH + c4) = lo;
+    } else {
+      *reinterpret_cast<float4*>(X + row * CH + c4) = x;
+    }
   }
   const float eG = expf(static_cast<float>(G));
   const float rk_i = rk_s[lane], rq_i = rq_s[lane];
@@ -362,21 +401,33 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
 }
 
 // ------------------------------------------------------------------ state: bf16 inputs, 4 waves per 16 columns
-constexpr int KB = 136;   // LDS pitch (bf16) of the K tile
-constexpr int SPT = 132;  // LDS pitch (floats) of S^T [16 columns][128 rows]
-constexpr int UP = 20;    // LDS pitch (floats) of the R / U tiles [64][16]
+// Every fp32 operand is split into bf16 hi + lo once, by the wave that
+// produces it, and exchanged through LDS as transposed bf16 planes, so each
+// consumer fragment is one 16-byte LDS read feeding an MFMA directly.
+constexpr int KTP = 72;   // LDS pitch (bf16) of K^T   [128 rows of dk][64 tokens]
+constexpr int SBP = 136;  // LDS pitch (bf16) of S^T   [16 columns][128 rows of dk]
+constexpr int TBP = 72;   // LDS pitch (bf16) of R^T, U^T, (cU)^T [16 columns][64 tokens]
 
 struct Prefetch {
-  uint4 kt[4];      // this thread's share of the K tile (for the LDS copy)
-  uint4 qf[4];      // Q A-fragments of this wave's token tile (4 k-steps)
-  float4 tf[4];     // T fragments (2 k-steps x 8 floats)
-  float4 pf[4];     // P fragments (2 k-steps x 8 floats, reversed order)
-  float vv[4];      // V values of this lane's 4 accumulator rows
+  uint4 kf[4];      // K A-fragments of this wave's token tile (4 k-steps over dk)
+  uint4 qf[4];      // Q A-fragments
+  uint4 th[2], tl[2];   // T fragments (hi / lo planes), 2 k-steps over tokens
+  uint4 ph[2], pl[2];   // P fragments (hi / lo), token order reversed inside a group of 8
+  float vv[4];      // V of this lane's 4 accumulator rows
   float sx, sy, sz, sw;   // per-token scalars of token tid % 64
   float eg;         // exp(G_C)
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ uint4 and4(const uint4& a, const uint4& m) {
+  return make_uint4(a.x & m.x, a.y & m.y, a.z & m.z, a.w & m.w);
+}
+// reverse the order of 8 packed bf16
+__device__ __forceinline__ uint4 rev8(const uint4& a) {
+  auto sw = [](uint32_t d) { return (d >> 16) | (d << 16); };
+  return make_uint4(sw(a.w), sw(a.z), sw(a.y), sw(a.x));
+}
+__device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <typename TO>
 __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
@@ -384,10 +435,15 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     int64_t ks, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk, int nv,
     const int32_t* __restrict__ chunk_off, const float* __restrict__ tp, const float4* __restrict__ sc,
     const float* __restrict__ egc, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][CH * KB];
-  __shared__ __attribute__((aligned(16))) float St[16 * SPT];
-  __shared__ __attribute__((aligned(16))) float Rs[CH * UP];
-  __shared__ __attribute__((aligned(16))) float Us[CH * UP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ktt[2][D * KTP];
+  __shared__ __attribute__((aligned(16))) uint16_t Sth[16 * SBP];
+  __shared__ __attribute__((aligned(16))) uint16_t Stl[16 * SBP];
+  __shared__ __attribute__((aligned(16))) uint16_t RTh[16 * TBP];
+  __shared__ __attribute__((aligned(16))) uint16_t RTl[16 * TBP];
+  __shared__ __attribute__((aligned(16))) uint16_t UTh[16 * TBP];
+  __shared__ __attribute__((aligned(16))) uint16_t UTl[16 * TBP];
+  __shared__ __attribute__((aligned(16))) uint16_t CTh[16 * TBP];
+  __shared__ __attribute__((aligned(16))) uint16_t CTl[16 * TBP];
   __shared__ float4 SCs[2][CH];
   __shared__ float egcs[2];
 
@@ -402,6 +458,23 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   const int row = 16 * w + lr;             // this lane's token row as an A-operand row
   const int nks = (16 * w + 15) / 32 + 1;  // k-steps of the triangular products
 
+  // masks of the triangular fragments (constant over chunks): T needs
+  // token < row, P needs token <= row (P slot j holds token 32s+8lg+7-j)
+  uint4 mT[2], mP[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    uint32_t mt[4], mp[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int k0 = 32 * s + 8 * lg + 2 * d;
+      mt[d] = (k0 < row ? 0x0000ffffu : 0u) | (k0 + 1 < row ? 0xffff0000u : 0u);
+      const int p0 = 32 * s + 8 * lg + 7 - 2 * d;
+      mp[d] = (p0 <= row ? 0x0000ffffu : 0u) | (p0 - 1 <= row ? 0xffff0000u : 0u);
+    }
+    mT[s] = make_uint4(mt[0], mt[1], mt[2], mt[3]);
+    mP[s] = make_uint4(mp[0], mp[1], mp[2], mp[3]);
+  }
+
   int64_t s_begin, s_end;
   seq_bounds(cu, n, T, s_begin, s_end);
   const int cbase = chunk_off[n];
@@ -415,171 +488,212 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
       for (int i = 0; i < 4; ++i) S[t][i] = S0[(static_cast<int64_t>(unit) * D + 32 * w + 16 * t + 4 * lg + i) * D + col];
   }
 
+  // lane-constant parts of the operand offsets (bytes)
+  const uint32_t ko0 = static_cast<uint32_t>(row * ks * 2 + 16 * lg);
+  const uint32_t qo0 = static_cast<uint32_t>(row * qs * 2 + 16 * lg);
+  const uint32_t to0 = static_cast<uint32_t>((row * CH + 8 * lg) * 2);
+  const uint32_t po0 = static_cast<uint32_t>(((63 - row) * CH + 56 - 8 * lg) * 2);
+  const uint32_t vo0 = static_cast<uint32_t>(((16 * w + 4 * lg) * vs + col) * 2);
+
   auto load_chunk = [&](int cc, Prefetch& pf) {
     const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
     const size_t tile = static_cast<size_t>(cbase + cc) * nv + h;
-    // rows past the sequence end read the last valid row and are zeroed by a
-    // select: no branch around a load, so all loads stay in flight together
-    const uint16_t* kb = k + t0 * ks + static_cast<int64_t>(hk) * D;
+    // Per-chunk buffer resources sized to the chunk's valid rows: rows past
+    // the sequence end read as zeros, with no branch around any load.
+    const rsrc_t rk = make_rsrc(k + t0 * ks + static_cast<int64_t>(hk) * D,
+                                static_cast<uint32_t>(((L - 1) * ks + D) * 2));
+    const rsrc_t rq = make_rsrc(q + t0 * qs + static_cast<int64_t>(hk) * D,
+                                static_cast<uint32_t>(((L - 1) * qs + D) * 2));
+    const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
+                                static_cast<uint32_t>(((L - 1) * vs + D) * 2));
+    const rsrc_t rx = make_rsrc(tp + tile * CH * CH, CH * CH * 4);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * 256 + tid, r = idx >> 4, seg = idx & 15;
-      pf.kt[it] = zero_if(r >= L, *reinterpret_cast<const uint4*>(kb + min(r, L - 1) * ks + seg * 8));
-    }
-    const uint16_t* qb = q + (t0 + min(row, L - 1)) * qs + static_cast<int64_t>(hk) * D + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) pf.qf[s] = zero_if(row >= L, *reinterpret_cast<const uint4*>(qb + 32 * s));
-    const float* X = tp + tile * CH * CH;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {   // (waves 0, 1 only use k-step 0; the rest is masked)
-      pf.tf[2 * s] = *reinterpret_cast<const float4*>(X + row * CH + 32 * s + 8 * lg);
-      pf.tf[2 * s + 1] = *reinterpret_cast<const float4*>(X + row * CH + 32 * s + 8 * lg + 4);
-      const int base = 56 - 32 * s - 8 * lg;
-      pf.pf[2 * s] = *reinterpret_cast<const float4*>(X + (63 - row) * CH + base);
-      pf.pf[2 * s + 1] = *reinterpret_cast<const float4*>(X + (63 - row) * CH + base + 4);
+    for (int s = 0; s < 4; ++s) {
+      pf.kf[s] = bload16(rk, ko0 + 64 * s);
+      pf.qf[s] = bload16(rq, qo0 + 64 * s);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * w + 4 * lg + i;
-      const float vx = bf16_to_f32(v[(t0 + min(tok, L - 1)) * vs + static_cast<int64_t>(h) * D + col]);
-      pf.vv[i] = tok < L ? vx : 0.0f;
+    for (int s = 0; s < 2; ++s) {   // hi plane, then lo plane 8 KB further
+      pf.th[s] = bload16(rx, to0 + 64 * s);
+      pf.tl[s] = bload16(rx, to0 + 64 * s + CH * CH * 2);
+      pf.ph[s] = bload16(rx, po0 - 64 * s);
+      pf.pl[s] = bload16(rx, po0 - 64 * s + CH * CH * 2);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf.vv[i] = bf16_to_f32(bload2(rv, vo0 + static_cast<uint32_t>(i * vs * 2)));
     const float4 s4 = sc[tile * CH + (tid & (CH - 1))];
     pf.sx = s4.x; pf.sy = s4.y; pf.sz = s4.z; pf.sw = s4.w;
-    pf.eg = egc[tile];
+    // exp(G_C) through a vector load: a uniform (scalar) load would share
+    // lgkmcnt with LDS traffic and stall the next LDS wait for a full memory
+    // round trip
+    pf.eg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(egc + tile, 4), static_cast<uint32_t>(tid & 0), 0, 0));
   };
+  // K^T of the chunk into LDS from the waves' own K fragments
   auto commit = [&](const Prefetch& pf, int buf) {
+    uint16_t* Kb = Ktt[buf];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * 256 + tid, r = idx >> 4, seg = idx & 15;
-      *reinterpret_cast<uint4*>(&Kt[buf][r * KB + seg * 8]) = pf.kt[it];
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t d[4] = {pf.kf[s].x, pf.kf[s].y, pf.kf[s].z, pf.kf[s].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        Kb[(32 * s + 8 * lg + j) * KTP + row] = static_cast<uint16_t>((j & 1) ? (d[j >> 1] >> 16) : (d[j >> 1] & 0xffffu));
     }
     if (tid < CH) SCs[buf][tid] = make_float4(pf.sx, pf.sy, pf.sz, pf.sw);
     if (tid == 0) egcs[buf] = pf.eg;
   };
-
-  Prefetch cur;
-  if (nchunks > 0) {
-    load_chunk(0, cur);
-    commit(cur, 0);
-  }
+  auto publish_S = [&]() {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(&St[lr * SPT + 32 * w + 16 * t + 4 * lg]) = S[t];
-  __syncthreads();
-
-  for (int cc = 0; cc < nchunks; ++cc) {
-    const int buf = cc & 1;
-    // operands of the next chunk (the last iteration re-reads its own chunk:
-    // unconditional, so the prefetch stays in registers)
-    Prefetch nxt;
-    load_chunk(min(cc + 1, nchunks - 1), nxt);
-    const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
-    const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-
-    // S (all 128 rows) as B fragments, split into bf16 hi + lo
-    bf16x8 bh[4], bl[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float f[8];
-      const float4 u0 = *reinterpret_cast<const float4*>(&St[lr * SPT + 32 * s + 8 * lg]);
-      const float4 u1 = *reinterpret_cast<const float4*>(&St[lr * SPT + 32 * s + 8 * lg + 4]);
-      f[0] = u0.x; f[1] = u0.y; f[2] = u0.z; f[3] = u0.w; f[4] = u1.x; f[5] = u1.y; f[6] = u1.z; f[7] = u1.w;
-      split_bf16x8(f, bh[s], bl[s]);
+    for (int t = 0; t < 2; ++t) {
+      uint2 hi, lo;
+      split4_packed(make_float4(S[t][0], S[t][1], S[t][2], S[t][3]), hi, lo);
+      *reinterpret_cast<uint2*>(&Sth[lr * SBP + 32 * w + 16 * t + 4 * lg]) = hi;
+      *reinterpret_cast<uint2*>(&Stl[lr * SBP + 32 * w + 16 * t + 4 * lg]) = lo;
     }
-    // X = K S, Y = Q S for token rows 16w..16w+15
+  };
+
+  // The output tile of chunk c is stored at the start of chunk c+1, after that
+  // chunk's prefetch loads are issued: loads and stores share one in-order
+  // completion counter, so a store issued before a load would make every
+  // wait on that load also wait for the store to reach memory.
+  f32x4 Opend = {0.f, 0.f, 0.f, 0.f};
+  int cc_pend = -1;
+  const uint32_t oo0 = static_cast<uint32_t>(((16 * w + 4 * lg) * nv * D + col) * sizeof(TO));
+  auto store_pending = [&]() {
+    const int64_t t0 = s_begin + static_cast<int64_t>(cc_pend) * CH;
+    const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+    const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
+                                static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = oo0 + static_cast<uint32_t>(i * nv * D * sizeof(TO));
+      if constexpr (sizeof(TO) == 4) bstore4(ro, off, Opend[i]);
+      else bstore2(ro, off, f32_to_bf16(Opend[i]));
+    }
+  };
+
+  // One chunk: prefetch the next chunk's operands into `nxt`, compute with
+  // `cur`, then stage `nxt` for the next iteration. The loop below alternates
+  // two register buffers so no copy is made between chunks.
+  auto step = [&](int cc, const Prefetch& cur, Prefetch& nxt) {
+    const int buf = cc & 1;
+    // (the last chunk re-reads itself: unconditional, so loads stay in registers)
+    load_chunk(min(cc + 1, nchunks - 1), nxt);
+    if (cc_pend >= 0) store_pending();
+
+    // X = K S, Y = Q S for token rows 16w..16w+15 (S as pre-split B fragments)
     f32x4 Xa = {0.f, 0.f, 0.f, 0.f}, Ya = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[buf][row * KB + 32 * s + 8 * lg]));
+      const bf16x8 bh = as_bf16x8(lds16(&Sth[lr * SBP + 32 * s + 8 * lg]));
+      const bf16x8 bl = as_bf16x8(lds16(&Stl[lr * SBP + 32 * s + 8 * lg]));
+      const bf16x8 ak = as_bf16x8(cur.kf[s]);
       const bf16x8 aq = as_bf16x8(cur.qf[s]);
-      Xa = mfma_bf16(ak, bl[s], Xa);
-      Ya = mfma_bf16(aq, bl[s], Ya);
-      Xa = mfma_bf16(ak, bh[s], Xa);
-      Ya = mfma_bf16(aq, bh[s], Ya);
+      Xa = mfma_bf16(ak, bl, Xa);
+      Ya = mfma_bf16(aq, bl, Ya);
+      Xa = mfma_bf16(ak, bh, Xa);
+      Ya = mfma_bf16(aq, bh, Ya);
     }
-    // R = beta v - b X
+    // R = beta v - b X -> R^T planes
     f32x4 Ra;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * w + 4 * lg + i;
-      const float4 s4 = SCs[buf][tok];
+      const float4 s4 = SCs[buf][16 * w + 4 * lg + i];
       Ra[i] = s4.w * cur.vv[i] - s4.y * Xa[i];
-      Rs[tok * UP + lr] = Ra[i];
+    }
+    {
+      uint2 hi, lo;
+      split4_packed(make_float4(Ra[0], Ra[1], Ra[2], Ra[3]), hi, lo);
+      *reinterpret_cast<uint2*>(&RTh[lr * TBP + 16 * w + 4 * lg]) = hi;
+      *reinterpret_cast<uint2*>(&RTl[lr * TBP + 16 * w + 4 * lg]) = lo;
     }
     __syncthreads();
 
-    // U = R + T_strict R
+    // U = R + T_strict R -> U^T and (c U)^T planes
     f32x4 Ua = Ra;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < nks) {
-        float a[8], b[8];
-        const float tv[8] = {cur.tf[2 * s].x, cur.tf[2 * s].y, cur.tf[2 * s].z, cur.tf[2 * s].w,
-                             cur.tf[2 * s + 1].x, cur.tf[2 * s + 1].y, cur.tf[2 * s + 1].z, cur.tf[2 * s + 1].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kk = 32 * s + 8 * lg + j;
-          a[j] = kk < row ? tv[j] : 0.0f;
-          b[j] = Rs[kk * UP + lr];
-        }
-        Mma<true, false, false>::run(Ua, a, b);
+        const bf16x8 ah = as_bf16x8(and4(cur.th[s], mT[s]));
+        const bf16x8 al = as_bf16x8(and4(cur.tl[s], mT[s]));
+        const bf16x8 bh = as_bf16x8(lds16(&RTh[lr * TBP + 32 * s + 8 * lg]));
+        const bf16x8 bl = as_bf16x8(lds16(&RTl[lr * TBP + 32 * s + 8 * lg]));
+        Ua = mfma_bf16(al, bh, Ua);
+        Ua = mfma_bf16(ah, bl, Ua);
+        Ua = mfma_bf16(ah, bh, Ua);
       }
     }
+    {
+      uint2 hi, lo;
+      split4_packed(make_float4(Ua[0], Ua[1], Ua[2], Ua[3]), hi, lo);
+      *reinterpret_cast<uint2*>(&UTh[lr * TBP + 16 * w + 4 * lg]) = hi;
+      *reinterpret_cast<uint2*>(&UTl[lr * TBP + 16 * w + 4 * lg]) = lo;
+      float cu4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Us[(16 * w + 4 * lg + i) * UP + lr] = Ua[i];
+      for (int i = 0; i < 4; ++i) cu4[i] = SCs[buf][16 * w + 4 * lg + i].z * Ua[i];
+      split4_packed(make_float4(cu4[0], cu4[1], cu4[2], cu4[3]), hi, lo);
+      *reinterpret_cast<uint2*>(&CTh[lr * TBP + 16 * w + 4 * lg]) = hi;
+      *reinterpret_cast<uint2*>(&CTl[lr * TBP + 16 * w + 4 * lg]) = lo;
+    }
     __syncthreads();
 
-    // O = a Y + P U
+    // O = a Y + P U (P fragments hold tokens in reversed order: reverse U too)
     f32x4 Oa;
 #pragma unroll
     for (int i = 0; i < 4; ++i) Oa[i] = SCs[buf][16 * w + 4 * lg + i].x * Ya[i];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < nks) {
-        float a[8], b[8];
-        const float pv[8] = {cur.pf[2 * s].x, cur.pf[2 * s].y, cur.pf[2 * s].z, cur.pf[2 * s].w,
-                             cur.pf[2 * s + 1].x, cur.pf[2 * s + 1].y, cur.pf[2 * s + 1].z, cur.pf[2 * s + 1].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kk = 32 * s + 8 * lg + j;
-          a[j] = kk <= row ? pv[7 - j] : 0.0f;
-          b[j] = Us[kk * UP + lr];
-        }
-        Mma<true, false, false>::run(Oa, a, b);
+        const bf16x8 ah = as_bf16x8(and4(cur.ph[s], mP[s]));
+        const bf16x8 al = as_bf16x8(and4(cur.pl[s], mP[s]));
+        const bf16x8 bh = as_bf16x8(rev8(lds16(&UTh[lr * TBP + 32 * s + 8 * lg])));
+        const bf16x8 bl = as_bf16x8(rev8(lds16(&UTl[lr * TBP + 32 * s + 8 * lg])));
+        Oa = mfma_bf16(al, bh, Oa);
+        Oa = mfma_bf16(ah, bl, Oa);
+        Oa = mfma_bf16(ah, bh, Oa);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * w + 4 * lg + i;
-      if (tok < L) Elem<TO>::store(o, ((t0 + tok) * nv + h) * static_cast<int64_t>(D) + col, Oa[i]);
-    }
+    Opend = Oa;          // stored at the start of the next chunk
+    cc_pend = cc;
 
     // S_w = e^{G_C} S_w + K[:, rows of w]^T (c U)
     const float eGC = egcs[buf];
+    bf16x8 ch[2], cl[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      ch[s] = as_bf16x8(lds16(&CTh[lr * TBP + 32 * s + 8 * lg]));
+      cl[s] = as_bf16x8(lds16(&CTl[lr * TBP + 32 * s + 8 * lg]));
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[t][i] *= eGC;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        float a[8], b[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kk = 32 * s + 8 * lg + j;
-          a[j] = bf16_to_f32(Kt[buf][kk * KB + 32 * w + 16 * t + lr]);
-          b[j] = SCs[buf][kk].z * Us[kk * UP + lr];
-        }
-        Mma<true, true, false>::run(S[t], a, b);
+        const bf16x8 a = as_bf16x8(lds16(&Ktt[buf][(32 * w + 16 * t + lr) * KTP + 32 * s + 8 * lg]));
+        S[t] = mfma_bf16(a, cl[s], S[t]);
+        S[t] = mfma_bf16(a, ch[s], S[t]);
       }
     }
-    // publish S for the next chunk (every wave has read St before the barriers above)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(&St[lr * SPT + 32 * w + 16 * t + 4 * lg]) = S[t];
+    // publish S for the next chunk (every wave has read S^T before the barriers above)
+    publish_S();
     commit(nxt, buf ^ 1);
-    cur = nxt;
     __syncthreads();
+  };
+
+  Prefetch pa, pb;
+  if (nchunks > 0) {
+    load_chunk(0, pa);
+    commit(pa, 0);
   }
+  publish_S();
+  __syncthreads();
+  for (int cc = 0; cc < nchunks; cc += 2) {
+    step(cc, pa, pb);
+    if (cc + 1 < nchunks) step(cc + 1, pb, pa);
+  }
+  if (cc_pend >= 0) store_pending();
 
   if (ST) {
 #pragma unroll
