@@ -400,8 +400,15 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
   if (lane == 0) egc[tile] = expf(static_cast<float>(GC));
 }
 
-// ------------------------------------------------------------------ state: bf16 inputs, 4 waves per 16 columns
-// Every fp32 operand is split into bf16 hi + lo once, by the wave that
+// ------------------------------------------------------------------ state: bf16 inputs, 8 waves per 16 columns
+// One workgroup per (sequence, value head, 16 value columns), eight waves with
+// two roles over the chunk's four 16-token tiles m = w % 4:
+//   waves 0-3 (recurrence side): X = K S, R = beta v - b X, U = R + T R;
+//   waves 4-7 (output side):     Y = Q S, O = a Y + P U.
+// Wave w also owns rows 16w..16w+15 of S (128 x 16, fp32, one MFMA
+// accumulator) and updates them: S_w = e^{G_C} S_w + K[:, rows]^T (c U).
+// Waves w and w+4 share a SIMD, so each SIMD interleaves one wave of each
+// side. Every fp32 operand is split into bf16 hi + lo once, by the wave that
 // produces it, and exchanged through LDS as transposed bf16 planes, so each
 // consumer fragment is one 16-byte LDS read feeding an MFMA directly.
 constexpr int KTP = 72;   // LDS pitch (bf16) of K^T   [128 rows of dk][64 tokens]
@@ -409,14 +416,18 @@ constexpr int SBP = 136;  // LDS pitch (bf16) of S^T   [16 columns][128 rows of 
 constexpr int TBP = 72;   // LDS pitch (bf16) of R^T, U^T, (cU)^T [16 columns][64 tokens]
 
 struct Prefetch {
-  uint4 kf[4];      // K A-fragments of this wave's token tile (4 k-steps over dk)
-  uint4 qf[4];      // Q A-fragments
-  uint4 th[2], tl[2];   // T fragments (hi / lo planes), 2 k-steps over tokens
-  uint4 ph[2], pl[2];   // P fragments (hi / lo), token order reversed inside a group of 8
-  float vv[4];      // V of this lane's 4 accumulator rows
-  float sx, sy, sz, sw;   // per-token scalars of token tid % 64
-  float eg;         // exp(G_C)
+  uint4 f[4];       // K (recurrence side) or Q (output side) A-fragments, 4 k-steps over dk
+  uint4 x[4];       // T (recurrence) or P (output) fragments: [hi k0, hi k1, lo k0, lo k1]
+  // Raw loaded words only: any arithmetic on a prefetched value at load time
+  // would force a wait for that load (and every load issued before it).
+  uint32_t vv[4];   // V (bf16 in the low half) of this lane's 4 accumulator rows
+  uint4 scv;        // per-token scalars (a, b, c, beta) of token lane, fp32 bits (recurrence side)
+  uint32_t eg;      // exp(G_C) bits (every wave)
 };
+// Every loaded word is consumed on every path of every wave that loads it.
+// A register whose load is still counted as pending when the compiler reuses
+// it makes it wait on the in-order counter, and with it on every load issued
+// since -- including the look-ahead loads of later chunks.
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ uint4 and4(const uint4& a, const uint4& m) {
@@ -430,7 +441,7 @@ __device__ __forceinline__ uint4 rev8(const uint4& a) {
 __device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <typename TO>
-__global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
+__global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t qs,
     int64_t ks, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk, int nv,
     const int32_t* __restrict__ chunk_off, const float* __restrict__ tp, const float4* __restrict__ sc,
@@ -445,34 +456,38 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t CTh[16 * TBP];
   __shared__ __attribute__((aligned(16))) uint16_t CTl[16 * TBP];
   __shared__ float4 SCs[2][CH];
-  __shared__ float egcs[2];
 
   const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int slice = bid & 7;
   const int unit = bid >> 3;               // n * nv + h
   const int n = unit / nv, h = unit % nv;
   const int hk = h / (nv / nk);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is wave-uniform; say so, so that every wave-level value
+  // (role, tile, buffer descriptors) lives in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool rec = w < 4;                  // recurrence side (wave-uniform)
+  const int m = w & 3;                     // token tile of this wave
   const int lr = lane & 15, lg = lane >> 4;
   const int col = slice * 16 + lr;
-  const int row = 16 * w + lr;             // this lane's token row as an A-operand row
-  const int nks = (16 * w + 15) / 32 + 1;  // k-steps of the triangular products
+  const int row = 16 * m + lr;             // this lane's token row as an A-operand row
 
   // masks of the triangular fragments (constant over chunks): T needs
   // token < row, P needs token <= row (P slot j holds token 32s+8lg+7-j)
-  uint4 mT[2], mP[2];
+  uint4 msk[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    uint32_t mt[4], mp[4];
+    uint32_t mm[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const int k0 = 32 * s + 8 * lg + 2 * d;
-      mt[d] = (k0 < row ? 0x0000ffffu : 0u) | (k0 + 1 < row ? 0xffff0000u : 0u);
-      const int p0 = 32 * s + 8 * lg + 7 - 2 * d;
-      mp[d] = (p0 <= row ? 0x0000ffffu : 0u) | (p0 - 1 <= row ? 0xffff0000u : 0u);
+      if (rec) {
+        const int k0 = 32 * s + 8 * lg + 2 * d;
+        mm[d] = (k0 < row ? 0x0000ffffu : 0u) | (k0 + 1 < row ? 0xffff0000u : 0u);
+      } else {
+        const int p0 = 32 * s + 8 * lg + 7 - 2 * d;
+        mm[d] = (p0 <= row ? 0x0000ffffu : 0u) | (p0 - 1 <= row ? 0xffff0000u : 0u);
+      }
     }
-    mT[s] = make_uint4(mt[0], mt[1], mt[2], mt[3]);
-    mP[s] = make_uint4(mp[0], mp[1], mp[2], mp[3]);
+    msk[s] = make_uint4(mm[0], mm[1], mm[2], mm[3]);
   }
 
   int64_t s_begin, s_end;
@@ -480,20 +495,18 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   const int cbase = chunk_off[n];
   const int nchunks = chunk_off[n + 1] - cbase;
 
-  f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 S = {0.f, 0.f, 0.f, 0.f};        // rows 16w + 4lg + i, column col
   if (S0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[t][i] = S0[(static_cast<int64_t>(unit) * D + 32 * w + 16 * t + 4 * lg + i) * D + col];
+    for (int i = 0; i < 4; ++i) S[i] = S0[(static_cast<int64_t>(unit) * D + 16 * w + 4 * lg + i) * D + col];
   }
 
   // lane-constant parts of the operand offsets (bytes)
-  const uint32_t ko0 = static_cast<uint32_t>(row * ks * 2 + 16 * lg);
-  const uint32_t qo0 = static_cast<uint32_t>(row * qs * 2 + 16 * lg);
-  const uint32_t to0 = static_cast<uint32_t>((row * CH + 8 * lg) * 2);
-  const uint32_t po0 = static_cast<uint32_t>(((63 - row) * CH + 56 - 8 * lg) * 2);
-  const uint32_t vo0 = static_cast<uint32_t>(((16 * w + 4 * lg) * vs + col) * 2);
+  const uint32_t fo0 = static_cast<uint32_t>(row * (rec ? ks : qs) * 2 + 16 * lg);
+  const uint32_t xo0 = rec ? static_cast<uint32_t>((row * CH + 8 * lg) * 2)
+                           : static_cast<uint32_t>(((63 - row) * CH + 56 - 8 * lg) * 2);
+  const int xstep = rec ? 64 : -64;        // byte step of one k-step along the fragment row
+  const uint32_t vo0 = static_cast<uint32_t>(((16 * m + 4 * lg) * vs + col) * 2);
 
   auto load_chunk = [&](int cc, Prefetch& pf) {
     const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
@@ -501,56 +514,51 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     const size_t tile = static_cast<size_t>(cbase + cc) * nv + h;
     // Per-chunk buffer resources sized to the chunk's valid rows: rows past
     // the sequence end read as zeros, with no branch around any load.
-    const rsrc_t rk = make_rsrc(k + t0 * ks + static_cast<int64_t>(hk) * D,
-                                static_cast<uint32_t>(((L - 1) * ks + D) * 2));
-    const rsrc_t rq = make_rsrc(q + t0 * qs + static_cast<int64_t>(hk) * D,
-                                static_cast<uint32_t>(((L - 1) * qs + D) * 2));
-    const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
-                                static_cast<uint32_t>(((L - 1) * vs + D) * 2));
+    const uint16_t* fb = rec ? k : q;
+    const int64_t fs = rec ? ks : qs;
+    const rsrc_t rf = make_rsrc(fb + t0 * fs + static_cast<int64_t>(hk) * D,
+                                static_cast<uint32_t>(((L - 1) * fs + D) * 2));
     const rsrc_t rx = make_rsrc(tp + tile * CH * CH, CH * CH * 4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      pf.kf[s] = bload16(rk, ko0 + 64 * s);
-      pf.qf[s] = bload16(rq, qo0 + 64 * s);
-    }
+    for (int s = 0; s < 4; ++s) pf.f[s] = bload16(rf, fo0 + 64 * s);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {   // hi plane, then lo plane 8 KB further
-      pf.th[s] = bload16(rx, to0 + 64 * s);
-      pf.tl[s] = bload16(rx, to0 + 64 * s + CH * CH * 2);
-      pf.ph[s] = bload16(rx, po0 - 64 * s);
-      pf.pl[s] = bload16(rx, po0 - 64 * s + CH * CH * 2);
+      pf.x[s] = bload16(rx, xo0 + xstep * s);
+      pf.x[2 + s] = bload16(rx, xo0 + xstep * s + CH * CH * 2);
     }
+    if (rec) {
+      const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
+                                  static_cast<uint32_t>(((L - 1) * vs + D) * 2));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf.vv[i] = bf16_to_f32(bload2(rv, vo0 + static_cast<uint32_t>(i * vs * 2)));
-    const float4 s4 = sc[tile * CH + (tid & (CH - 1))];
-    pf.sx = s4.x; pf.sy = s4.y; pf.sz = s4.z; pf.sw = s4.w;
+      for (int i = 0; i < 4; ++i) pf.vv[i] = bload2(rv, vo0 + static_cast<uint32_t>(i * vs * 2));
+      pf.scv = bload16(make_rsrc(sc + tile * CH, CH * 16), static_cast<uint32_t>(lane * 16));
+    }
     // exp(G_C) through a vector load: a uniform (scalar) load would share
-    // lgkmcnt with LDS traffic and stall the next LDS wait for a full memory
-    // round trip
-    pf.eg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-        make_rsrc(egc + tile, 4), static_cast<uint32_t>(tid & 0), 0, 0));
+    // lgkmcnt with LDS traffic and stall the next LDS wait for a full
+    // memory round trip
+    pf.eg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + tile, 4), static_cast<uint32_t>(lane & 0), 0, 0);
   };
-  // K^T of the chunk into LDS from the waves' own K fragments
+  // stage the next chunk: K^T into LDS from the recurrence waves' K fragments
   auto commit = [&](const Prefetch& pf, int buf) {
-    uint16_t* Kb = Ktt[buf];
+    if (rec) {
+      uint16_t* Kb = Ktt[buf];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t d[4] = {pf.kf[s].x, pf.kf[s].y, pf.kf[s].z, pf.kf[s].w};
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t d[4] = {pf.f[s].x, pf.f[s].y, pf.f[s].z, pf.f[s].w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        Kb[(32 * s + 8 * lg + j) * KTP + row] = static_cast<uint16_t>((j & 1) ? (d[j >> 1] >> 16) : (d[j >> 1] & 0xffffu));
+        for (int j = 0; j < 8; ++j)
+          Kb[(32 * s + 8 * lg + j) * KTP + row] =
+              static_cast<uint16_t>((j & 1) ? (d[j >> 1] >> 16) : (d[j >> 1] & 0xffffu));
+      }
+      // (all four recurrence waves write the same values: see Prefetch)
+      *reinterpret_cast<uint4*>(&SCs[buf][lane]) = pf.scv;
     }
-    if (tid < CH) SCs[buf][tid] = make_float4(pf.sx, pf.sy, pf.sz, pf.sw);
-    if (tid == 0) egcs[buf] = pf.eg;
   };
   auto publish_S = [&]() {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint2 hi, lo;
-      split4_packed(make_float4(S[t][0], S[t][1], S[t][2], S[t][3]), hi, lo);
-      *reinterpret_cast<uint2*>(&Sth[lr * SBP + 32 * w + 16 * t + 4 * lg]) = hi;
-      *reinterpret_cast<uint2*>(&Stl[lr * SBP + 32 * w + 16 * t + 4 * lg]) = lo;
-    }
+    uint2 hi, lo;
+    split4_packed(make_float4(S[0], S[1], S[2], S[3]), hi, lo);
+    *reinterpret_cast<uint2*>(&Sth[lr * SBP + 16 * w + 4 * lg]) = hi;
+    *reinterpret_cast<uint2*>(&Stl[lr * SBP + 16 * w + 4 * lg]) = lo;
   };
 
   // The output tile of chunk c is stored at the start of chunk c+1, after that
@@ -559,7 +567,7 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   // wait on that load also wait for the store to reach memory.
   f32x4 Opend = {0.f, 0.f, 0.f, 0.f};
   int cc_pend = -1;
-  const uint32_t oo0 = static_cast<uint32_t>(((16 * w + 4 * lg) * nv * D + col) * sizeof(TO));
+  const uint32_t oo0 = static_cast<uint32_t>(((16 * m + 4 * lg) * nv * D + col) * sizeof(TO));
   auto store_pending = [&]() {
     const int64_t t0 = s_begin + static_cast<int64_t>(cc_pend) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
@@ -573,107 +581,95 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     }
   };
 
-  // One chunk: prefetch the next chunk's operands into `nxt`, compute with
-  // `cur`, then stage `nxt` for the next iteration. The loop below alternates
-  // two register buffers so no copy is made between chunks.
-  auto step = [&](int cc, const Prefetch& cur, Prefetch& nxt) {
+  // One chunk: issue the loads of chunk cc+2 into `nxt2`, compute chunk cc
+  // with `cur`, then stage chunk cc+1 (`nxt`, loaded one chunk ago) in LDS.
+  // Three register buffers rotate, so no copy is made between chunks and
+  // every load has two chunks of compute to arrive.
+  auto step = [&](int cc, const Prefetch& cur, const Prefetch& nxt, Prefetch& nxt2) {
     const int buf = cc & 1;
-    // (the last chunk re-reads itself: unconditional, so loads stay in registers)
-    load_chunk(min(cc + 1, nchunks - 1), nxt);
-    if (cc_pend >= 0) store_pending();
+    // (past the end the last chunk is re-read: unconditional, so loads stay in registers)
+    load_chunk(min(cc + 2, nchunks - 1), nxt2);
+    if (!rec && cc_pend >= 0) store_pending();
 
-    // X = K S, Y = Q S for token rows 16w..16w+15 (S as pre-split B fragments)
-    f32x4 Xa = {0.f, 0.f, 0.f, 0.f}, Ya = {0.f, 0.f, 0.f, 0.f};
+    // X = K S (recurrence side) or Y = Q S (output side) for this wave's tile
+    f32x4 XY = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 bh = as_bf16x8(lds16(&Sth[lr * SBP + 32 * s + 8 * lg]));
       const bf16x8 bl = as_bf16x8(lds16(&Stl[lr * SBP + 32 * s + 8 * lg]));
-      const bf16x8 ak = as_bf16x8(cur.kf[s]);
-      const bf16x8 aq = as_bf16x8(cur.qf[s]);
-      Xa = mfma_bf16(ak, bl, Xa);
-      Ya = mfma_bf16(aq, bl, Ya);
-      Xa = mfma_bf16(ak, bh, Xa);
-      Ya = mfma_bf16(aq, bh, Ya);
+      const bf16x8 a = as_bf16x8(cur.f[s]);
+      XY = mfma_bf16(a, bl, XY);
+      XY = mfma_bf16(a, bh, XY);
     }
-    // R = beta v - b X -> R^T planes
-    f32x4 Ra;
+    f32x4 Ra = {0.f, 0.f, 0.f, 0.f};
+    if (rec) {   // R = beta v - b X -> R^T planes
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 s4 = SCs[buf][16 * w + 4 * lg + i];
-      Ra[i] = s4.w * cur.vv[i] - s4.y * Xa[i];
-    }
-    {
+      for (int i = 0; i < 4; ++i) {
+        const float4 s4 = SCs[buf][16 * m + 4 * lg + i];
+        Ra[i] = s4.w * bf16_to_f32(static_cast<uint16_t>(cur.vv[i])) - s4.y * XY[i];
+      }
       uint2 hi, lo;
       split4_packed(make_float4(Ra[0], Ra[1], Ra[2], Ra[3]), hi, lo);
-      *reinterpret_cast<uint2*>(&RTh[lr * TBP + 16 * w + 4 * lg]) = hi;
-      *reinterpret_cast<uint2*>(&RTl[lr * TBP + 16 * w + 4 * lg]) = lo;
+      *reinterpret_cast<uint2*>(&RTh[lr * TBP + 16 * m + 4 * lg]) = hi;
+      *reinterpret_cast<uint2*>(&RTl[lr * TBP + 16 * m + 4 * lg]) = lo;
     }
     __syncthreads();
 
-    // U = R + T_strict R -> U^T and (c U)^T planes
-    f32x4 Ua = Ra;
+    if (rec) {   // U = R + T_strict R -> U^T and (c U)^T planes
+      f32x4 Ua = Ra;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < nks) {
-        const bf16x8 ah = as_bf16x8(and4(cur.th[s], mT[s]));
-        const bf16x8 al = as_bf16x8(and4(cur.tl[s], mT[s]));
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 ah = as_bf16x8(and4(cur.x[s], msk[s]));
+        const bf16x8 al = as_bf16x8(and4(cur.x[2 + s], msk[s]));
         const bf16x8 bh = as_bf16x8(lds16(&RTh[lr * TBP + 32 * s + 8 * lg]));
         const bf16x8 bl = as_bf16x8(lds16(&RTl[lr * TBP + 32 * s + 8 * lg]));
         Ua = mfma_bf16(al, bh, Ua);
         Ua = mfma_bf16(ah, bl, Ua);
         Ua = mfma_bf16(ah, bh, Ua);
       }
-    }
-    {
       uint2 hi, lo;
       split4_packed(make_float4(Ua[0], Ua[1], Ua[2], Ua[3]), hi, lo);
-      *reinterpret_cast<uint2*>(&UTh[lr * TBP + 16 * w + 4 * lg]) = hi;
-      *reinterpret_cast<uint2*>(&UTl[lr * TBP + 16 * w + 4 * lg]) = lo;
+      *reinterpret_cast<uint2*>(&UTh[lr * TBP + 16 * m + 4 * lg]) = hi;
+      *reinterpret_cast<uint2*>(&UTl[lr * TBP + 16 * m + 4 * lg]) = lo;
       float cu4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cu4[i] = SCs[buf][16 * w + 4 * lg + i].z * Ua[i];
+      for (int i = 0; i < 4; ++i) cu4[i] = SCs[buf][16 * m + 4 * lg + i].z * Ua[i];
       split4_packed(make_float4(cu4[0], cu4[1], cu4[2], cu4[3]), hi, lo);
-      *reinterpret_cast<uint2*>(&CTh[lr * TBP + 16 * w + 4 * lg]) = hi;
-      *reinterpret_cast<uint2*>(&CTl[lr * TBP + 16 * w + 4 * lg]) = lo;
+      *reinterpret_cast<uint2*>(&CTh[lr * TBP + 16 * m + 4 * lg]) = hi;
+      *reinterpret_cast<uint2*>(&CTl[lr * TBP + 16 * m + 4 * lg]) = lo;
     }
     __syncthreads();
 
-    // O = a Y + P U (P fragments hold tokens in reversed order: reverse U too)
-    f32x4 Oa;
+    if (!rec) {  // O = a Y + P U (P fragments hold tokens in reversed order: reverse U too)
+      f32x4 Oa;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Oa[i] = SCs[buf][16 * w + 4 * lg + i].x * Ya[i];
+      for (int i = 0; i < 4; ++i) Oa[i] = SCs[buf][16 * m + 4 * lg + i].x * XY[i];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < nks) {
-        const bf16x8 ah = as_bf16x8(and4(cur.ph[s], mP[s]));
-        const bf16x8 al = as_bf16x8(and4(cur.pl[s], mP[s]));
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 ah = as_bf16x8(and4(cur.x[s], msk[s]));
+        const bf16x8 al = as_bf16x8(and4(cur.x[2 + s], msk[s]));
         const bf16x8 bh = as_bf16x8(rev8(lds16(&UTh[lr * TBP + 32 * s + 8 * lg])));
         const bf16x8 bl = as_bf16x8(rev8(lds16(&UTl[lr * TBP + 32 * s + 8 * lg])));
         Oa = mfma_bf16(al, bh, Oa);
         Oa = mfma_bf16(ah, bl, Oa);
         Oa = mfma_bf16(ah, bh, Oa);
       }
+      Opend = Oa;          // stored at the start of the next chunk
+      cc_pend = cc;
     }
-    Opend = Oa;          // stored at the start of the next chunk
-    cc_pend = cc;
 
     // S_w = e^{G_C} S_w + K[:, rows of w]^T (c U)
-    const float eGC = egcs[buf];
-    bf16x8 ch[2], cl[2];
+    {
+      const float eGC = __builtin_bit_cast(float, cur.eg);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      ch[s] = as_bf16x8(lds16(&CTh[lr * TBP + 32 * s + 8 * lg]));
-      cl[s] = as_bf16x8(lds16(&CTl[lr * TBP + 32 * s + 8 * lg]));
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[t][i] *= eGC;
+      for (int i = 0; i < 4; ++i) S[i] *= eGC;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 a = as_bf16x8(lds16(&Ktt[buf][(32 * w + 16 * t + lr) * KTP + 32 * s + 8 * lg]));
-        S[t] = mfma_bf16(a, cl[s], S[t]);
-        S[t] = mfma_bf16(a, ch[s], S[t]);
+        const bf16x8 a = as_bf16x8(lds16(&Ktt[buf][(16 * w + lr) * KTP + 32 * s + 8 * lg]));
+        const bf16x8 ch = as_bf16x8(lds16(&CTh[lr * TBP + 32 * s + 8 * lg]));
+        const bf16x8 cl = as_bf16x8(lds16(&CTl[lr * TBP + 32 * s + 8 * lg]));
+        S = mfma_bf16(a, cl, S);
+        S = mfma_bf16(a, ch, S);
       }
     }
     // publish S for the next chunk (every wave has read S^T before the barriers above)
@@ -682,25 +678,30 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     __syncthreads();
   };
 
-  Prefetch pa, pb;
+  Prefetch pa, pb, pc;
   if (nchunks > 0) {
     load_chunk(0, pa);
+    load_chunk(min(1, nchunks - 1), pb);
     commit(pa, 0);
   }
   publish_S();
   __syncthreads();
-  for (int cc = 0; cc < nchunks; cc += 2) {
-    step(cc, pa, pb);
-    if (cc + 1 < nchunks) step(cc + 1, pb, pa);
+  // Whole rotations in the loop, the last one or two chunks after it: a loop
+  // body without early exits lets the compiler count exactly which loads are
+  // still in flight at every wait.
+  int cc = 0;
+  for (; cc + 3 <= nchunks; cc += 3) {
+    step(cc, pa, pb, pc);
+    step(cc + 1, pb, pc, pa);
+    step(cc + 2, pc, pa, pb);
   }
-  if (cc_pend >= 0) store_pending();
+  if (cc < nchunks) step(cc, pa, pb, pc);
+  if (cc + 1 < nchunks) step(cc + 1, pb, pc, pa);
+  if (!rec && cc_pend >= 0) store_pending();
 
   if (ST) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ST[(static_cast<int64_t>(unit) * D + 32 * w + 16 * t + 4 * lg + i) * D + col] = S[t][i];
+    for (int i = 0; i < 4; ++i) ST[(static_cast<int64_t>(unit) * D + 16 * w + 4 * lg + i) * D + col] = S[i];
   }
 }
 
@@ -921,11 +922,11 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   const unsigned grid = static_cast<unsigned>(n_seqs) * nv * (D / 16);
   if constexpr (sizeof(TIn) == 2) {
     if (o_bf16)
-      chunk_state_bf16_kernel<uint16_t><<<grid, 256, 0, s>>>(
+      chunk_state_bf16_kernel<uint16_t><<<grid, 512, 0, s>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qs, ks,
           vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, static_cast<uint16_t*>(o));
     else
-      chunk_state_bf16_kernel<float><<<grid, 256, 0, s>>>(
+      chunk_state_bf16_kernel<float><<<grid, 512, 0, s>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qs, ks,
           vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, static_cast<float*>(o));
     return hipGetLastError();
