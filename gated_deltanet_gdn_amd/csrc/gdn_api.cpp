@@ -109,9 +109,9 @@ int gdn_gating(const void* a, const void* b, int ab_dtype, const float* A_log, c
 }
 
 size_t gdn_chunk_fwd_workspace_size(int64_t T_tot, int n_seqs, int nk, int nv, int dk, int dv, int in_dtype) {
-  (void)nk; (void)dk; (void)dv; (void)in_dtype;
-  if (T_tot < 0 || n_seqs <= 0 || nv <= 0) return 0;
-  return gdn::chunk_workspace_bytes(T_tot, n_seqs, nv);
+  (void)dk; (void)dv;
+  if (T_tot < 0 || n_seqs <= 0 || nk <= 0 || nv <= 0) return 0;
+  return gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, in_dtype == GDN_BF16);
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype, int64_t q_tok_stride,
@@ -126,7 +126,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype, int
   if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
   if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
   if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
-  const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nv);
+  const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, in_dtype == GDN_BF16);
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));

@@ -31,9 +31,10 @@ hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf1
                             float* state, void* o, int o_bf16, hipStream_t s);
 
 // Chunked path. The workspace holds, per chunk and value head, the packed
-// 64x64 tile [T strictly lower | P^T on and above the diagonal] and the
-// per-token scalars; see k_chunk.hip.
-size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nv);
+// 64x64 tile [T strictly lower | P turned by 180 degrees on and above the
+// diagonal] and the per-token scalars, and for bf16 inputs per chunk and key
+// head the K, Q and K^T operand tiles; see k_chunk.hip.
+size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nk, int nv, int bf16);
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf16,
                             int64_t qs, int64_t ks, int64_t vs, const float* g, const float* beta,
                             const int32_t* cu, int n_seqs, int64_t T, int nk, int nv, float scale,

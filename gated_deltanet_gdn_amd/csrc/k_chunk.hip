@@ -53,17 +53,29 @@ constexpr int D = 128;     // dk = dv
 constexpr int AP = 68;     // LDS pitch (floats) of 64 x 64 fp32 tiles (16-byte rows)
 constexpr float kEps = 1e-6f;
 
+constexpr int TILE_ELEMS = CH * D;   // bf16 elements of one 16 KB operand tile
+
+// Workspace: chunk table | per (chunk, value head): 16 KB tile, 1 KB of
+// per-token scalars, exp(G_C) | bf16 inputs only, per (chunk, key head): K, Q
+// and K^T operand tiles of 16 KB each.
 struct WsLayout {
-  size_t off_chunk_off, off_tp, off_sc, off_egc, total;
+  size_t off_chunk_off, off_tp, off_sc, off_egc, off_kf, off_qf, off_ktf, total;
 };
-inline WsLayout ws_layout(int64_t T, int n_seqs, int nv) {
+inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
   const int64_t nch = T / CH + n_seqs;   // >= sum_n ceil(len_n / 64)
+  const size_t tile_bytes = static_cast<size_t>(TILE_ELEMS) * 2;
   WsLayout w{};
   size_t o = 0;
   w.off_chunk_off = o; o += (static_cast<size_t>(n_seqs) + 1) * sizeof(int32_t); o = (o + 255) & ~size_t(255);
-  w.off_tp = o;        o += static_cast<size_t>(nch) * nv * CH * CH * sizeof(float);
+  w.off_tp = o;        o += static_cast<size_t>(nch) * nv * tile_bytes;
   w.off_sc = o;        o += static_cast<size_t>(nch) * nv * CH * sizeof(float4);
   w.off_egc = o;       o += static_cast<size_t>(nch) * nv * sizeof(float); o = (o + 255) & ~size_t(255);
+  w.off_kf = w.off_qf = w.off_ktf = o;
+  if (bf16) {
+    w.off_kf = o;  o += static_cast<size_t>(nch) * nk * tile_bytes;
+    w.off_qf = o;  o += static_cast<size_t>(nch) * nk * tile_bytes;
+    w.off_ktf = o; o += static_cast<size_t>(nch) * nk * tile_bytes;
+  }
   w.total = o;
   return w;
 }
@@ -170,6 +182,76 @@ __device__ __forceinline__ void mm16(f32x4& acc, const float* A, int lda, const 
   }
 }
 
+// ------------------------------------------------------------------ operand blocks (bf16 inputs)
+// The state recurrence reads each operand as whole blocks: one wave's MFMA
+// fragment, 64 lanes x 16 bytes with lane l at byte 16 l, so every wave load
+// is one contiguous kilobyte. Inside a 32-wide k-step, slot j of lane
+// (lr, lg) holds index perm32(lg, j) = 16 (j / 4) + 4 lg + j % 4: slots 0-3
+// are the four accumulator rows that lane holds in 16-row tile 2s, slots
+// 4-7 those of tile 2s + 1. In that order an accumulator tile already is
+// this lane's share of a B operand, so tiles pass between waves through LDS
+// with no shuffle. The order also commutes with the 180-degree turn of the
+// packed T|P tile: 63 - (32 (1-s) + perm32(3-lg, j)) = 32 s + perm32(lg, 7-j).
+constexpr int BLK_ELEMS = 64 * 8;    // bf16 elements of one block
+__device__ __forceinline__ int perm32(int lg, int j) { return 16 * (j >> 2) + 4 * lg + (j & 3); }
+
+// K or Q tile in LDS (bf16 [64][EP]; rows >= L hold copies) -> 16 blocks
+// (m, s), m = 16-token tile, s = k-step over dk: lane (lr, lg) holds
+// X[16m + lr][32s + perm32(lg, j)], rows >= L zero.
+template <int EP>
+__device__ __forceinline__ void write_row_blocks(const uint16_t* tile, int L, uint16_t* __restrict__ dst, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int row = 16 * m + lr;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint2 a = *reinterpret_cast<const uint2*>(tile + row * EP + 32 * s + 4 * lg);
+      const uint2 b = *reinterpret_cast<const uint2*>(tile + row * EP + 32 * s + 16 + 4 * lg);
+      *reinterpret_cast<uint4*>(dst + (4 * m + s) * BLK_ELEMS + lane * 8) =
+          zero_if(row >= L, make_uint4(a.x, a.y, b.x, b.y));
+    }
+  }
+}
+// K tile in LDS -> 16 transposed blocks (w, s), w = 16 rows of dk, s =
+// 32-token k-step: lane (lr, lg) holds K[32s + perm32(lg, j)][16w + lr],
+// tokens >= L zero.
+template <int EP>
+__device__ __forceinline__ void write_col_blocks(const uint16_t* tile, int L, uint16_t* __restrict__ dst, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint32_t d[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int t0 = 32 * s + perm32(lg, 2 * p);   // slot 2p + 1 holds token t0 + 1
+        const uint32_t e0 = tile[t0 * EP + 16 * w + lr], e1 = tile[(t0 + 1) * EP + 16 * w + lr];
+        d[p] = (t0 < L ? e0 : 0u) | ((t0 + 1 < L ? e1 : 0u) << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + (2 * w + s) * BLK_ELEMS + lane * 8) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+  }
+}
+// packed T|P tile in LDS (fp32 [64][AP]) -> 8 blocks (m, s) per plane, hi
+// plane then lo: lane (lr, lg) holds X[16m + lr][32s + perm32(lg, j)].
+__device__ __forceinline__ void write_tile_blocks(const float* Tw, uint16_t* __restrict__ dst, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float* r = Tw + (16 * m + lr) * AP + 32 * s + 4 * lg;
+      uint2 ah, al, bh, bl;
+      split4_packed(*reinterpret_cast<const float4*>(r), ah, al);
+      split4_packed(*reinterpret_cast<const float4*>(r + 16), bh, bl);
+      *reinterpret_cast<uint4*>(dst + (2 * m + s) * BLK_ELEMS + lane * 8) = make_uint4(ah.x, ah.y, bh.x, bh.y);
+      *reinterpret_cast<uint4*>(dst + (8 + 2 * m + s) * BLK_ELEMS + lane * 8) = make_uint4(al.x, al.y, bl.x, bl.y);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ prep
 template <typename TIn>
 constexpr int prep_pitch() { return sizeof(TIn) == 2 ? 136 : 132; }   // 16-byte rows
@@ -185,7 +267,8 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t qs, int64_t ks,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int n_seqs, int64_t T, int nk, int nv, float scale, int l2, const int32_t* __restrict__ chunk_off,
-    float* __restrict__ tp, float4* __restrict__ sc, float* __restrict__ egc) {
+    float* __restrict__ tp, float4* __restrict__ sc, float* __restrict__ egc, uint16_t* __restrict__ kf,
+    uint16_t* __restrict__ qf, uint16_t* __restrict__ ktf) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int EP = prep_pitch<TIn>();
   using MG = Mma<BF, true, true>;
@@ -269,6 +352,17 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
         MG::run(gqk[p], aq, bk);
       }
     }
+  }
+  // 3b. bf16 inputs: K, Q and K^T operand blocks of the state recurrence,
+  //     once per key head (by the first / last value head that reads it)
+  if constexpr (BF) {
+    const int r = nv / nk, rho = h % r;
+    const size_t kt = (static_cast<size_t>(c) * nk + hk) * TILE_ELEMS;
+    if (rho == 0) {
+      write_row_blocks<EP>(Ks, L, kf + kt, lane);
+      write_col_blocks<EP>(Ks, L, ktf + kt, lane);
+    }
+    if (rho == r - 1) write_row_blocks<EP>(Qs, L, qf + kt, lane);
   }
   // 4. norms: |k_i|^2 from the Gram diagonal (diagonal tiles p = 0, 2, 5, 9)
   if (lr >= 4 * lg && lr < 4 * lg + 4) {
@@ -376,27 +470,26 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
 
   // 9. packed tile and scalars to the workspace
   const size_t tile = static_cast<size_t>(c) * nv + h;
-  float* X = tp + tile * CH * CH;
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int idx = it * 64 + lane, row = idx >> 4, c4 = (idx & 15) * 4;
-    const float4 x = *reinterpret_cast<const float4*>(Tw + row * AP + c4);
-    if constexpr (BF) {
-      // bf16 inputs: the tile is stored as two bf16 planes, hi = bf16(x) and
-      // lo = bf16(x - hi), each 64 x 64, in the same 16 KB
-      uint16_t* Xh = reinterpret_cast<uint16_t*>(X);
-      uint16_t* Xl = Xh + CH * CH;
-      uint2 hi, lo;
-      split4_packed(x, hi, lo);
-      *reinterpret_cast<uint2*>(Xh + row * CH + c4) = hi;
-      *reinterpret_cast<uint2*>(Xl + row * CH + c4) = lo;
-    } else {
-      *reinterpret_cast<float4*>(X + row * CH + c4) = x;
-    }
-  }
   const float eG = expf(static_cast<float>(G));
   const float rk_i = rk_s[lane], rq_i = rq_s[lane];
-  sc[tile * CH + lane] = make_float4(scale * rq_i * eG, bi * rk_i * eG, rk_i * expf(static_cast<float>(GC - G)), bi);
+  const float sa = scale * rq_i * eG, sb = bi * rk_i * eG, scc = rk_i * expf(static_cast<float>(GC - G));
+  if constexpr (BF) {
+    // operand blocks (bf16 hi and lo planes) and the scalars as planes a | b | c | beta
+    write_tile_blocks(Tw, reinterpret_cast<uint16_t*>(tp) + tile * TILE_ELEMS, lane);
+    float* sp = reinterpret_cast<float*>(sc + tile * CH);
+    sp[lane] = sa;
+    sp[CH + lane] = sb;
+    sp[2 * CH + lane] = scc;
+    sp[3 * CH + lane] = bi;
+  } else {
+    float* X = tp + tile * CH * CH;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane, row = idx >> 4, c4 = (idx & 15) * 4;
+      *reinterpret_cast<float4*>(X + row * CH + c4) = *reinterpret_cast<const float4*>(Tw + row * AP + c4);
+    }
+    sc[tile * CH + lane] = make_float4(sa, sb, scc, bi);
+  }
   if (lane == 0) egc[tile] = expf(static_cast<float>(GC));
 }
 
@@ -404,30 +497,33 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
 // One workgroup per (sequence, value head, 16 value columns), eight waves with
 // two roles over the chunk's four 16-token tiles m = w % 4:
 //   waves 0-3 (recurrence side): X = K S, R = beta v - b X, U = R + T R;
-//   waves 4-7 (output side):     Y = Q S, O = a Y + P U.
+//   waves 4-7 (output side):     Y = Q S, O = a Y + P U, computed transposed
+//                                (operands swapped) so a lane holds 4
+//                                consecutive columns of one token row.
 // Wave w also owns rows 16w..16w+15 of S (128 x 16, fp32, one MFMA
-// accumulator) and updates them: S_w = e^{G_C} S_w + K[:, rows]^T (c U).
-// Waves w and w+4 share a SIMD, so each SIMD interleaves one wave of each
-// side. Every fp32 operand is split into bf16 hi + lo once, by the wave that
-// produces it, and exchanged through LDS as transposed bf16 planes, so each
-// consumer fragment is one 16-byte LDS read feeding an MFMA directly.
-constexpr int KTP = 72;   // LDS pitch (bf16) of K^T   [128 rows of dk][64 tokens]
-constexpr int SBP = 136;  // LDS pitch (bf16) of S^T   [16 columns][128 rows of dk]
-constexpr int TBP = 72;   // LDS pitch (bf16) of R^T, U^T, (cU)^T [16 columns][64 tokens]
+// accumulator) and updates them: S_w = e^{G_C} S_w + K[:, rows of w]^T (c U).
+// Waves w and w+4 share a SIMD, so each SIMD interleaves one wave of each side.
+//
+// Every operand comes from the workspace as contiguous blocks already in
+// fragment order (see the operand-block writers), loaded two chunks ahead
+// into three rotating register sets, in three groups spread over the chunk's
+// three phases so the memory pipe never backs up into the waves. Tiles
+// produced inside the chunk (S, R, U, c U) are split into bf16 hi + lo by
+// the producing wave and pass through LDS in the same block order, so a
+// consumer reads its share of a B operand with one 16-byte read per plane.
+constexpr int BLK_BYTES = BLK_ELEMS * 2;
 
 struct Prefetch {
-  uint4 f[4];       // K (recurrence side) or Q (output side) A-fragments, 4 k-steps over dk
-  uint4 x[4];       // T (recurrence) or P (output) fragments: [hi k0, hi k1, lo k0, lo k1]
-  // Raw loaded words only: any arithmetic on a prefetched value at load time
-  // would force a wait for that load (and every load issued before it).
-  uint32_t vv[4];   // V (bf16 in the low half) of this lane's 4 accumulator rows
-  uint4 scv;        // per-token scalars (a, b, c, beta) of token lane, fp32 bits (recurrence side)
-  uint32_t eg;      // exp(G_C) bits (every wave)
+  uint4 f[4];       // K (recurrence side) or Q (output side) blocks, k-steps 0..3 over dk
+  uint4 x[4];       // T (recurrence) or P (output) blocks: hi k0, hi k1, lo k0, lo k1
+  uint4 kt[2];      // K^T blocks of this wave's 16 rows of S, token k-steps 0, 1
+  uint4 st[2];      // staging wave only: per-token scalars and exp(G_C), or the V slice
 };
-// Every loaded word is consumed on every path of every wave that loads it.
-// A register whose load is still counted as pending when the compiler reuses
-// it makes it wait on the in-order counter, and with it on every load issued
-// since -- including the look-ahead loads of later chunks.
+constexpr int kScalarWave = 4;   // loads the chunk's scalar planes and exp(G_C)
+constexpr int kValueWave = 5;    // loads the chunk's 64 x 16 slice of V
+// Every loaded word is consumed on every path of every wave that loads it: a
+// register whose load is still counted as pending when the compiler reuses it
+// makes it wait on the in-order counter, and with it on every later load.
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ uint4 and4(const uint4& a, const uint4& m) {
@@ -438,24 +534,37 @@ __device__ __forceinline__ uint4 rev8(const uint4& a) {
   auto sw = [](uint32_t d) { return (d >> 16) | (d << 16); };
   return make_uint4(sw(a.w), sw(a.z), sw(a.y), sw(a.x));
 }
-__device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 lds16(const unsigned char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// Accumulator tile -> LDS exchange slot: a lane's 4 rows of 16-row tile t
+// are slots 4 (t % 2) .. +3 of that lane's 16 bytes in k-step t / 2.
+__device__ __forceinline__ void put_tile(unsigned char* X, int planes_off, int t, int lane, const f32x4& v) {
+  uint2 hi, lo;
+  split4_packed(make_float4(v[0], v[1], v[2], v[3]), hi, lo);
+  unsigned char* p = X + (t >> 1) * BLK_BYTES + lane * 16 + (t & 1) * 8;
+  *reinterpret_cast<uint2*>(p) = hi;
+  *reinterpret_cast<uint2*>(p + planes_off) = lo;
+}
 
 template <typename TO>
 __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t qs,
-    int64_t ks, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk, int nv,
-    const int32_t* __restrict__ chunk_off, const float* __restrict__ tp, const float4* __restrict__ sc,
-    const float* __restrict__ egc, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ktt[2][D * KTP];
-  __shared__ __attribute__((aligned(16))) uint16_t Sth[16 * SBP];
-  __shared__ __attribute__((aligned(16))) uint16_t Stl[16 * SBP];
-  __shared__ __attribute__((aligned(16))) uint16_t RTh[16 * TBP];
-  __shared__ __attribute__((aligned(16))) uint16_t RTl[16 * TBP];
-  __shared__ __attribute__((aligned(16))) uint16_t UTh[16 * TBP];
-  __shared__ __attribute__((aligned(16))) uint16_t UTl[16 * TBP];
-  __shared__ __attribute__((aligned(16))) uint16_t CTh[16 * TBP];
-  __shared__ __attribute__((aligned(16))) uint16_t CTl[16 * TBP];
-  __shared__ float4 SCs[2][CH];
+    const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
+    int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
+    const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
+    const uint16_t* __restrict__ ktf, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
+  // exchange tiles, each [plane hi | plane lo][k-step][64 lanes][16 B]
+  __shared__ __attribute__((aligned(16))) unsigned char SX[2 * 4 * BLK_BYTES];   // S, 4 dk k-steps
+  __shared__ __attribute__((aligned(16))) unsigned char RX[2 * 2 * BLK_BYTES];   // R, 2 token k-steps
+  __shared__ __attribute__((aligned(16))) unsigned char UX[2 * 2 * BLK_BYTES];   // U
+  __shared__ __attribute__((aligned(16))) unsigned char CX[2 * 2 * BLK_BYTES];   // c U
+  constexpr int SXP = 4 * BLK_BYTES, TXP = 2 * BLK_BYTES;                        // plane offsets
+  // per-chunk inputs staged by one wave each, double-buffered by chunk parity:
+  // scalar planes a | b | c | beta over the 64 tokens, exp(G_C) (every entry),
+  // and V of the four recurrence tiles in accumulator order [tile][lane][row]
+  __shared__ __attribute__((aligned(16))) float SCS[2][4 * CH];
+  __shared__ float EGS[2][64];
+  __shared__ __attribute__((aligned(16))) uint16_t VS[2][4 * 64 * 4];
 
   const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int slice = bid & 7;
@@ -471,21 +580,23 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
   const int col = slice * 16 + lr;
   const int row = 16 * m + lr;             // this lane's token row as an A-operand row
 
-  // masks of the triangular fragments (constant over chunks): T needs
-  // token < row, P needs token <= row (P slot j holds token 32s+8lg+7-j)
+  // masks of the triangular blocks (constant over chunks): T needs token <
+  // row; P slot j holds token 32s + perm32(lg, 7 - j) and needs it <= row
   uint4 msk[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     uint32_t mm[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+      bool lo, hi;
       if (rec) {
-        const int k0 = 32 * s + 8 * lg + 2 * d;
-        mm[d] = (k0 < row ? 0x0000ffffu : 0u) | (k0 + 1 < row ? 0xffff0000u : 0u);
+        lo = 32 * s + perm32(lg, 2 * d) < row;
+        hi = 32 * s + perm32(lg, 2 * d + 1) < row;
       } else {
-        const int p0 = 32 * s + 8 * lg + 7 - 2 * d;
-        mm[d] = (p0 <= row ? 0x0000ffffu : 0u) | (p0 - 1 <= row ? 0xffff0000u : 0u);
+        lo = 32 * s + perm32(lg, 7 - 2 * d) <= row;
+        hi = 32 * s + perm32(lg, 6 - 2 * d) <= row;
       }
+      mm[d] = (lo ? 0x0000ffffu : 0u) | (hi ? 0xffff0000u : 0u);
     }
     msk[s] = make_uint4(mm[0], mm[1], mm[2], mm[3]);
   }
@@ -501,178 +612,226 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
     for (int i = 0; i < 4; ++i) S[i] = S0[(static_cast<int64_t>(unit) * D + 16 * w + 4 * lg + i) * D + col];
   }
 
-  // lane-constant parts of the operand offsets (bytes)
-  const uint32_t fo0 = static_cast<uint32_t>(row * (rec ? ks : qs) * 2 + 16 * lg);
-  const uint32_t xo0 = rec ? static_cast<uint32_t>((row * CH + 8 * lg) * 2)
-                           : static_cast<uint32_t>(((63 - row) * CH + 56 - 8 * lg) * 2);
-  const int xstep = rec ? 64 : -64;        // byte step of one k-step along the fragment row
-  const uint32_t vo0 = static_cast<uint32_t>(((16 * m + 4 * lg) * vs + col) * 2);
+  // lane-constant block offsets (bytes). The T block of k-step s is (m, s);
+  // the P block is the turned tile's (3 - m, 1 - s) read in reversed lane
+  // order. Tiles 0 and 1 need only k-step 0 of either: their second block
+  // reads as zeros from past the resource, so no branch guards any load.
+  const uint32_t lo16 = static_cast<uint32_t>(lane * 16);
+  uint32_t xo[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    xo[s] = rec ? static_cast<uint32_t>((2 * m + s) * BLK_BYTES) + lo16
+                : static_cast<uint32_t>((2 * (3 - m) + 1 - s) * BLK_BYTES + (63 - lane) * 16);
+  const bool two_k = m >= 2;               // tiles 0, 1 need only k-step 0 of T and P
+  const uint32_t fo = static_cast<uint32_t>(4 * m * BLK_BYTES) + lo16;
+  const uint32_t kto = static_cast<uint32_t>(2 * w * BLK_BYTES) + lo16;
+  // V staging: lane l of instruction i loads token 32i + l / 2, columns 8 (l % 2) .. +7
+  const uint32_t vo0 = static_cast<uint32_t>(((lane >> 1) * vs + slice * 16 + 8 * (lane & 1)) * 2);
 
-  auto load_chunk = [&](int cc, Prefetch& pf) {
-    const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
-    const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-    const size_t tile = static_cast<size_t>(cbase + cc) * nv + h;
-    // Per-chunk buffer resources sized to the chunk's valid rows: rows past
-    // the sequence end read as zeros, with no branch around any load.
-    const uint16_t* fb = rec ? k : q;
-    const int64_t fs = rec ? ks : qs;
-    const rsrc_t rf = make_rsrc(fb + t0 * fs + static_cast<int64_t>(hk) * D,
-                                static_cast<uint32_t>(((L - 1) * fs + D) * 2));
-    const rsrc_t rx = make_rsrc(tp + tile * CH * CH, CH * CH * 4);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) pf.f[s] = bload16(rf, fo0 + 64 * s);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {   // hi plane, then lo plane 8 KB further
-      pf.x[s] = bload16(rx, xo0 + xstep * s);
-      pf.x[2 + s] = bload16(rx, xo0 + xstep * s + CH * CH * 2);
-    }
-    if (rec) {
-      const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
-                                  static_cast<uint32_t>(((L - 1) * vs + D) * 2));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pf.vv[i] = bload2(rv, vo0 + static_cast<uint32_t>(i * vs * 2));
-      pf.scv = bload16(make_rsrc(sc + tile * CH, CH * 16), static_cast<uint32_t>(lane * 16));
-    }
-    // exp(G_C) through a vector load: a uniform (scalar) load would share
-    // lgkmcnt with LDS traffic and stall the next LDS wait for a full
-    // memory round trip
-    pf.eg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + tile, 4), static_cast<uint32_t>(lane & 0), 0, 0);
-  };
-  // stage the next chunk: K^T into LDS from the recurrence waves' K fragments
-  auto commit = [&](const Prefetch& pf, int buf) {
-    if (rec) {
-      uint16_t* Kb = Ktt[buf];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t d[4] = {pf.f[s].x, pf.f[s].y, pf.f[s].z, pf.f[s].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          Kb[(32 * s + 8 * lg + j) * KTP + row] =
-              static_cast<uint16_t>((j & 1) ? (d[j >> 1] >> 16) : (d[j >> 1] & 0xffffu));
+  // group 0: T/P blocks (and the scalar block on the scalar wave); group 1:
+  // K/Q blocks (and V on the value wave); group 2: K^T blocks
+  auto load_chunk = [&](int cc, Prefetch& pf, int part) {
+    const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;    // (chunk, value head)
+    const size_t kt = static_cast<size_t>(cbase + cc) * nk + hk;   // (chunk, key head)
+    if (part == 0) {
+      const rsrc_t rx = make_rsrc(xf + ct * TILE_ELEMS, TILE_ELEMS * 2);
+      pf.x[0] = bload16(rx, xo[0]);
+      pf.x[2] = bload16(rx, xo[0] + 8 * BLK_BYTES);
+      if (two_k) {
+        pf.x[1] = bload16(rx, xo[1]);
+        pf.x[3] = bload16(rx, xo[1] + 8 * BLK_BYTES);
       }
-      // (all four recurrence waves write the same values: see Prefetch)
-      *reinterpret_cast<uint4*>(&SCs[buf][lane]) = pf.scv;
+      if (w == kScalarWave) {
+        // exp(G_C) through a vector load: a uniform (scalar) load would share
+        // lgkmcnt with LDS traffic and stall the next LDS wait for a full
+        // memory round trip
+        pf.st[0] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
+        pf.st[1].x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
+      }
+    } else if (part == 1) {
+      const rsrc_t rf = make_rsrc((rec ? kf : qf) + kt * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) pf.f[s] = bload16(rf, fo + s * BLK_BYTES);
+      if (w == kValueWave) {
+        // V rows past the sequence end read as zeros (resource sized to the valid rows)
+        const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+        const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
+                                    static_cast<uint32_t>(((L - 1) * vs + D) * 2));
+        pf.st[0] = bload16(rv, vo0);
+        pf.st[1] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
+      }
+    } else {
+      const rsrc_t rk = make_rsrc(ktf + kt * TILE_ELEMS, TILE_ELEMS * 2);
+      pf.kt[0] = bload16(rk, kto);
+      pf.kt[1] = bload16(rk, kto + BLK_BYTES);
     }
   };
-  auto publish_S = [&]() {
-    uint2 hi, lo;
-    split4_packed(make_float4(S[0], S[1], S[2], S[3]), hi, lo);
-    *reinterpret_cast<uint2*>(&Sth[lr * SBP + 16 * w + 4 * lg]) = hi;
-    *reinterpret_cast<uint2*>(&Stl[lr * SBP + 16 * w + 4 * lg]) = lo;
+  // stage a chunk's scalars, exp(G_C) and V slice in LDS buffer `buf`
+  auto commit = [&](const Prefetch& pf, int buf) {
+    if (w == kScalarWave) {
+      *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = pf.st[0];
+      EGS[buf][lane] = bits_f(pf.st[1].x);
+    }
+    if (w == kValueWave) {
+      // lane holds V[t][8 (lane % 2) + e], e = 0..7, for t = 32i + lane / 2;
+      // slot of (t, c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t d[4] = {pf.st[i].x, pf.st[i].y, pf.st[i].z, pf.st[i].w};
+        const int t = 32 * i + (lane >> 1);
+        uint16_t* base = &VS[buf][((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          base[(8 * (lane & 1) + e) * 4] = static_cast<uint16_t>((e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xffffu));
+      }
+    }
   };
+  auto publish_S = [&]() { put_tile(SX, SXP, w, lane, S); };
 
   // The output tile of chunk c is stored at the start of chunk c+1, after that
-  // chunk's prefetch loads are issued: loads and stores share one in-order
+  // chunk's first loads are issued: loads and stores share one in-order
   // completion counter, so a store issued before a load would make every
   // wait on that load also wait for the store to reach memory.
   f32x4 Opend = {0.f, 0.f, 0.f, 0.f};
   int cc_pend = -1;
-  const uint32_t oo0 = static_cast<uint32_t>(((16 * m + 4 * lg) * nv * D + col) * sizeof(TO));
+  // O^T tile: lane (lr, lg) holds O[token 16m + lr][columns 16 slice + 4lg + i]
+  const uint32_t oo0 = static_cast<uint32_t>((row * nv * D + slice * 16 + 4 * lg) * sizeof(TO));
   auto store_pending = [&]() {
     const int64_t t0 = s_begin + static_cast<int64_t>(cc_pend) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
     const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
                                 static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = oo0 + static_cast<uint32_t>(i * nv * D * sizeof(TO));
-      if constexpr (sizeof(TO) == 4) bstore4(ro, off, Opend[i]);
-      else bstore2(ro, off, f32_to_bf16(Opend[i]));
+    if constexpr (sizeof(TO) == 4) {
+      // (__float_as_uint: a bit cast of a vector element is miscompiled to element 0)
+      bstore16(ro, oo0, make_uint4(__float_as_uint(Opend[0]), __float_as_uint(Opend[1]), __float_as_uint(Opend[2]),
+                                   __float_as_uint(Opend[3])));
+    } else {
+      bstore8(ro, oo0, make_uint2(f32_to_bf16(Opend[0]) | (static_cast<uint32_t>(f32_to_bf16(Opend[1])) << 16),
+                                  f32_to_bf16(Opend[2]) | (static_cast<uint32_t>(f32_to_bf16(Opend[3])) << 16)));
     }
   };
 
-  // One chunk: issue the loads of chunk cc+2 into `nxt2`, compute chunk cc
-  // with `cur`, then stage chunk cc+1 (`nxt`, loaded one chunk ago) in LDS.
-  // Three register buffers rotate, so no copy is made between chunks and
-  // every load has two chunks of compute to arrive.
+  // One chunk with `cur`; the loads of chunk cc+2 go into `nxt2` (the set in
+  // between is in flight). Three register sets rotate, so nothing is copied
+  // between chunks and every load has about two chunks of compute to arrive.
   auto step = [&](int cc, const Prefetch& cur, const Prefetch& nxt, Prefetch& nxt2) {
+    const int ln = min(cc + 2, nchunks - 1);   // past the end the last chunk is re-read
     const int buf = cc & 1;
-    // (past the end the last chunk is re-read: unconditional, so loads stay in registers)
-    load_chunk(min(cc + 2, nchunks - 1), nxt2);
+    // T/P operands, masked; the k-step 1 blocks of tiles 0 and 1 are not
+    // loaded, but are consumed here on every path (their mask is zero)
+    uint4 xa[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      xa[s] = and4(cur.x[s], msk[s]);
+      xa[2 + s] = and4(cur.x[2 + s], msk[s]);
+    }
+    load_chunk(ln, nxt2, 0);
     if (!rec && cc_pend >= 0) store_pending();
 
-    // X = K S (recurrence side) or Y = Q S (output side) for this wave's tile
-    f32x4 XY = {0.f, 0.f, 0.f, 0.f};
+    // phase 1: X = K S (recurrence side) or Y^T = S^T Q^T (output side),
+    // hi and lo parts of S in two accumulators
+    f32x4 XH = {0.f, 0.f, 0.f, 0.f}, XL = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 bh = as_bf16x8(lds16(&Sth[lr * SBP + 32 * s + 8 * lg]));
-      const bf16x8 bl = as_bf16x8(lds16(&Stl[lr * SBP + 32 * s + 8 * lg]));
       const bf16x8 a = as_bf16x8(cur.f[s]);
-      XY = mfma_bf16(a, bl, XY);
-      XY = mfma_bf16(a, bh, XY);
-    }
-    f32x4 Ra = {0.f, 0.f, 0.f, 0.f};
-    if (rec) {   // R = beta v - b X -> R^T planes
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 s4 = SCs[buf][16 * m + 4 * lg + i];
-        Ra[i] = s4.w * bf16_to_f32(static_cast<uint16_t>(cur.vv[i])) - s4.y * XY[i];
+      const bf16x8 sl = as_bf16x8(lds16(SX + SXP + s * BLK_BYTES + lane * 16));
+      const bf16x8 sh = as_bf16x8(lds16(SX + s * BLK_BYTES + lane * 16));
+      if (rec) {
+        XL = mfma_bf16(a, sl, XL);
+        XH = mfma_bf16(a, sh, XH);
+      } else {
+        XL = mfma_bf16(sl, a, XL);
+        XH = mfma_bf16(sh, a, XH);
       }
-      uint2 hi, lo;
-      split4_packed(make_float4(Ra[0], Ra[1], Ra[2], Ra[3]), hi, lo);
-      *reinterpret_cast<uint2*>(&RTh[lr * TBP + 16 * m + 4 * lg]) = hi;
-      *reinterpret_cast<uint2*>(&RTl[lr * TBP + 16 * m + 4 * lg]) = lo;
+    }
+    f32x4 XY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) XY[i] = XH[i] + XL[i];
+    f32x4 Ra = {0.f, 0.f, 0.f, 0.f};
+    const int srow = 16 * m + 4 * lg;      // first of this lane's 4 accumulator rows
+    if (rec) {   // R = beta v - b X
+      const float4 bb = *reinterpret_cast<const float4*>(&SCS[buf][CH + srow]);
+      const float4 be = *reinterpret_cast<const float4*>(&SCS[buf][3 * CH + srow]);
+      const uint2 vv = *reinterpret_cast<const uint2*>(&VS[buf][(m * 64 + lane) * 4]);
+      Ra[0] = be.x * bf16_to_f32(static_cast<uint16_t>(vv.x)) - bb.x * XY[0];
+      Ra[1] = be.y * bf16_to_f32(static_cast<uint16_t>(vv.x >> 16)) - bb.y * XY[1];
+      Ra[2] = be.z * bf16_to_f32(static_cast<uint16_t>(vv.y)) - bb.z * XY[2];
+      Ra[3] = be.w * bf16_to_f32(static_cast<uint16_t>(vv.y >> 16)) - bb.w * XY[3];
+      put_tile(RX, TXP, m, lane, Ra);
     }
     __syncthreads();
+    load_chunk(ln, nxt2, 1);
 
-    if (rec) {   // U = R + T_strict R -> U^T and (c U)^T planes
-      f32x4 Ua = Ra;
+    // phase 2: U = R + T_strict R -> U and c U tiles
+    if (rec) {
+      f32x4 U0 = Ra, U1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 ah = as_bf16x8(and4(cur.x[s], msk[s]));
-        const bf16x8 al = as_bf16x8(and4(cur.x[2 + s], msk[s]));
-        const bf16x8 bh = as_bf16x8(lds16(&RTh[lr * TBP + 32 * s + 8 * lg]));
-        const bf16x8 bl = as_bf16x8(lds16(&RTl[lr * TBP + 32 * s + 8 * lg]));
+        if (s == 1 && !two_k) break;
+        const bf16x8 ah = as_bf16x8(xa[s]), al = as_bf16x8(xa[2 + s]);
+        const bf16x8 bh = as_bf16x8(lds16(RX + s * BLK_BYTES + lane * 16));
+        const bf16x8 bl = as_bf16x8(lds16(RX + TXP + s * BLK_BYTES + lane * 16));
+        f32x4& Ua = s == 0 ? U0 : U1;
         Ua = mfma_bf16(al, bh, Ua);
         Ua = mfma_bf16(ah, bl, Ua);
         Ua = mfma_bf16(ah, bh, Ua);
       }
-      uint2 hi, lo;
-      split4_packed(make_float4(Ua[0], Ua[1], Ua[2], Ua[3]), hi, lo);
-      *reinterpret_cast<uint2*>(&UTh[lr * TBP + 16 * m + 4 * lg]) = hi;
-      *reinterpret_cast<uint2*>(&UTl[lr * TBP + 16 * m + 4 * lg]) = lo;
-      float cu4[4];
+      f32x4 Ua, cU;
+      const float4 cb = *reinterpret_cast<const float4*>(&SCS[buf][2 * CH + srow]);
+      const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cu4[i] = SCs[buf][16 * m + 4 * lg + i].z * Ua[i];
-      split4_packed(make_float4(cu4[0], cu4[1], cu4[2], cu4[3]), hi, lo);
-      *reinterpret_cast<uint2*>(&CTh[lr * TBP + 16 * m + 4 * lg]) = hi;
-      *reinterpret_cast<uint2*>(&CTl[lr * TBP + 16 * m + 4 * lg]) = lo;
+      for (int i = 0; i < 4; ++i) {
+        Ua[i] = U0[i] + U1[i];
+        cU[i] = cbv[i] * Ua[i];
+      }
+      put_tile(UX, TXP, m, lane, Ua);
+      put_tile(CX, TXP, m, lane, cU);
     }
     __syncthreads();
+    load_chunk(ln, nxt2, 2);
 
-    if (!rec) {  // O = a Y + P U (P fragments hold tokens in reversed order: reverse U too)
-      f32x4 Oa;
+    // phase 3: O^T = a Y^T + U^T P^T (P slots hold tokens in reversed order: reverse U too)
+    if (!rec) {
+      f32x4 O0, O1 = {0.f, 0.f, 0.f, 0.f};
+      const float ar = SCS[buf][row];      // a of this lane's token row
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Oa[i] = SCs[buf][16 * m + 4 * lg + i].x * XY[i];
+      for (int i = 0; i < 4; ++i) O0[i] = ar * XY[i];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 ah = as_bf16x8(and4(cur.x[s], msk[s]));
-        const bf16x8 al = as_bf16x8(and4(cur.x[2 + s], msk[s]));
-        const bf16x8 bh = as_bf16x8(rev8(lds16(&UTh[lr * TBP + 32 * s + 8 * lg])));
-        const bf16x8 bl = as_bf16x8(rev8(lds16(&UTl[lr * TBP + 32 * s + 8 * lg])));
-        Oa = mfma_bf16(al, bh, Oa);
-        Oa = mfma_bf16(ah, bl, Oa);
-        Oa = mfma_bf16(ah, bh, Oa);
+        if (s == 1 && !two_k) break;
+        const bf16x8 ah = as_bf16x8(xa[s]), al = as_bf16x8(xa[2 + s]);
+        const bf16x8 bh = as_bf16x8(rev8(lds16(UX + s * BLK_BYTES + lane * 16)));
+        const bf16x8 bl = as_bf16x8(rev8(lds16(UX + TXP + s * BLK_BYTES + lane * 16)));
+        f32x4& Oa = s == 0 ? O0 : O1;
+        Oa = mfma_bf16(bh, al, Oa);
+        Oa = mfma_bf16(bl, ah, Oa);
+        Oa = mfma_bf16(bh, ah, Oa);
       }
-      Opend = Oa;          // stored at the start of the next chunk
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Opend[i] = O0[i] + O1[i];   // stored at the start of the next chunk
       cc_pend = cc;
     }
 
-    // S_w = e^{G_C} S_w + K[:, rows of w]^T (c U)
+    // S_w = e^{G_C} S_w + K[:, rows of w]^T (c U), the two token k-steps in two accumulators
     {
-      const float eGC = __builtin_bit_cast(float, cur.eg);
+      const float eGC = EGS[buf][0];
+      f32x4 S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[i] *= eGC;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 a = as_bf16x8(lds16(&Ktt[buf][(16 * w + lr) * KTP + 32 * s + 8 * lg]));
-        const bf16x8 ch = as_bf16x8(lds16(&CTh[lr * TBP + 32 * s + 8 * lg]));
-        const bf16x8 cl = as_bf16x8(lds16(&CTl[lr * TBP + 32 * s + 8 * lg]));
-        S = mfma_bf16(a, cl, S);
-        S = mfma_bf16(a, ch, S);
+        const bf16x8 a = as_bf16x8(cur.kt[s]);
+        const bf16x8 ch = as_bf16x8(lds16(CX + s * BLK_BYTES + lane * 16));
+        const bf16x8 cl = as_bf16x8(lds16(CX + TXP + s * BLK_BYTES + lane * 16));
+        f32x4& Sa = s == 0 ? S : S1;
+        Sa = mfma_bf16(a, cl, Sa);
+        Sa = mfma_bf16(a, ch, Sa);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[i] += S1[i];
     }
-    // publish S for the next chunk (every wave has read S^T before the barriers above)
+    // publish S for the next chunk (every wave has read S before the barriers above)
     publish_S();
     commit(nxt, buf ^ 1);
     __syncthreads();
@@ -680,8 +839,11 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
 
   Prefetch pa, pb, pc;
   if (nchunks > 0) {
-    load_chunk(0, pa);
-    load_chunk(min(1, nchunks - 1), pb);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      load_chunk(0, pa, p);
+      load_chunk(min(1, nchunks - 1), pb, p);
+    }
     commit(pa, 0);
   }
   publish_S();
@@ -896,12 +1058,16 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
                           const float* g, const float* beta, const int32_t* cu, int n_seqs, int64_t T, int nk,
                           int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
                           hipStream_t s) {
-  const WsLayout lay = ws_layout(T, n_seqs, nv);
+  constexpr bool BF = sizeof(TIn) == 2;
+  const WsLayout lay = ws_layout(T, n_seqs, nk, nv, BF);
   char* base = static_cast<char*>(ws);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + lay.off_chunk_off);
   float* tp = reinterpret_cast<float*>(base + lay.off_tp);
   float4* sc = reinterpret_cast<float4*>(base + lay.off_sc);
   float* egc = reinterpret_cast<float*>(base + lay.off_egc);
+  uint16_t* kf = BF ? reinterpret_cast<uint16_t*>(base + lay.off_kf) : nullptr;
+  uint16_t* qf = BF ? reinterpret_cast<uint16_t*>(base + lay.off_qf) : nullptr;
+  uint16_t* ktf = BF ? reinterpret_cast<uint16_t*>(base + lay.off_ktf) : nullptr;
 
   const int64_t nch = T / CH + n_seqs;
   chunk_offsets_kernel<<<1, 256, 0, s>>>(cu, n_seqs, T, static_cast<int32_t>(nch), chunk_off);
@@ -915,20 +1081,21 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     if (e != hipSuccess) return e;
     kern<<<dim3(static_cast<unsigned>(nch), static_cast<unsigned>(nv)), 64, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, g, beta, cu, n_seqs, T, nk, nv, scale, l2,
-        chunk_off, tp, sc, egc);
+        chunk_off, tp, sc, egc, kf, qf, ktf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const unsigned grid = static_cast<unsigned>(n_seqs) * nv * (D / 16);
-  if constexpr (sizeof(TIn) == 2) {
+  if constexpr (BF) {
+    const uint16_t* xf = reinterpret_cast<const uint16_t*>(tp);
+    const float* scp = reinterpret_cast<const float*>(sc);
+    const uint16_t* vb = static_cast<const uint16_t*>(v);
     if (o_bf16)
-      chunk_state_bf16_kernel<uint16_t><<<grid, 512, 0, s>>>(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qs, ks,
-          vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, static_cast<uint16_t*>(o));
+      chunk_state_bf16_kernel<uint16_t><<<grid, 512, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
+                                                             kf, qf, ktf, S0, ST, static_cast<uint16_t*>(o));
     else
-      chunk_state_bf16_kernel<float><<<grid, 512, 0, s>>>(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qs, ks,
-          vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, static_cast<float*>(o));
+      chunk_state_bf16_kernel<float><<<grid, 512, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
+                                                          kf, qf, ktf, S0, ST, static_cast<float*>(o));
     return hipGetLastError();
   } else {
     const size_t lds = generic_lds_bytes();
@@ -947,7 +1114,9 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
 
 }  // namespace
 
-size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nv) { return ws_layout(T, n_seqs, nv).total; }
+size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nk, int nv, int bf16) {
+  return ws_layout(T, n_seqs, nk, nv, bf16 != 0).total;
+}
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf16, int64_t qs, int64_t ks,
                             int64_t vs, const float* g, const float* beta, const int32_t* cu, int n_seqs,
