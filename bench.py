@@ -18,11 +18,17 @@ The CPU baseline times the fp64 oracle (gating + token recurrence) on the
 whole prefill workload on the host (threads stated); it is a reported
 baseline, not a target.
 
+roofline.traffic is the HBM traffic of one call, from the rocprofv3
+FETCH_SIZE / WRITE_SIZE summary committed under profiles/ (written by
+bench_profile.py, calibrated on a plain 1 GiB copy); it is null when the
+kernel sources differ from the ones the counters were taken on.
+
 Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +39,31 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_t8k_decode_256seq.md")
+CSRC = os.path.join(ROOT, "gated_deltanet_gdn_amd", "csrc")
+# kernel sources each measured figure depends on
+SOURCES = {"chunk": ["k_chunk.hip", "gdn_device.hpp"], "recurrent": ["k_recurrent.hip", "gdn_device.hpp"]}
+
+
+def source_hash(part):
+    h = hashlib.sha256()
+    for f in SOURCES[part]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(part):
+    """HBM bytes per call from the committed counter summary, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                if line.startswith("traffic_json:"):
+                    rec = json.loads(line.split(":", 1)[1])[part]
+                    return rec["bytes_per_call"] if rec["source_hash"] == source_hash(part) else None
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
 
 
 def chunk_flops_per_token_head(C=64, dk=128, dv=128, r=2):
@@ -89,6 +120,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="finish with one plain 1 GiB device copy (counter calibration runs only)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GDN core shards by head or sequence with no "
@@ -140,7 +173,7 @@ def main():
     achieved_tflops = flops / (chunk_ms * 1e-3) / 1e12
     roofline = dict(bound="mfma", kernel="gdn_chunk_fwd (chunk_offsets + chunk_prep + chunk_state launches)",
                     achieved=round(achieved_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("chunk"),
                     avg_ms=round(chunk_ms, 4), algorithmic_flops=flops, algorithmic_bytes=cbytes,
                     hbm_gbps_algorithmic=round(cbytes / (chunk_ms * 1e-3) / 1e9, 1))
 
@@ -185,7 +218,15 @@ def main():
                       step_ms=round(dstep_ms, 4),
                       roofline=dict(bound="hbm", kernel="recurrent_kernel", achieved=round(gbps, 1),
                                     peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
-                                    traffic=None, avg_ms=round(rec_ms,4), algorithmic_bytes=rbytes))
+                                    traffic=measured_traffic("recurrent"), avg_ms=round(rec_ms, 4),
+                                    algorithmic_bytes=rbytes))
+
+    if args.calibrate_copy:   # known-size reference for the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.ones(1 << 28, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.skip_cpu_baseline:

@@ -1,0 +1,183 @@
+"""rocprofv3 summaries of the benchmark, written under profiles/.
+
+    python bench_profile.py run        [--out gpurun_out/profile]   # on the GPU machine
+    python bench_profile.py summarize  [--out gpurun_out/profile]   # anywhere, from run's CSVs
+
+Runs bench.py (no CPU baseline, ending with one plain 1 GiB device copy) as a
+child process under rocprofv3, once per pass. Counters are never combined
+with tracing:
+  1. --kernel-trace --stats                    per-kernel calls and durations
+  2. --pmc FETCH_SIZE                          HBM read KiB per dispatch
+  3. --pmc WRITE_SIZE                          HBM write KiB per dispatch
+  4. --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA   MFMA work per dispatch
+The copy gives the calibration factors: true bytes / counter reading for a
+copy of known size, applied to every kernel's reading.
+
+Writes
+  profiles/bench_prefill_t8k_decode_256seq_kernel_stats.md
+  profiles/hbm_traffic_prefill_t8k_decode_256seq.md   (its traffic_json line is
+      read by bench.py, with the hash of the kernel sources it was taken on)
+This process itself never touches the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402  (top level imports no GPU library)
+
+BENCH_ARGS = ["--steps", "20", "--warmup", "3", "--skip-cpu-baseline", "--calibrate-copy"]
+COPY_BYTES = 1 << 30
+KERNELS = {  # what one call of each measured entry point launches (bf16 in, fp32 out)
+    "chunk": ["chunk_offsets_kernel", "chunk_prep_kernel<unsigned short>", "chunk_state_bf16_kernel<float>"],
+    "recurrent": ["recurrent_kernel<unsigned short, float>"],
+}
+
+
+PASSES = [  # name, rocprofv3 arguments
+    ("ktrace", ["--kernel-trace", "--stats"]),
+    ("fetch", ["--pmc", "FETCH_SIZE"]),
+    ("write", ["--pmc", "WRITE_SIZE"]),
+    ("mfma", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA"]),
+]
+
+
+def pass_command(name, prof_args):
+    return " ".join(["rocprofv3", *prof_args, "-f", "csv", "-d", f"<out>/{name}", "-o", name, "--",
+                     "python3", "bench.py", *BENCH_ARGS])
+
+
+def run_pass(out, name, prof_args, timeout):
+    d = os.path.join(out, name)
+    cmd = ["rocprofv3", *prof_args, "-f", "csv", "-d", d, "-o", name, "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *BENCH_ARGS]
+    print("[pass]", name, " ".join(cmd), flush=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=timeout)
+    with open(os.path.join(out, name + ".log"), "w") as fh:
+        fh.write(r.stdout + r.stderr)
+    if not [l for l in r.stdout.splitlines() if l.startswith("{")]:
+        raise RuntimeError(f"pass {name}: bench.py printed no result (rc={r.returncode}); see {name}.log")
+
+
+def bench_line(out, name):
+    with open(os.path.join(out, name + ".log")) as fh:
+        return json.loads([l for l in fh.read().splitlines() if l.startswith("{")][-1])
+
+
+def kernel_stats(d):
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
+    return list(csv.DictReader(open(f)))
+
+
+def counters(d):
+    """{kernel name: {counter: [value per dispatch]}}"""
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            out[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+def pick(table, key):
+    hits = [n for n in table if key in n]
+    if len(hits) != 1:
+        raise RuntimeError(f"kernel {key!r}: {len(hits)} matches in the profile")
+    return hits[0]
+
+
+def avg(v):
+    return sum(v) / len(v)
+
+
+def summarize(out):
+    d1, d2, d3, d4 = (os.path.join(out, n) for n, _ in PASSES)
+    cmd1, cmd2, cmd3, cmd4 = (pass_command(n, a) for n, a in PASSES)
+    b1 = bench_line(out, "ktrace")
+
+    # ---- kernel trace
+    ks = kernel_stats(d1)
+    by_name = {r["Name"]: r for r in ks}
+    lines = ["# Kernel trace: bench.py, prefill T=8192 (16->32 heads, bf16) and decode 256 seqs", "",
+             "Command (from /tmp, TMPDIR=/tmp; written by `python bench_profile.py run`, summarised by",
+             "`python bench_profile.py summarize`):", "", "    " + cmd1, "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in sorted(ks, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    chunk_sum = sum(float(by_name[pick(by_name, k)]["AverageNs"]) for k in KERNELS["chunk"]) / 1e3
+    rec_avg = float(by_name[pick(by_name, KERNELS["recurrent"][0])]["AverageNs"]) / 1e3
+    lines += ["", "Agreement with the HIP-event figures bench.py printed in the same run:", "",
+              f"- gdn_chunk_fwd = chunk_offsets + chunk_prep + chunk_state: sum of averages {chunk_sum:.1f} us; "
+              f"events {b1['roofline']['avg_ms'] * 1e3:.1f} us per call",
+              f"- recurrent_kernel: average {rec_avg:.1f} us; events {b1['decode']['roofline']['avg_ms'] * 1e3:.1f} us",
+              "", "bench.py line of this run:", "", "    " + json.dumps(b1), ""]
+    with open(os.path.join(ROOT, "profiles", "bench_prefill_t8k_decode_256seq_kernel_stats.md"), "w") as fh:
+        fh.write("\n".join(lines))
+
+    # ---- traffic and MFMA counters
+    cf, cw, cm = counters(d2), counters(d3), counters(d4)
+    copy_f = max(cf[pick(cf, "copyBuffer")]["FETCH_SIZE"])
+    copy_w = max(cw[pick(cw, "copyBuffer")]["WRITE_SIZE"])
+    kf, kw = COPY_BYTES / 1024 / copy_f, COPY_BYTES / 1024 / copy_w
+    rec = {}
+    rows = ["| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read bytes | write bytes | MFMA ops (x512 flop) |",
+            "|---|---|---|---|---|---|"]
+    for part, names in KERNELS.items():
+        total = 0.0
+        flops = 0.0
+        for k in names:
+            f_kib = avg(cf[pick(cf, k)]["FETCH_SIZE"])
+            w_kib = avg(cw[pick(cw, k)]["WRITE_SIZE"])
+            mops = avg(cm[pick(cm, k)]["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+            rb, wb = f_kib * 1024 * kf, w_kib * 1024 * kw
+            total += rb + wb
+            flops += mops * 512
+            rows.append(f"| `{k}` | {f_kib:.1f} | {w_kib:.1f} | {rb / 1e6:.1f} MB | {wb / 1e6:.1f} MB | {mops:.3e} |")
+        rec[part] = dict(bytes_per_call=round(total), mfma_flops_per_call=flops, source_hash=bench.source_hash(part))
+    lines = ["# HBM traffic and MFMA work per call: prefill T=8192 (bf16, 16->32 heads) and decode 256 seqs", "",
+             "Commands (from /tmp, TMPDIR=/tmp), one counter set per run:", "",
+             "    " + cmd2, "    " + cmd3, "    " + cmd4, "",
+             "Calibration on the plain 1 GiB device copy (`copyBuffer`) in the same runs:", "",
+             f"- FETCH_SIZE read {copy_f:.1f} KiB for {COPY_BYTES // 1024} KiB: read bytes = {kf:.4f} x 1024 x FETCH_SIZE",
+             f"- WRITE_SIZE read {copy_w:.1f} KiB for {COPY_BYTES // 1024} KiB: write bytes = {kw:.4f} x 1024 x WRITE_SIZE",
+             "", *rows, "",
+             f"- gdn_chunk_fwd (three launches): {rec['chunk']['bytes_per_call'] / 1e6:.1f} MB per call "
+             f"(algorithmic {bench.chunk_bytes(8192, 16, 32) / 1e6:.1f} MB); MFMA work "
+             f"{rec['chunk']['mfma_flops_per_call'] / 1e9:.2f} GFLOP executed (hi/lo passes included) vs "
+             f"{bench.chunk_flops_per_token_head() * 8192 * 32 / 1e9:.2f} GFLOP algorithmic",
+             f"- recurrent_kernel: {rec['recurrent']['bytes_per_call'] / 1e6:.1f} MB per call "
+             f"(algorithmic {bench.recurrent_bytes(256, 16, 32) / 1e6:.1f} MB)", "",
+             "Source hashes are of the kernel sources the counters were taken on; bench.py reports traffic",
+             "only while they match.", "",
+             "traffic_json: " + json.dumps(rec), ""]
+    with open(bench.TRAFFIC_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines))
+    print("[profile] wrote", bench.TRAFFIC_SUMMARY, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("mode", choices=["run", "summarize"])
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"))
+    ap.add_argument("--timeout", type=int, default=240)
+    args = ap.parse_args()
+    if args.mode == "run":
+        os.makedirs(args.out, exist_ok=True)
+        for name, prof_args in PASSES:
+            run_pass(args.out, name, prof_args, args.timeout)
+        print("[profile] passes done in", args.out, flush=True)
+    else:
+        summarize(args.out)
+
+
+if __name__ == "__main__":
+    main()

@@ -288,8 +288,11 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
   float* b_s = rq_s + CH;
   float* scr = b_s + 2 * CH;                       // [16][20] scratch
 
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
+  // heads vary fastest: the value heads of one key head, and the per-token
+  // g and beta of all heads (one cache line per token), are read by
+  // neighbouring workgroups and hit in L2
+  const int h = blockIdx.x;
+  const int c = blockIdx.y;
   const int hk = h / (nv / nk);
   const int total = chunk_off[n_seqs];
   if (c >= total) return;
@@ -1079,7 +1082,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    kern<<<dim3(static_cast<unsigned>(nch), static_cast<unsigned>(nv)), 64, lds, s>>>(
+    kern<<<dim3(static_cast<unsigned>(nv), static_cast<unsigned>(nch)), 64, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, g, beta, cu, n_seqs, T, nk, nv, scale, l2,
         chunk_off, tp, sc, egc, kf, qf, ktf);
     e = hipGetLastError();
