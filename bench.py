@@ -171,7 +171,7 @@ def main():
     flops = chunk_flops_per_token_head(r=r) * T * wl.nv
     cbytes = chunk_bytes(T, wl.nk, wl.nv)
     achieved_tflops = flops / (chunk_ms * 1e-3) / 1e12
-    roofline = dict(bound="mfma", kernel="gdn_chunk_fwd (chunk_offsets + chunk_prep + chunk_state launches)",
+    roofline = dict(bound="mfma", kernel="gdn_chunk_fwd (chunk_prep + chunk_state launches)",
                     achieved=round(achieved_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("chunk"),
                     avg_ms=round(chunk_ms, 4), algorithmic_flops=flops, algorithmic_bytes=cbytes,

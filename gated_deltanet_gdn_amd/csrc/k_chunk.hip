@@ -121,6 +121,19 @@ __device__ __forceinline__ int find_le(const int32_t* a, int n, int64_t x) {
   return lo;
 }
 
+// First chunk slot and chunk count of sequence n. Without cu_seqlens there is
+// one sequence and no chunk table is built.
+__device__ __forceinline__ void chunk_span(const int32_t* chunk_off, const int32_t* cu, int64_t T, int n,
+                                           int& first, int& count) {
+  if (!cu) {
+    first = 0;
+    count = static_cast<int>((T + CH - 1) / CH);
+    return;
+  }
+  first = chunk_off[n];
+  count = chunk_off[n + 1] - first;
+}
+
 // Raw copies of 8 input elements (16 bytes of bf16 or 32 bytes of fp32).
 __device__ __forceinline__ void copy8(const uint16_t* src, uint16_t* dst) {
   *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
@@ -195,75 +208,129 @@ __device__ __forceinline__ void mm16(f32x4& acc, const float* A, int lda, const 
 constexpr int BLK_ELEMS = 64 * 8;    // bf16 elements of one block
 __device__ __forceinline__ int perm32(int lg, int j) { return 16 * (j >> 2) + 4 * lg + (j & 3); }
 
-// K or Q tile in LDS (bf16 [64][EP]; rows >= L hold copies) -> 16 blocks
-// (m, s), m = 16-token tile, s = k-step over dk: lane (lr, lg) holds
-// X[16m + lr][32s + perm32(lg, j)], rows >= L zero.
+// K or Q tile in LDS (bf16 [64][EP]; rows >= L hold copies) -> blocks (m, s),
+// m = 16-token tile, s = k-step over dk: lane (lr, lg) holds
+// X[16m + lr][32s + perm32(lg, j)], rows >= L zero. This call writes tile m's
+// four blocks.
 template <int EP>
-__device__ __forceinline__ void write_row_blocks(const uint16_t* tile, int L, uint16_t* __restrict__ dst, int lane) {
+__device__ __forceinline__ void write_row_blocks(const uint16_t* tile, int L, uint16_t* __restrict__ dst, int lane,
+                                                 int m) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const int row = 16 * m + lr;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint2 a = *reinterpret_cast<const uint2*>(tile + row * EP + 32 * s + 4 * lg);
+    const uint2 b = *reinterpret_cast<const uint2*>(tile + row * EP + 32 * s + 16 + 4 * lg);
+    *reinterpret_cast<uint4*>(dst + (4 * m + s) * BLK_ELEMS + lane * 8) =
+        zero_if(row >= L, make_uint4(a.x, a.y, b.x, b.y));
+  }
+}
+// K tile in LDS -> transposed blocks (w, s), w = 16 rows of dk, s = 32-token
+// k-step: lane (lr, lg) holds K[32s + perm32(lg, j)][16w + lr], tokens >= L
+// zero. This call writes w = 2 s2, 2 s2 + 1 (dk step s2). The transpose runs
+// on MFMA: with A = 16 token rows x 32 dk of K and B = a 0/1 matrix that picks
+// dk 16w + c for column c, D = K[16t + r][16w + c] lands in accumulator order
+// (lane (c, lg) holds rows 4 lg .. +3), which is slots 0-3 (t = 2s) or 4-7
+// (t = 2s + 1) of the block. Each D entry is a single bf16 product with 1, so
+// it converts back to bf16 exactly.
+template <int EP>
+__device__ __forceinline__ void write_col_blocks(const uint16_t* tile, int L, uint16_t* __restrict__ dst, int lane,
+                                                 int s2) {
+  const int lr = lane & 15, lg = lane >> 4;
+  // sel[hh] picks dk 16 hh + lr out of the 32-wide step (B slot (lg, j) is dk 8 lg + j)
+  bf16x8 sel[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int k0 = 8 * lg + 2 * p;
+      d[p] = (k0 == 16 * hh + lr ? 0x3f80u : 0u) | (k0 + 1 == 16 * hh + lr ? 0x3f800000u : 0u);
+    }
+    sel[hh] = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+  }
+  f32x4 Dt[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 16 * t + lr;
+    const bf16x8 a = __builtin_bit_cast(
+        bf16x8, zero_if(row >= L, *reinterpret_cast<const uint4*>(tile + row * EP + 32 * s2 + 8 * lg)));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) Dt[hh][t] = mfma_bf16(a, sel[hh], f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int w = 2 * s2 + hh;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f32x4& lo = Dt[hh][2 * s];
+      const f32x4& hi = Dt[hh][2 * s + 1];
+      uint2 p0, p1, unused;
+      split4_packed(make_float4(lo[0], lo[1], lo[2], lo[3]), p0, unused);
+      split4_packed(make_float4(hi[0], hi[1], hi[2], hi[3]), p1, unused);
+      *reinterpret_cast<uint4*>(dst + (2 * w + s) * BLK_ELEMS + lane * 8) = make_uint4(p0.x, p0.y, p1.x, p1.y);
+    }
+  }
+}
+// packed T|P tile in LDS (fp32 [64][AP]) -> blocks (m, s) per plane, hi plane
+// then lo: lane (lr, lg) holds X[16m + lr][32s + perm32(lg, j)]. This call
+// writes tile m's blocks.
+__device__ __forceinline__ void write_tile_blocks(const float* Tw, uint16_t* __restrict__ dst, int lane, int m) {
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int row = 16 * m + lr;
+  for (int s = 0; s < 2; ++s) {
+    const float* r = Tw + (16 * m + lr) * AP + 32 * s + 4 * lg;
+    uint2 ah, al, bh, bl;
+    split4_packed(*reinterpret_cast<const float4*>(r), ah, al);
+    split4_packed(*reinterpret_cast<const float4*>(r + 16), bh, bl);
+    *reinterpret_cast<uint4*>(dst + (2 * m + s) * BLK_ELEMS + lane * 8) = make_uint4(ah.x, ah.y, bh.x, bh.y);
+    *reinterpret_cast<uint4*>(dst + (8 + 2 * m + s) * BLK_ELEMS + lane * 8) = make_uint4(al.x, al.y, bl.x, bl.y);
+  }
+}
+
+// acc += A(16x16 fp32 in LDS, row pitch lda) * B, with B held in accumulator
+// layout (lane (lr, lg) holds B[4 lg + i][lr]). Ordering the k-slots of lane
+// group lg as k = 4 lg + slot makes that the B-operand layout, so B needs no
+// trip through LDS.
+template <bool BF>
+__device__ __forceinline__ void mm16_regb(f32x4& acc, const float* A, int lda, const f32x4& B, int lr, int lg) {
+  using M = Mma16<BF, false, false>;
+  if constexpr (BF) {
+    float a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] = A[lr * lda + 4 * lg + j];
+      b[j] = B[j];
+    }
+    M::run(acc, a, b);
+  } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint2 a = *reinterpret_cast<const uint2*>(tile + row * EP + 32 * s + 4 * lg);
-      const uint2 b = *reinterpret_cast<const uint2*>(tile + row * EP + 32 * s + 16 + 4 * lg);
-      *reinterpret_cast<uint4*>(dst + (4 * m + s) * BLK_ELEMS + lane * 8) =
-          zero_if(row >= L, make_uint4(a.x, a.y, b.x, b.y));
-    }
-  }
-}
-// K tile in LDS -> 16 transposed blocks (w, s), w = 16 rows of dk, s =
-// 32-token k-step: lane (lr, lg) holds K[32s + perm32(lg, j)][16w + lr],
-// tokens >= L zero.
-template <int EP>
-__device__ __forceinline__ void write_col_blocks(const uint16_t* tile, int L, uint16_t* __restrict__ dst, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint32_t d[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int t0 = 32 * s + perm32(lg, 2 * p);   // slot 2p + 1 holds token t0 + 1
-        const uint32_t e0 = tile[t0 * EP + 16 * w + lr], e1 = tile[(t0 + 1) * EP + 16 * w + lr];
-        d[p] = (t0 < L ? e0 : 0u) | ((t0 + 1 < L ? e1 : 0u) << 16);
-      }
-      *reinterpret_cast<uint4*>(dst + (2 * w + s) * BLK_ELEMS + lane * 8) = make_uint4(d[0], d[1], d[2], d[3]);
-    }
-  }
-}
-// packed T|P tile in LDS (fp32 [64][AP]) -> 8 blocks (m, s) per plane, hi
-// plane then lo: lane (lr, lg) holds X[16m + lr][32s + perm32(lg, j)].
-__device__ __forceinline__ void write_tile_blocks(const float* Tw, uint16_t* __restrict__ dst, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const float* r = Tw + (16 * m + lr) * AP + 32 * s + 4 * lg;
-      uint2 ah, al, bh, bl;
-      split4_packed(*reinterpret_cast<const float4*>(r), ah, al);
-      split4_packed(*reinterpret_cast<const float4*>(r + 16), bh, bl);
-      *reinterpret_cast<uint4*>(dst + (2 * m + s) * BLK_ELEMS + lane * 8) = make_uint4(ah.x, ah.y, bh.x, bh.y);
-      *reinterpret_cast<uint4*>(dst + (8 + 2 * m + s) * BLK_ELEMS + lane * 8) = make_uint4(al.x, al.y, bl.x, bl.y);
+      const float a[1] = {A[lr * lda + 4 * lg + s]}, b[1] = {B[s]};
+      M::run(acc, a, b);
     }
   }
 }
 
 // ------------------------------------------------------------------ prep
+// Four waves per (chunk, value head). The ten lower 16x16 tile pairs (mi, mj)
+// of the Grams, A and P are dealt round-robin (pair p goes to wave p % 4);
+// wave w writes token tile w of every operand block; the off-diagonal blocks
+// of T are formed one level at a time with one wave per block.
 template <typename TIn>
 constexpr int prep_pitch() { return sizeof(TIn) == 2 ? 136 : 132; }   // 16-byte rows
 template <typename TIn>
 constexpr size_t prep_lds_bytes() {
   constexpr size_t tiles = 2 * CH * prep_pitch<TIn>() * sizeof(TIn);
   constexpr size_t at = 2 * CH * AP * sizeof(float);
-  return (tiles > at ? tiles : at) + CH * sizeof(double) + 4 * CH * sizeof(float) + 16 * 20 * sizeof(float);
+  return (tiles > at ? tiles : at) + CH * sizeof(double) + 4 * CH * sizeof(float);
 }
+constexpr int PREP_WAVES = 4;
 
+// (at most 128 VGPRs: four waves per SIMD, i.e. four blocks per CU, which is
+// also what the LDS holds)
 template <typename TIn>
-__global__ void __launch_bounds__(64) chunk_prep_kernel(
+__global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_per_eu(4))) chunk_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t qs, int64_t ks,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int n_seqs, int64_t T, int nk, int nv, float scale, int l2, const int32_t* __restrict__ chunk_off,
@@ -276,6 +343,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
   constexpr size_t tiles = 2 * CH * EP * sizeof(TIn);
   constexpr size_t at = 2 * CH * AP * sizeof(float);
   constexpr size_t head = tiles > at ? tiles : at;
+  constexpr int NT = 64 * PREP_WAVES;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   TIn* Ks = reinterpret_cast<TIn*>(smem);          // [64][EP]   (input tiles)
@@ -286,32 +354,36 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
   float* rk_s = reinterpret_cast<float*>(Gs + CH);
   float* rq_s = rk_s + CH;
   float* b_s = rq_s + CH;
-  float* scr = b_s + 2 * CH;                       // [16][20] scratch
 
   // heads vary fastest: the value heads of one key head, and the per-token
   // g and beta of all heads (one cache line per token), are read by
-  // neighbouring workgroups and hit in L2
+  // neighbouring workgroups
   const int h = blockIdx.x;
   const int c = blockIdx.y;
   const int hk = h / (nv / nk);
-  const int total = chunk_off[n_seqs];
+  const int total = cu ? chunk_off[n_seqs] : static_cast<int>((T + CH - 1) / CH);
   if (c >= total) return;
-  const int n = find_le(chunk_off, n_seqs, c);
+  const int n = cu ? find_le(chunk_off, n_seqs, c) : 0;
   int64_t s_begin, s_end;
   seq_bounds(cu, n, T, s_begin, s_end);
-  const int64_t t0 = s_begin + static_cast<int64_t>(c - chunk_off[n]) * CH;
+  const int64_t t0 = s_begin + static_cast<int64_t>(c - (cu ? chunk_off[n] : 0)) * CH;
   const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // per-token g and beta (wave 0, lane = token), issued first so their
+  // latency overlaps the tile loads and the Grams
+  const float g_ld = g[(t0 + min(lane, L - 1)) * nv + h];
+  const float b_ld = beta[(t0 + min(lane, L - 1)) * nv + h];
 
-  // 1. K and Q tiles into LDS (rows >= L zero); 4 rows per instruction
+  // 1. K and Q tiles into LDS; rows past the sequence end re-read the last
+  //    valid row: their norms are forced to 0 below, so they contribute
+  //    nothing to A, P or the scalars
   {
     const TIn* kb = k + t0 * ks + static_cast<int64_t>(hk) * D;
     const TIn* qb = q + t0 * qs + static_cast<int64_t>(hk) * D;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int idx = it * 64 + lane, row = idx >> 4, seg = idx & 15;
-      // rows past the sequence end re-read the last valid row: their norms
-      // are forced to 0 below, so they contribute nothing to A, P or scalars
+    for (int it = 0; it < CH * 16 / NT; ++it) {
+      const int idx = it * NT + tid, row = idx >> 4, seg = idx & 15;
       const int rr = min(row, L - 1);
       copy8(kb + rr * ks + seg * 8, Ks + row * EP + seg * 8);
       copy8(qb + rr * qs + seg * 8, Qs + row * EP + seg * 8);
@@ -319,20 +391,29 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
   }
   __syncthreads();
 
-  // 2. |q_i|^2 (lane = row)
-  float sqq = 0.f;
+  // 2. |q_i|^2: four threads per row, 32 elements each
+  {
+    const int row = tid >> 2, part = tid & 3;
+    float sqq = 0.f;
 #pragma unroll 8
-  for (int e = 0; e < D; ++e) {
-    const float x = tof(Qs[lane * EP + e]);
-    sqq = fmaf(x, x, sqq);
+    for (int e = 0; e < D / 4; ++e) {
+      const float x = tof(Qs[row * EP + part * (D / 4) + e]);
+      sqq = fmaf(x, x, sqq);
+    }
+    sqq += __shfl_xor(sqq, 1, 64);
+    sqq += __shfl_xor(sqq, 2, 64);
+    if (part == 0) rq_s[row] = row < L ? (l2 ? 1.0f / sqrtf(sqq + kEps) : 1.0f) : 0.0f;
   }
-  // 3. Grams on the lower 16x16 tiles, kept in registers
-  f32x4 gkk[10], gqk[10];
+  // 3. Grams on this wave's lower 16x16 tile pairs p = wv + 4 u, kept in registers
+  constexpr int NP = 3;
+  f32x4 gkk[NP], gqk[NP];
 #pragma unroll
-  for (int p = 0; p < 10; ++p) {
+  for (int u = 0; u < NP; ++u) {
+    gkk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gqk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int p = wv + 4 * u;
+    if (p >= 10) break;
     const int mi = tile_mi(p), mj = tile_mj(p);
-    gkk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-    gqk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / KS; ++s) {
       if constexpr (BF) {   // raw bf16 fragments, one 16-byte LDS read each
@@ -340,8 +421,8 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
         const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + (16 * mi + lr) * EP + kk);
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + (16 * mi + lr) * EP + kk);
         const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Ks + (16 * mj + lr) * EP + kk);
-        gkk[p] = mfma_bf16(ak, bk, gkk[p]);
-        gqk[p] = mfma_bf16(aq, bk, gqk[p]);
+        gkk[u] = mfma_bf16(ak, bk, gkk[u]);
+        gqk[u] = mfma_bf16(aq, bk, gqk[u]);
       } else {
         float ak[KPL], aq[KPL], bk[KPL];
 #pragma unroll
@@ -351,77 +432,91 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
           aq[j] = tof(Qs[(16 * mi + lr) * EP + kk]);
           bk[j] = tof(Ks[(16 * mj + lr) * EP + kk]);
         }
-        MG::run(gkk[p], ak, bk);
-        MG::run(gqk[p], aq, bk);
+        MG::run(gkk[u], ak, bk);
+        MG::run(gqk[u], aq, bk);
       }
     }
   }
   // 3b. bf16 inputs: K, Q and K^T operand blocks of the state recurrence,
-  //     once per key head (by the first / last value head that reads it)
+  //     once per key head: K and Q by its first value head, K^T by its last;
+  //     wave wv writes token tile wv (K, Q) and dk step wv (K^T)
   if constexpr (BF) {
     const int r = nv / nk, rho = h % r;
     const size_t kt = (static_cast<size_t>(c) * nk + hk) * TILE_ELEMS;
     if (rho == 0) {
-      write_row_blocks<EP>(Ks, L, kf + kt, lane);
-      write_col_blocks<EP>(Ks, L, ktf + kt, lane);
+      write_row_blocks<EP>(Ks, L, kf + kt, lane, wv);
+      write_row_blocks<EP>(Qs, L, qf + kt, lane, wv);
     }
-    if (rho == r - 1) write_row_blocks<EP>(Qs, L, qf + kt, lane);
+    if (rho == r - 1) write_col_blocks<EP>(Ks, L, ktf + kt, lane, wv);
   }
-  // 4. norms: |k_i|^2 from the Gram diagonal (diagonal tiles p = 0, 2, 5, 9)
-  if (lr >= 4 * lg && lr < 4 * lg + 4) {
+  // 4. |k_i|^2 from the Gram diagonals (pairs 0, 2, 5, 9)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int p = m * (m + 1) / 2 + m;
-      const int row = 16 * m + lr;
-      const float skk = gkk[p][lr - 4 * lg];
+  for (int u = 0; u < NP; ++u) {
+    const int p = wv + 4 * u;
+    if (p >= 10) break;
+    const int mi = tile_mi(p), mj = tile_mj(p);
+    if (mi == mj && lr >= 4 * lg && lr < 4 * lg + 4) {
+      const int row = 16 * mi + lr;
+      const float skk = gkk[u][lr - 4 * lg];
       rk_s[row] = row < L ? (l2 ? 1.0f / sqrtf(skk + kEps) : 1.0f) : 0.0f;
     }
   }
-  rq_s[lane] = lane < L ? (l2 ? 1.0f / sqrtf(sqq + kEps) : 1.0f) : 0.0f;
-  // 5. chunk-local cumulative decay in fp64
-  const bool valid = lane < L;
-  const float g_ld = g[(t0 + min(lane, L - 1)) * nv + h];
-  const float b_ld = beta[(t0 + min(lane, L - 1)) * nv + h];
-  const float gi = valid ? g_ld : 0.0f;
-  const float bi = valid ? b_ld : 0.0f;
-  double G = gi;
+  // 5. chunk-local cumulative decay in fp64 (wave 0, lane = token)
+  if (wv == 0) {
+    const bool valid = lane < L;
+    double G = valid ? g_ld : 0.0f;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(G, off, 64);
-    if (lane >= off) G += y;
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(G, off, 64);
+      if (lane >= off) G += y;
+    }
+    Gs[lane] = G;
+    b_s[lane] = valid ? b_ld : 0.0f;
   }
-  const double GC = __shfl(G, 63, 64);
-  Gs[lane] = G;
-  b_s[lane] = bi;
   __syncthreads();   // norms, G, beta visible; K/Q tiles no longer read
 
-  // 6. A (into LDS) and P (kept in registers, in place of the QK^T Gram)
+  // 6. A (into LDS) and P (kept in registers, in place of the QK^T Gram);
+  //    per-token values are read before the first write to Aw (which could
+  //    alias them as far as the compiler knows)
   {
-    double Gc[4];
-    float rkc[4];
+    double Gc[NP], Gr[NP][4];
+    float rkc[NP], ar[NP][4], pr[NP][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) { Gc[m] = Gs[16 * m + lr]; rkc[m] = rk_s[16 * m + lr]; }
+    for (int u = 0; u < NP; ++u) {
+      const int p = min(wv + 4 * u, 9);
+      const int mi = tile_mi(p), mj = tile_mj(p);
+      Gc[u] = Gs[16 * mj + lr];
+      rkc[u] = rk_s[16 * mj + lr];
 #pragma unroll
-    for (int p = 0; p < 10; ++p) {
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * mi + 4 * lg + ii;
+        Gr[u][ii] = Gs[i];
+        ar[u][ii] = b_s[i] * rk_s[i];
+        pr[u][ii] = scale * rq_s[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int p = wv + 4 * u;
+      if (p >= 10) break;
       const int mi = tile_mi(p), mj = tile_mj(p);
       const int j = 16 * mj + lr;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * mi + 4 * lg + ii;
-        const double Gi = Gs[i];
-        const float dec = (j <= i) ? expf(static_cast<float>(Gi - Gc[mj])) : 0.0f;
-        const float rki = rk_s[i];
-        Aw[i * AP + j] = (j < i) ? b_s[i] * rki * rkc[mj] * dec * gkk[p][ii] : 0.0f;
-        gqk[p][ii] = (j <= i) ? scale * rq_s[i] * rkc[mj] * dec * gqk[p][ii] : 0.0f;
+        const float dec = (j <= i) ? expf(static_cast<float>(Gr[u][ii] - Gc[u])) : 0.0f;
+        Aw[i * AP + j] = (j < i) ? ar[u][ii] * rkc[u] * dec * gkk[u][ii] : 0.0f;
+        gqk[u][ii] = (j <= i) ? pr[u][ii] * rkc[u] * dec * gqk[u][ii] : 0.0f;
       }
     }
   }
   __syncthreads();
 
-  // 7. T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
-  //    (lane = (block lg, column lr)), then the off-diagonal blocks
-  //    T_IJ = -T_II * sum_{M=J}^{I-1} A_IM T_MJ on MFMA, one level at a time.
-  {
+  // 7. T = (I + A)^-1: the four diagonal 16x16 blocks by forward substitution
+  //    (wave 0, lane = (block lg, column lr)), then the off-diagonal blocks
+  //    T_IJ = -T_II * sum_{M=J}^{I-1} A_IM T_MJ on MFMA, one level at a time,
+  //    block (J + lvl, J) on wave J
+  if (wv == 0) {
     const int I = lg, jc = lr;
     float t[16];
 #pragma unroll
@@ -438,62 +533,64 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
     }
   }
   __syncthreads();
-  constexpr int SP = 20;
 #pragma unroll
   for (int lvl = 1; lvl <= 3; ++lvl) {
-#pragma unroll
-    for (int I = lvl; I <= 3; ++I) {
-      const int J = I - lvl;
+    if (wv <= 3 - lvl) {
+      const int J = wv, I = J + lvl;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int Mb = J; Mb < I; ++Mb)
         mm16<BF>(acc, Aw + 16 * I * AP + 16 * Mb, AP, Tw + 16 * Mb * AP + 16 * J, AP, lr, lg);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) scr[(4 * lg + ii) * SP + lr] = acc[ii];
-      __syncthreads();
       f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-      mm16<BF>(acc2, Tw + 16 * I * AP + 16 * I, AP, scr, SP, lr, lg);
+      mm16_regb<BF>(acc2, Tw + 16 * I * AP + 16 * I, AP, acc, lr, lg);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) Tw[(16 * I + 4 * lg + ii) * AP + 16 * J + lr] = -acc2[ii];
-      __syncthreads();
     }
+    __syncthreads();
   }
 
   // 8. P into the upper triangle turned by 180 degrees: X[63-i][63-j] = P[i][j], j <= i
 #pragma unroll
-  for (int p = 0; p < 10; ++p) {
+  for (int u = 0; u < NP; ++u) {
+    const int p = wv + 4 * u;
+    if (p >= 10) break;
     const int mi = tile_mi(p), mj = tile_mj(p);
     const int j = 16 * mj + lr;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = 16 * mi + 4 * lg + ii;
-      if (j <= i) Tw[(63 - i) * AP + (63 - j)] = gqk[p][ii];
+      if (j <= i) Tw[(63 - i) * AP + (63 - j)] = gqk[u][ii];
     }
   }
   __syncthreads();
 
-  // 9. packed tile and scalars to the workspace
+  // 9. packed tile and scalars to the workspace (tile rows 16 wv .. +15 per wave)
   const size_t tile = static_cast<size_t>(c) * nv + h;
-  const float eG = expf(static_cast<float>(G));
-  const float rk_i = rk_s[lane], rq_i = rq_s[lane];
-  const float sa = scale * rq_i * eG, sb = bi * rk_i * eG, scc = rk_i * expf(static_cast<float>(GC - G));
   if constexpr (BF) {
-    // operand blocks (bf16 hi and lo planes) and the scalars as planes a | b | c | beta
-    write_tile_blocks(Tw, reinterpret_cast<uint16_t*>(tp) + tile * TILE_ELEMS, lane);
-    float* sp = reinterpret_cast<float*>(sc + tile * CH);
-    sp[lane] = sa;
-    sp[CH + lane] = sb;
-    sp[2 * CH + lane] = scc;
-    sp[3 * CH + lane] = bi;
+    write_tile_blocks(Tw, reinterpret_cast<uint16_t*>(tp) + tile * TILE_ELEMS, lane, wv);
   } else {
     float* X = tp + tile * CH * CH;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int idx = it * 64 + lane, row = idx >> 4, c4 = (idx & 15) * 4;
+    for (int it = 0; it < CH * CH / 4 / NT; ++it) {
+      const int idx = it * NT + tid, row = idx >> 4, c4 = (idx & 15) * 4;
       *reinterpret_cast<float4*>(X + row * CH + c4) = *reinterpret_cast<const float4*>(Tw + row * AP + c4);
     }
-    sc[tile * CH + lane] = make_float4(sa, sb, scc, bi);
   }
-  if (lane == 0) egc[tile] = expf(static_cast<float>(GC));
+  if (wv == 1) {   // per-token scalars (lane = token) and exp(G_C)
+    const double G = Gs[lane], GC = Gs[CH - 1];
+    const float eG = expf(static_cast<float>(G));
+    const float rk_i = rk_s[lane], rq_i = rq_s[lane], bi = b_s[lane];
+    const float sa = scale * rq_i * eG, sb = bi * rk_i * eG, scc = rk_i * expf(static_cast<float>(GC - G));
+    if constexpr (BF) {   // planes a | b | c | beta
+      float* sp = reinterpret_cast<float*>(sc + tile * CH);
+      sp[lane] = sa;
+      sp[CH + lane] = sb;
+      sp[2 * CH + lane] = scc;
+      sp[3 * CH + lane] = bi;
+    } else {
+      sc[tile * CH + lane] = make_float4(sa, sb, scc, bi);
+    }
+    if (lane == 0) egc[tile] = expf(static_cast<float>(GC));
+  }
 }
 
 // ------------------------------------------------------------------ state: bf16 inputs, 8 waves per 16 columns
@@ -502,7 +599,8 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(
 //   waves 0-3 (recurrence side): X = K S, R = beta v - b X, U = R + T R;
 //   waves 4-7 (output side):     Y = Q S, O = a Y + P U, computed transposed
 //                                (operands swapped) so a lane holds 4
-//                                consecutive columns of one token row.
+//                                consecutive columns of one token row, one
+//                                phase behind the recurrence side.
 // Wave w also owns rows 16w..16w+15 of S (128 x 16, fp32, one MFMA
 // accumulator) and updates them: S_w = e^{G_C} S_w + K[:, rows of w]^T (c U).
 // Waves w and w+4 share a SIMD, so each SIMD interleaves one wave of each side.
@@ -520,10 +618,12 @@ struct Prefetch {
   uint4 f[4];       // K (recurrence side) or Q (output side) blocks, k-steps 0..3 over dk
   uint4 x[4];       // T (recurrence) or P (output) blocks: hi k0, hi k1, lo k0, lo k1
   uint4 kt[2];      // K^T blocks of this wave's 16 rows of S, token k-steps 0, 1
-  uint4 st[2];      // staging wave only: per-token scalars and exp(G_C), or the V slice
 };
-constexpr int kScalarWave = 4;   // loads the chunk's scalar planes and exp(G_C)
-constexpr int kValueWave = 5;    // loads the chunk's 64 x 16 slice of V
+// Tiles 0 and 1 need only k-step 0 of T and P, so x[1] and x[3] are free on
+// waves 0, 1, 4, 5; two of those waves carry the per-chunk staging loads there
+// (their masks zero x[1] and x[3] wherever T or P blocks are formed).
+constexpr int kScalarWave = 4;   // per-token scalars (x[1]) and exp(G_C) (x[3].x)
+constexpr int kValueWave = 5;    // the chunk's 64 x 16 slice of V (x[1], x[3])
 // Every loaded word is consumed on every path of every wave that loads it: a
 // register whose load is still counted as pending when the compiler reuses it
 // makes it wait on the in-order counter, and with it on every later load.
@@ -606,8 +706,8 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
 
   int64_t s_begin, s_end;
   seq_bounds(cu, n, T, s_begin, s_end);
-  const int cbase = chunk_off[n];
-  const int nchunks = chunk_off[n + 1] - cbase;
+  int cbase, nchunks;
+  chunk_span(chunk_off, cu, T, n, cbase, nchunks);
 
   f32x4 S = {0.f, 0.f, 0.f, 0.f};        // rows 16w + 4lg + i, column col
   if (S0) {
@@ -648,8 +748,8 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
         // exp(G_C) through a vector load: a uniform (scalar) load would share
         // lgkmcnt with LDS traffic and stall the next LDS wait for a full
         // memory round trip
-        pf.st[0] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
-        pf.st[1].x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
+        pf.x[1] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
+        pf.x[3].x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
       }
     } else if (part == 1) {
       const rsrc_t rf = make_rsrc((rec ? kf : qf) + kt * TILE_ELEMS, TILE_ELEMS * 2);
@@ -661,8 +761,8 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
         const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
         const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
                                     static_cast<uint32_t>(((L - 1) * vs + D) * 2));
-        pf.st[0] = bload16(rv, vo0);
-        pf.st[1] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
+        pf.x[1] = bload16(rv, vo0);
+        pf.x[3] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
       }
     } else {
       const rsrc_t rk = make_rsrc(ktf + kt * TILE_ELEMS, TILE_ELEMS * 2);
@@ -673,15 +773,16 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
   // stage a chunk's scalars, exp(G_C) and V slice in LDS buffer `buf`
   auto commit = [&](const Prefetch& pf, int buf) {
     if (w == kScalarWave) {
-      *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = pf.st[0];
-      EGS[buf][lane] = bits_f(pf.st[1].x);
+      *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = pf.x[1];
+      EGS[buf][lane] = bits_f(pf.x[3].x);
     }
     if (w == kValueWave) {
       // lane holds V[t][8 (lane % 2) + e], e = 0..7, for t = 32i + lane / 2;
       // slot of (t, c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const uint32_t d[4] = {pf.st[i].x, pf.st[i].y, pf.st[i].z, pf.st[i].w};
+        const uint4& vi = pf.x[2 * i + 1];
+        const uint32_t d[4] = {vi.x, vi.y, vi.z, vi.w};
         const int t = 32 * i + (lane >> 1);
         uint16_t* base = &VS[buf][((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3)];
 #pragma unroll
@@ -692,26 +793,56 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
   };
   auto publish_S = [&]() { put_tile(SX, SXP, w, lane, S); };
 
-  // The output tile of chunk c is stored at the start of chunk c+1, after that
-  // chunk's first loads are issued: loads and stores share one in-order
-  // completion counter, so a store issued before a load would make every
-  // wait on that load also wait for the store to reach memory.
-  f32x4 Opend = {0.f, 0.f, 0.f, 0.f};
-  int cc_pend = -1;
+  // The output side runs one phase behind the recurrence side: Y of chunk c
+  // is formed in phase 2 of chunk c and kept in registers with chunk c's
+  // masked P blocks, and the O tile of chunk c in phase 1 of chunk c+1, from
+  // those, U of chunk c (still in LDS) and its scalars. The recurrence chain
+  // X -> R -> U -> S then never waits on output work, and the S reads split
+  // over two phases.
+  f32x4 Yprev = {0.f, 0.f, 0.f, 0.f};
+  uint4 Pprev[4] = {};
   // O^T tile: lane (lr, lg) holds O[token 16m + lr][columns 16 slice + 4lg + i]
   const uint32_t oo0 = static_cast<uint32_t>((row * nv * D + slice * 16 + 4 * lg) * sizeof(TO));
-  auto store_pending = [&]() {
-    const int64_t t0 = s_begin + static_cast<int64_t>(cc_pend) * CH;
+  // O^T = a Y^T + U^T P^T for chunk co (P slots hold tokens in reversed order:
+  // reverse U too), stored at once: the chunk's loads are already issued, and
+  // a store issued before a load would make every wait on that load also wait
+  // for the store (one in-order completion counter)
+  auto out_tile = [&](int co, const uint4 (&xp)[4]) {
+    f32x4 O0, O1 = {0.f, 0.f, 0.f, 0.f};
+    const float ar = SCS[co & 1][row];     // a of this lane's token row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) O0[i] = ar * Yprev[i];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s == 1 && !two_k) break;
+      const bf16x8 ah = as_bf16x8(xp[s]), al = as_bf16x8(xp[2 + s]);
+      const bf16x8 bh = as_bf16x8(rev8(lds16(UX + s * BLK_BYTES + lane * 16)));
+      const bf16x8 bl = as_bf16x8(rev8(lds16(UX + TXP + s * BLK_BYTES + lane * 16)));
+      f32x4& Oa = s == 0 ? O0 : O1;
+      Oa = mfma_bf16(bh, al, Oa);
+      Oa = mfma_bf16(bl, ah, Oa);
+      Oa = mfma_bf16(bh, ah, Oa);
+    }
+    float Ov[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ov[i] = O0[i] + O1[i];
+    const int64_t t0 = s_begin + static_cast<int64_t>(co) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
     const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
                                 static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
     if constexpr (sizeof(TO) == 4) {
-      // (__float_as_uint: a bit cast of a vector element is miscompiled to element 0)
-      bstore16(ro, oo0, make_uint4(__float_as_uint(Opend[0]), __float_as_uint(Opend[1]), __float_as_uint(Opend[2]),
-                                   __float_as_uint(Opend[3])));
+      bstore16(ro, oo0, make_uint4(__float_as_uint(Ov[0]), __float_as_uint(Ov[1]), __float_as_uint(Ov[2]),
+                                   __float_as_uint(Ov[3])));
     } else {
-      bstore8(ro, oo0, make_uint2(f32_to_bf16(Opend[0]) | (static_cast<uint32_t>(f32_to_bf16(Opend[1])) << 16),
-                                  f32_to_bf16(Opend[2]) | (static_cast<uint32_t>(f32_to_bf16(Opend[3])) << 16)));
+      bstore8(ro, oo0, make_uint2(f32_to_bf16(Ov[0]) | (static_cast<uint32_t>(f32_to_bf16(Ov[1])) << 16),
+                                  f32_to_bf16(Ov[2]) | (static_cast<uint32_t>(f32_to_bf16(Ov[3])) << 16)));
+    }
+  };
+  auto masked = [&](const Prefetch& pf, uint4 (&xa)[4]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      xa[s] = and4(pf.x[s], msk[s]);
+      xa[2 + s] = and4(pf.x[2 + s], msk[s]);
     }
   };
 
@@ -721,52 +852,42 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
   auto step = [&](int cc, const Prefetch& cur, const Prefetch& nxt, Prefetch& nxt2) {
     const int ln = min(cc + 2, nchunks - 1);   // past the end the last chunk is re-read
     const int buf = cc & 1;
-    // T/P operands, masked; the k-step 1 blocks of tiles 0 and 1 are not
-    // loaded, but are consumed here on every path (their mask is zero)
+    // masked T or P blocks of this chunk. The k-step 1 blocks of tiles 0 and 1
+    // are not loaded (or carry staging loads) but are consumed here on every
+    // path (their mask is zero).
     uint4 xa[4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      xa[s] = and4(cur.x[s], msk[s]);
-      xa[2 + s] = and4(cur.x[2 + s], msk[s]);
-    }
+    masked(cur, xa);
     load_chunk(ln, nxt2, 0);
-    if (!rec && cc_pend >= 0) store_pending();
 
-    // phase 1: X = K S (recurrence side) or Y^T = S^T Q^T (output side),
-    // hi and lo parts of S in two accumulators
-    f32x4 XH = {0.f, 0.f, 0.f, 0.f}, XL = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 a = as_bf16x8(cur.f[s]);
-      const bf16x8 sl = as_bf16x8(lds16(SX + SXP + s * BLK_BYTES + lane * 16));
-      const bf16x8 sh = as_bf16x8(lds16(SX + s * BLK_BYTES + lane * 16));
-      if (rec) {
-        XL = mfma_bf16(a, sl, XL);
-        XH = mfma_bf16(a, sh, XH);
-      } else {
-        XL = mfma_bf16(sl, a, XL);
-        XH = mfma_bf16(sh, a, XH);
-      }
-    }
-    f32x4 XY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) XY[i] = XH[i] + XL[i];
+    // phase 1: X = K S and R = beta v - b X (recurrence side); O of the
+    // previous chunk (output side)
     f32x4 Ra = {0.f, 0.f, 0.f, 0.f};
     const int srow = 16 * m + 4 * lg;      // first of this lane's 4 accumulator rows
-    if (rec) {   // R = beta v - b X
+    if (rec) {
+      f32x4 XH = {0.f, 0.f, 0.f, 0.f}, XL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = as_bf16x8(cur.f[s]);
+        XL = mfma_bf16(a, as_bf16x8(lds16(SX + SXP + s * BLK_BYTES + lane * 16)), XL);
+        XH = mfma_bf16(a, as_bf16x8(lds16(SX + s * BLK_BYTES + lane * 16)), XH);
+      }
       const float4 bb = *reinterpret_cast<const float4*>(&SCS[buf][CH + srow]);
       const float4 be = *reinterpret_cast<const float4*>(&SCS[buf][3 * CH + srow]);
       const uint2 vv = *reinterpret_cast<const uint2*>(&VS[buf][(m * 64 + lane) * 4]);
-      Ra[0] = be.x * bf16_to_f32(static_cast<uint16_t>(vv.x)) - bb.x * XY[0];
-      Ra[1] = be.y * bf16_to_f32(static_cast<uint16_t>(vv.x >> 16)) - bb.y * XY[1];
-      Ra[2] = be.z * bf16_to_f32(static_cast<uint16_t>(vv.y)) - bb.z * XY[2];
-      Ra[3] = be.w * bf16_to_f32(static_cast<uint16_t>(vv.y >> 16)) - bb.w * XY[3];
+      Ra[0] = be.x * bf16_to_f32(static_cast<uint16_t>(vv.x)) - bb.x * (XH[0] + XL[0]);
+      Ra[1] = be.y * bf16_to_f32(static_cast<uint16_t>(vv.x >> 16)) - bb.y * (XH[1] + XL[1]);
+      Ra[2] = be.z * bf16_to_f32(static_cast<uint16_t>(vv.y)) - bb.z * (XH[2] + XL[2]);
+      Ra[3] = be.w * bf16_to_f32(static_cast<uint16_t>(vv.y >> 16)) - bb.w * (XH[3] + XL[3]);
       put_tile(RX, TXP, m, lane, Ra);
+    } else if (cc > 0) {
+      out_tile(cc - 1, Pprev);
     }
     __syncthreads();
     load_chunk(ln, nxt2, 1);
 
-    // phase 2: U = R + T_strict R -> U and c U tiles
+    // phase 2: U = R + T_strict R -> U and c U tiles (recurrence side);
+    // Y^T = S^T Q^T of this chunk, hi and lo parts of S in two accumulators
+    // (output side)
     if (rec) {
       f32x4 U0 = Ra, U1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -790,33 +911,24 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
       }
       put_tile(UX, TXP, m, lane, Ua);
       put_tile(CX, TXP, m, lane, cU);
+    } else {
+      f32x4 YH = {0.f, 0.f, 0.f, 0.f}, YL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = as_bf16x8(cur.f[s]);
+        YL = mfma_bf16(as_bf16x8(lds16(SX + SXP + s * BLK_BYTES + lane * 16)), a, YL);
+        YH = mfma_bf16(as_bf16x8(lds16(SX + s * BLK_BYTES + lane * 16)), a, YH);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Yprev[i] = YH[i] + YL[i];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Pprev[s] = xa[s];
     }
     __syncthreads();
     load_chunk(ln, nxt2, 2);
 
-    // phase 3: O^T = a Y^T + U^T P^T (P slots hold tokens in reversed order: reverse U too)
-    if (!rec) {
-      f32x4 O0, O1 = {0.f, 0.f, 0.f, 0.f};
-      const float ar = SCS[buf][row];      // a of this lane's token row
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O0[i] = ar * XY[i];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s == 1 && !two_k) break;
-        const bf16x8 ah = as_bf16x8(xa[s]), al = as_bf16x8(xa[2 + s]);
-        const bf16x8 bh = as_bf16x8(rev8(lds16(UX + s * BLK_BYTES + lane * 16)));
-        const bf16x8 bl = as_bf16x8(rev8(lds16(UX + TXP + s * BLK_BYTES + lane * 16)));
-        f32x4& Oa = s == 0 ? O0 : O1;
-        Oa = mfma_bf16(bh, al, Oa);
-        Oa = mfma_bf16(bl, ah, Oa);
-        Oa = mfma_bf16(bh, ah, Oa);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Opend[i] = O0[i] + O1[i];   // stored at the start of the next chunk
-      cc_pend = cc;
-    }
-
-    // S_w = e^{G_C} S_w + K[:, rows of w]^T (c U), the two token k-steps in two accumulators
+    // phase 3: S_w = e^{G_C} S_w + K[:, rows of w]^T (c U), the two token
+    // k-steps in two accumulators
     {
       const float eGC = EGS[buf][0];
       f32x4 S1 = {0.f, 0.f, 0.f, 0.f};
@@ -840,7 +952,7 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
     __syncthreads();
   };
 
-  Prefetch pa, pb, pc;
+  Prefetch pa{}, pb{}, pc{};
   if (nchunks > 0) {
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
@@ -862,7 +974,7 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
   }
   if (cc < nchunks) step(cc, pa, pb, pc);
   if (cc + 1 < nchunks) step(cc + 1, pb, pc, pa);
-  if (!rec && cc_pend >= 0) store_pending();
+  if (!rec && nchunks > 0) out_tile(nchunks - 1, Pprev);   // the last chunk's output
 
   if (ST) {
 #pragma unroll
@@ -921,7 +1033,8 @@ __global__ void __launch_bounds__(64) chunk_state_generic_kernel(
 
   int64_t s_begin, s_end;
   seq_bounds(cu, n, T, s_begin, s_end);
-  const int nchunks = chunk_off[n + 1] - chunk_off[n];
+  int cbase, nchunks;
+  chunk_span(chunk_off, cu, T, n, cbase, nchunks);
 
   f32x4 S[8];
 #pragma unroll
@@ -933,7 +1046,7 @@ __global__ void __launch_bounds__(64) chunk_state_generic_kernel(
   for (int cc = 0; cc < nchunks; ++cc) {
     const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-    const size_t tile = static_cast<size_t>(chunk_off[n] + cc) * nv + h;
+    const size_t tile = static_cast<size_t>(cbase + cc) * nv + h;
     __syncthreads();
     load_tile_64x128(k + t0 * ks + static_cast<int64_t>(hk) * D, ks, L, Ks, lane, 64);
     load_tile_64x128(q + t0 * qs + static_cast<int64_t>(hk) * D, qs, L, Qs, lane, 64);
@@ -1073,16 +1186,19 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   uint16_t* ktf = BF ? reinterpret_cast<uint16_t*>(base + lay.off_ktf) : nullptr;
 
   const int64_t nch = T / CH + n_seqs;
-  chunk_offsets_kernel<<<1, 256, 0, s>>>(cu, n_seqs, T, static_cast<int32_t>(nch), chunk_off);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (cu) {   // varlen chunk table (one sequence needs none)
+    chunk_offsets_kernel<<<1, 256, 0, s>>>(cu, n_seqs, T, static_cast<int32_t>(nch), chunk_off);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   {
     auto kern = chunk_prep_kernel<TIn>;
     const size_t lds = prep_lds_bytes<TIn>();
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    kern<<<dim3(static_cast<unsigned>(nv), static_cast<unsigned>(nch)), 64, lds, s>>>(
+    kern<<<dim3(static_cast<unsigned>(nv), static_cast<unsigned>(nch)), 64 * PREP_WAVES, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, g, beta, cu, n_seqs, T, nk, nv, scale, l2,
         chunk_off, tp, sc, egc, kf, qf, ktf);
     e = hipGetLastError();
