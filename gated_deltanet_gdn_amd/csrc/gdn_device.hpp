@@ -17,10 +17,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
+  __device__ static __forceinline__ float cvt(float x) { return x; }
   __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
   __device__ static __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
 };
 template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float cvt(uint16_t x) { return bf16_to_f32(x); }
   __device__ static __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ static __forceinline__ void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
