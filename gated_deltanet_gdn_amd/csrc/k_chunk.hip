@@ -732,7 +732,8 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
   const uint32_t vo0 = static_cast<uint32_t>(((lane >> 1) * vs + slice * 16 + 8 * (lane & 1)) * 2);
 
   // group 0: T/P blocks (and the scalar block on the scalar wave); group 1:
-  // K/Q blocks (and V on the value wave); group 2: K^T blocks
+  // K^T blocks (and V on the value wave); group 2: K/Q blocks -- the larger
+  // groups go to the phases with less LDS traffic
   auto load_chunk = [&](int cc, Prefetch& pf, int part) {
     const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;    // (chunk, value head)
     const size_t kt = static_cast<size_t>(cbase + cc) * nk + hk;   // (chunk, key head)
@@ -752,9 +753,9 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
         pf.x[3].x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
       }
     } else if (part == 1) {
-      const rsrc_t rf = make_rsrc((rec ? kf : qf) + kt * TILE_ELEMS, TILE_ELEMS * 2);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) pf.f[s] = bload16(rf, fo + s * BLK_BYTES);
+      const rsrc_t rk = make_rsrc(ktf + kt * TILE_ELEMS, TILE_ELEMS * 2);
+      pf.kt[0] = bload16(rk, kto);
+      pf.kt[1] = bload16(rk, kto + BLK_BYTES);
       if (w == kValueWave) {
         // V rows past the sequence end read as zeros (resource sized to the valid rows)
         const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
@@ -765,9 +766,9 @@ __global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
         pf.x[3] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
       }
     } else {
-      const rsrc_t rk = make_rsrc(ktf + kt * TILE_ELEMS, TILE_ELEMS * 2);
-      pf.kt[0] = bload16(rk, kto);
-      pf.kt[1] = bload16(rk, kto + BLK_BYTES);
+      const rsrc_t rf = make_rsrc((rec ? kf : qf) + kt * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) pf.f[s] = bload16(rf, fo + s * BLK_BYTES);
     }
   };
   // stage a chunk's scalars, exp(G_C) and V slice in LDS buffer `buf`
