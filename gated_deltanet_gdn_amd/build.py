@@ -33,9 +33,15 @@ COMMON = [
 ]
 
 
+# The chunk kernels run one workgroup per CU (their LDS needs), so the compiler
+# would place MFMA accumulators in AGPRs and copy them out for every VALU use;
+# keep MFMA results in VGPRs.
+EXTRA = {"k_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

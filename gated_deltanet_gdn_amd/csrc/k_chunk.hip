@@ -22,26 +22,28 @@
 // Kernels:
 //   chunk_offsets : exclusive prefix of ceil(len/64) over sequences (varlen
 //                   chunk table on the device; no host synchronisation).
-//   chunk_prep    : one wave per (chunk, value head), fully parallel. Grams
+//   chunk_prep    : four waves per (chunk, value head), fully parallel. Grams
 //                   K K^T and Q K^T on MFMA from the raw inputs (exact
-//                   operands, kept in registers), fp64 cumsum of g, A, the
-//                   blocked inverse T (16x16 diagonal blocks by substitution,
-//                   off-diagonal blocks on MFMA), P and per-token scalars.
-//                   Output per (chunk, value head): one packed 64x64 fp32
-//                   tile X with X[i][j] = T[i][j] for j < i and
-//                   X[63-i][63-j] = P[i][j] for j <= i (P turned by 180
-//                   degrees into the upper triangle), so rows of both T and
-//                   P are contiguous; plus 64 float4 scalars and exp(G_C).
-//   chunk_state   : sequential over a sequence's chunks. bf16 inputs: four
-//                   waves per (sequence, value head, 16 value columns); wave
-//                   w holds rows 32w..32w+31 of S (128 x 16, fp32) in MFMA
-//                   accumulators and computes token rows 16w..16w+15 of the
-//                   chunk; S is exchanged through LDS once per chunk. Q, T,
-//                   P and V operands are loaded straight into registers in
-//                   MFMA fragment layout one chunk ahead; K is staged in LDS
-//                   (double-buffered) because the state update reads it
-//                   transposed. fp32 inputs use a simple one-wave variant.
-//                   Products with an fp32 operand split it into bf16 hi + lo.
+//                   operands), fp64 cumsum of g, A, the blocked inverse T
+//                   (16x16 diagonal blocks by substitution, off-diagonal
+//                   blocks on MFMA), P and per-token scalars. Output per
+//                   (chunk, value head): one packed 64x64 tile X with
+//                   X[i][j] = T[i][j] for j < i and X[63-i][63-j] = P[i][j]
+//                   for j <= i (P turned by 180 degrees into the upper
+//                   triangle), the scalars a, b, c, beta per token and
+//                   exp(G_C); for bf16 inputs X is split into bf16 hi + lo
+//                   planes and, per (chunk, key head), the raw K and Q rows
+//                   are re-laid in MFMA fragment order.
+//   chunk_state   : sequential over a sequence's chunks, one workgroup per
+//                   (sequence, value head, 16 value columns). bf16 inputs:
+//                   four waves, one per SIMD -- two recurrence waves that
+//                   each own half of the rows of S (in MFMA accumulators) and
+//                   swap partial products K S through LDS once per chunk, and
+//                   two output waves one chunk behind. fp32 inputs use a
+//                   simple one-wave variant. Products with an fp32 operand
+//                   split it into bf16 hi + lo.
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -56,10 +58,10 @@ constexpr float kEps = 1e-6f;
 constexpr int TILE_ELEMS = CH * D;   // bf16 elements of one 16 KB operand tile
 
 // Workspace: chunk table | per (chunk, value head): 16 KB tile, 1 KB of
-// per-token scalars, exp(G_C) | bf16 inputs only, per (chunk, key head): K, Q
-// and K^T operand tiles of 16 KB each.
+// per-token scalars, exp(G_C) | bf16 inputs only, per (chunk, key head): K and
+// Q operand tiles of 16 KB each.
 struct WsLayout {
-  size_t off_chunk_off, off_tp, off_sc, off_egc, off_kf, off_qf, off_ktf, total;
+  size_t off_chunk_off, off_tp, off_sc, off_egc, off_kf, off_qf, total;
 };
 inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
   const int64_t nch = T / CH + n_seqs;   // >= sum_n ceil(len_n / 64)
@@ -70,11 +72,10 @@ inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
   w.off_tp = o;        o += static_cast<size_t>(nch) * nv * tile_bytes;
   w.off_sc = o;        o += static_cast<size_t>(nch) * nv * CH * sizeof(float4);
   w.off_egc = o;       o += static_cast<size_t>(nch) * nv * sizeof(float); o = (o + 255) & ~size_t(255);
-  w.off_kf = w.off_qf = w.off_ktf = o;
+  w.off_kf = w.off_qf = o;
   if (bf16) {
     w.off_kf = o;  o += static_cast<size_t>(nch) * nk * tile_bytes;
     w.off_qf = o;  o += static_cast<size_t>(nch) * nk * tile_bytes;
-    w.off_ktf = o; o += static_cast<size_t>(nch) * nk * tile_bytes;
   }
   w.total = o;
   return w;
@@ -225,53 +226,6 @@ __device__ __forceinline__ void write_row_blocks(const uint16_t* tile, int L, ui
         zero_if(row >= L, make_uint4(a.x, a.y, b.x, b.y));
   }
 }
-// K tile in LDS -> transposed blocks (w, s), w = 16 rows of dk, s = 32-token
-// k-step: lane (lr, lg) holds K[32s + perm32(lg, j)][16w + lr], tokens >= L
-// zero. This call writes w = 2 s2, 2 s2 + 1 (dk step s2). The transpose runs
-// on MFMA: with A = 16 token rows x 32 dk of K and B = a 0/1 matrix that picks
-// dk 16w + c for column c, D = K[16t + r][16w + c] lands in accumulator order
-// (lane (c, lg) holds rows 4 lg .. +3), which is slots 0-3 (t = 2s) or 4-7
-// (t = 2s + 1) of the block. Each D entry is a single bf16 product with 1, so
-// it converts back to bf16 exactly.
-template <int EP>
-__device__ __forceinline__ void write_col_blocks(const uint16_t* tile, int L, uint16_t* __restrict__ dst, int lane,
-                                                 int s2) {
-  const int lr = lane & 15, lg = lane >> 4;
-  // sel[hh] picks dk 16 hh + lr out of the 32-wide step (B slot (lg, j) is dk 8 lg + j)
-  bf16x8 sel[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    uint32_t d[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int k0 = 8 * lg + 2 * p;
-      d[p] = (k0 == 16 * hh + lr ? 0x3f80u : 0u) | (k0 + 1 == 16 * hh + lr ? 0x3f800000u : 0u);
-    }
-    sel[hh] = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
-  }
-  f32x4 Dt[2][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int row = 16 * t + lr;
-    const bf16x8 a = __builtin_bit_cast(
-        bf16x8, zero_if(row >= L, *reinterpret_cast<const uint4*>(tile + row * EP + 32 * s2 + 8 * lg)));
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) Dt[hh][t] = mfma_bf16(a, sel[hh], f32x4{0.f, 0.f, 0.f, 0.f});
-  }
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int w = 2 * s2 + hh;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const f32x4& lo = Dt[hh][2 * s];
-      const f32x4& hi = Dt[hh][2 * s + 1];
-      uint2 p0, p1, unused;
-      split4_packed(make_float4(lo[0], lo[1], lo[2], lo[3]), p0, unused);
-      split4_packed(make_float4(hi[0], hi[1], hi[2], hi[3]), p1, unused);
-      *reinterpret_cast<uint4*>(dst + (2 * w + s) * BLK_ELEMS + lane * 8) = make_uint4(p0.x, p0.y, p1.x, p1.y);
-    }
-  }
-}
 // packed T|P tile in LDS (fp32 [64][AP]) -> blocks (m, s) per plane, hi plane
 // then lo: lane (lr, lg) holds X[16m + lr][32s + perm32(lg, j)]. This call
 // writes tile m's blocks.
@@ -335,7 +289,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int n_seqs, int64_t T, int nk, int nv, float scale, int l2, const int32_t* __restrict__ chunk_off,
     float* __restrict__ tp, float4* __restrict__ sc, float* __restrict__ egc, uint16_t* __restrict__ kf,
-    uint16_t* __restrict__ qf, uint16_t* __restrict__ ktf) {
+    uint16_t* __restrict__ qf) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int EP = prep_pitch<TIn>();
   using MG = Mma<BF, true, true>;
@@ -437,17 +391,14 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
       }
     }
   }
-  // 3b. bf16 inputs: K, Q and K^T operand blocks of the state recurrence,
-  //     once per key head: K and Q by its first value head, K^T by its last;
-  //     wave wv writes token tile wv (K, Q) and dk step wv (K^T)
+  // 3b. bf16 inputs: K and Q operand blocks of the state recurrence, once
+  //     per key head: K by its first value head, Q by its last; wave wv
+  //     writes token tile wv
   if constexpr (BF) {
     const int r = nv / nk, rho = h % r;
     const size_t kt = (static_cast<size_t>(c) * nk + hk) * TILE_ELEMS;
-    if (rho == 0) {
-      write_row_blocks<EP>(Ks, L, kf + kt, lane, wv);
-      write_row_blocks<EP>(Qs, L, qf + kt, lane, wv);
-    }
-    if (rho == r - 1) write_col_blocks<EP>(Ks, L, ktf + kt, lane, wv);
+    if (rho == 0) write_row_blocks<EP>(Ks, L, kf + kt, lane, wv);
+    if (rho == r - 1) write_row_blocks<EP>(Qs, L, qf + kt, lane, wv);
   }
   // 4. |k_i|^2 from the Gram diagonals (pairs 0, 2, 5, 9)
 #pragma unroll
@@ -593,40 +544,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   }
 }
 
-// ------------------------------------------------------------------ state: bf16 inputs, 8 waves per 16 columns
-// One workgroup per (sequence, value head, 16 value columns), eight waves with
-// two roles over the chunk's four 16-token tiles m = w % 4:
-//   waves 0-3 (recurrence side): X = K S, R = beta v - b X, U = R + T R;
-//   waves 4-7 (output side):     Y = Q S, O = a Y + P U, computed transposed
-//                                (operands swapped) so a lane holds 4
-//                                consecutive columns of one token row, one
-//                                phase behind the recurrence side.
-// Wave w also owns rows 16w..16w+15 of S (128 x 16, fp32, one MFMA
-// accumulator) and updates them: S_w = e^{G_C} S_w + K[:, rows of w]^T (c U).
-// Waves w and w+4 share a SIMD, so each SIMD interleaves one wave of each side.
-//
-// Every operand comes from the workspace as contiguous blocks already in
-// fragment order (see the operand-block writers), loaded two chunks ahead
-// into three rotating register sets, in three groups spread over the chunk's
-// three phases so the memory pipe never backs up into the waves. Tiles
-// produced inside the chunk (S, R, U, c U) are split into bf16 hi + lo by
-// the producing wave and pass through LDS in the same block order, so a
-// consumer reads its share of a B operand with one 16-byte read per plane.
 constexpr int BLK_BYTES = BLK_ELEMS * 2;
-
-struct Prefetch {
-  uint4 f[4];       // K (recurrence side) or Q (output side) blocks, k-steps 0..3 over dk
-  uint4 x[4];       // T (recurrence) or P (output) blocks: hi k0, hi k1, lo k0, lo k1
-  uint4 kt[2];      // K^T blocks of this wave's 16 rows of S, token k-steps 0, 1
-};
-// Tiles 0 and 1 need only k-step 0 of T and P, so x[1] and x[3] are free on
-// waves 0, 1, 4, 5; two of those waves carry the per-chunk staging loads there
-// (their masks zero x[1] and x[3] wherever T or P blocks are formed).
-constexpr int kScalarWave = 4;   // per-token scalars (x[1]) and exp(G_C) (x[3].x)
-constexpr int kValueWave = 5;    // the chunk's 64 x 16 slice of V (x[1], x[3])
-// Every loaded word is consumed on every path of every wave that loads it: a
-// register whose load is still counted as pending when the compiler reuses it
-// makes it wait on the in-order counter, and with it on every later load.
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ uint4 and4(const uint4& a, const uint4& m) {
@@ -637,352 +555,487 @@ __device__ __forceinline__ uint4 rev8(const uint4& a) {
   auto sw = [](uint32_t d) { return (d >> 16) | (d << 16); };
   return make_uint4(sw(a.w), sw(a.z), sw(a.y), sw(a.x));
 }
-__device__ __forceinline__ uint4 lds16(const unsigned char* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// Accumulator tile -> LDS exchange slot: a lane's 4 rows of 16-row tile t
-// are slots 4 (t % 2) .. +3 of that lane's 16 bytes in k-step t / 2.
-__device__ __forceinline__ void put_tile(unsigned char* X, int planes_off, int t, int lane, const f32x4& v) {
-  uint2 hi, lo;
-  split4_packed(make_float4(v[0], v[1], v[2], v[3]), hi, lo);
-  unsigned char* p = X + (t >> 1) * BLK_BYTES + lane * 16 + (t & 1) * 8;
-  *reinterpret_cast<uint2*>(p) = hi;
-  *reinterpret_cast<uint2*>(p + planes_off) = lo;
+// ------------------------------------------------------------------ state: bf16 inputs, 4 waves per 16 columns
+// One workgroup per (sequence, value head, 16 value columns), one wave per SIMD.
+//   Waves 0 and 1 (recurrence): wave h owns rows 64h .. 64h+63 of S (128 x 16
+//     fp32, four MFMA accumulators). Per chunk it forms its partial product
+//     X_h = K[:, rows of h] S_h and swaps it with the other half through LDS
+//     (the chunk's one barrier); both waves then form X = X_0 + X_1,
+//     R = beta v - b X, U = R + T_strict R and c U, bit-identical in both,
+//     and update their own rows: S_h = e^{G_C} S_h + K[:, rows of h]^T (c U).
+//   Waves 2 and 3 (output), one chunk behind: Y^T = S^T Q^T for two token
+//     tiles, then O^T = a Y^T + U^T P^T, from S and U published in LDS; the
+//     operands are swapped so that a lane holds 4 consecutive columns of one
+//     token row and the tile goes out as one 16-byte store per lane. Wave 2
+//     takes tiles 0 and 3, wave 3 tiles 1 and 2 (equal P work).
+// The output waves also stage chunk inputs in LDS for the recurrence waves,
+// one chunk ahead: wave 2 the masked T blocks (both recurrence waves use all
+// of them), wave 3 the per-token scalars, exp(G_C) and beta * v in
+// accumulator layout.
+//
+// Barrier B(c) separates: the recurrence waves' S_c (as bf16 hi | lo) and
+// partial X_c, and the staged inputs of chunk c, all written before it; after
+// it the recurrence waves finish chunk c and start c+1, and the output waves
+// form Y of chunk c and O of chunk c-1 (U_{c-1} was written before B(c)).
+// Every LDS buffer is double-buffered by chunk parity: a buffer written
+// between B(c-1) and B(c) is read only between B(c) and B(c+1).
+
+constexpr int KL_BLK = 64 * 16 + 4 * 64;   // one padded K block in LDS
+
+// LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives in slot j the (i % 4)-th 16-bit element of the 8 bytes addressed
+// by lane 4 j + i / 4 of the group.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
 }
+// lane l's 16 bytes in a padded LDS K block
+__device__ __forceinline__ int kl_lane(int l) { return 16 * l + 64 * (l >> 4); }
 
 template <typename TO>
-__global__ void __launch_bounds__(512) chunk_state_bf16_kernel(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) chunk_state_bf16_kernel(
     const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
     int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
     const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
-    const uint16_t* __restrict__ ktf, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
-  // exchange tiles, each [plane hi | plane lo][k-step][64 lanes][16 B]
-  __shared__ __attribute__((aligned(16))) unsigned char SX[2 * 4 * BLK_BYTES];   // S, 4 dk k-steps
-  __shared__ __attribute__((aligned(16))) unsigned char RX[2 * 2 * BLK_BYTES];   // R, 2 token k-steps
-  __shared__ __attribute__((aligned(16))) unsigned char UX[2 * 2 * BLK_BYTES];   // U
-  __shared__ __attribute__((aligned(16))) unsigned char CX[2 * 2 * BLK_BYTES];   // c U
-  constexpr int SXP = 4 * BLK_BYTES, TXP = 2 * BLK_BYTES;                        // plane offsets
-  // per-chunk inputs staged by one wave each, double-buffered by chunk parity:
-  // scalar planes a | b | c | beta over the 64 tokens, exp(G_C) (every entry),
-  // and V of the four recurrence tiles in accumulator order [tile][lane][row]
-  __shared__ __attribute__((aligned(16))) float SCS[2][4 * CH];
-  __shared__ float EGS[2][64];
-  __shared__ __attribute__((aligned(16))) uint16_t VS[2][4 * 64 * 4];
+    const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
+  __shared__ f32x4 XPX[2][2][4][64];     // partial X: [parity][half][token tile][lane]
+  __shared__ uint4 SBX[2][2][4][64];     // S as B operand: [parity][hi | lo][dk k-step][lane]
+  __shared__ f32x4 UXF[2][4][64];        // U, accumulator layout: [parity][token tile][lane]
+  __shared__ f32x4 BVS[2][4][64];        // beta * v, accumulator layout
+  __shared__ uint4 TSX[2][12][64];       // masked T blocks: [parity][hi (6) | lo (6)][lane]
+  // each recurrence wave's K blocks of the current chunk, read back transposed;
+  // lane l at byte 16 l + 64 (l / 16) of its block (the pad spreads the
+  // transposed reads over all banks)
+  __shared__ __attribute__((aligned(16))) unsigned char KLX[2][8][KL_BLK];
+  __shared__ __attribute__((aligned(16))) float SCS[2][4 * CH];   // planes a | b | c | beta
+  __shared__ float EGS[2];               // exp(G_C)
 
   const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int slice = bid & 7;
-  const int unit = bid >> 3;               // n * nv + h
+  const int unit = bid >> 3;             // n * nv + h
   const int n = unit / nv, h = unit % nv;
   const int hk = h / (nv / nk);
-  // the wave index is wave-uniform; say so, so that every wave-level value
-  // (role, tile, buffer descriptors) lives in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool rec = w < 4;                  // recurrence side (wave-uniform)
-  const int m = w & 3;                     // token tile of this wave
   const int lr = lane & 15, lg = lane >> 4;
   const int col = slice * 16 + lr;
-  const int row = 16 * m + lr;             // this lane's token row as an A-operand row
-
-  // masks of the triangular blocks (constant over chunks): T needs token <
-  // row; P slot j holds token 32s + perm32(lg, 7 - j) and needs it <= row
-  uint4 msk[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    uint32_t mm[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      bool lo, hi;
-      if (rec) {
-        lo = 32 * s + perm32(lg, 2 * d) < row;
-        hi = 32 * s + perm32(lg, 2 * d + 1) < row;
-      } else {
-        lo = 32 * s + perm32(lg, 7 - 2 * d) <= row;
-        hi = 32 * s + perm32(lg, 6 - 2 * d) <= row;
-      }
-      mm[d] = (lo ? 0x0000ffffu : 0u) | (hi ? 0xffff0000u : 0u);
-    }
-    msk[s] = make_uint4(mm[0], mm[1], mm[2], mm[3]);
-  }
+  const uint32_t lo16 = static_cast<uint32_t>(lane * 16);
 
   int64_t s_begin, s_end;
   seq_bounds(cu, n, T, s_begin, s_end);
   int cbase, nchunks;
   chunk_span(chunk_off, cu, T, n, cbase, nchunks);
 
-  f32x4 S = {0.f, 0.f, 0.f, 0.f};        // rows 16w + 4lg + i, column col
-  if (S0) {
+  if (w < 2) {
+    // ================================================================ recurrence waves
+    // The half is a compile-time constant in each instantiation: register
+    // arrays are then indexed by constants only (a wave-uniform runtime index
+    // into a register array becomes indirect register moves, whose reads of
+    // fresh MFMA results the compiler does not protect with wait states).
+    auto rec_role = [&](auto hfc) {
+      constexpr int hf = decltype(hfc)::value;
+      f32x4 S[4];                          // rows 64 hf + 16 tt + 4 lg + i, column col
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[i] = S0[(static_cast<int64_t>(unit) * D + 16 * w + 4 * lg + i) * D + col];
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[tt][i] = S0 ? S0[(static_cast<int64_t>(unit) * D + 64 * hf + 16 * tt + 4 * lg + i) * D + col] : 0.0f;
+
+      if (nchunks > 0) {
+        // operand blocks of one chunk, one register set: each group is reloaded
+        // for the next chunk right after its last use
+        uint4 kb[4][2];                    // K (token tile m, dk k-step 2 hf + kk)
+        auto load_k = [&](int cc) {
+          const size_t kt = static_cast<size_t>(cbase + cc) * nk + hk;
+          const rsrc_t r = make_rsrc(kf + kt * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) kb[m][kk] = bload16(r, (4 * m + 2 * hf + kk) * BLK_BYTES + lo16);
+        };
+        f32x4 Xp[4];
+        // S_c as B operand (published for the output waves) and this half's X_c
+        auto first_half = [&](int c) {
+          const int buf = c & 1;
+          uint4 sh[2], sl[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            uint2 h0, l0, h1, l1;
+            split4_packed(make_float4(S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3]), h0, l0);
+            split4_packed(make_float4(S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]), h1, l1);
+            sh[kk] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            sl[kk] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+            SBX[buf][0][2 * hf + kk][lane] = sh[kk];
+            SBX[buf][1][2 * hf + kk][lane] = sl[kk];
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              x = mfma_bf16(as_bf16x8(kb[m][kk]), as_bf16x8(sl[kk]), x);
+              x = mfma_bf16(as_bf16x8(kb[m][kk]), as_bf16x8(sh[kk]), x);
+            }
+            Xp[m] = x;
+            XPX[buf][hf][m][lane] = x;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+              *reinterpret_cast<uint4*>(&KLX[hf][2 * m + kk][kl_lane(lane)]) = kb[m][kk];
+          }
+          load_k(min(c + 1, nchunks - 1));
+        };
+        // the rest of chunk c: X, R, U, c U, and the update of this half of S
+        auto second_half = [&](int c) {
+          const int buf = c & 1;
+          const int ln = min(c + 1, nchunks - 1);
+          f32x4 R[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 xo = XPX[buf][1 - hf][m][lane];
+            const f32x4 bv = BVS[buf][m][lane];
+            const float4 bb = *reinterpret_cast<const float4*>(&SCS[buf][CH + 16 * m + 4 * lg]);
+            const float bbv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R[m][i] = bv[i] - bbv[i] * (Xp[m][i] + xo[i]);
+          }
+          uint4 rh[2], rl[2];              // R as B operand, token k-steps 0, 1
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            uint2 h0, l0, h1, l1;
+            split4_packed(make_float4(R[2 * s][0], R[2 * s][1], R[2 * s][2], R[2 * s][3]), h0, l0);
+            split4_packed(make_float4(R[2 * s + 1][0], R[2 * s + 1][1], R[2 * s + 1][2], R[2 * s + 1][3]), h1, l1);
+            rh[s] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            rl[s] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+          }
+          // T blocks (m, s): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), masked, hi | lo
+          uint4 mh[6], ml[6];
+#pragma unroll
+          for (int b = 0; b < 6; ++b) {
+            mh[b] = TSX[buf][b][lane];
+            ml[b] = TSX[buf][6 + b][lane];
+          }
+          // U = R + T_strict R
+          f32x4 U[4];
+          auto tr = [&](f32x4& acc, int b, int s) {
+            acc = mfma_bf16(as_bf16x8(ml[b]), as_bf16x8(rh[s]), acc);
+            acc = mfma_bf16(as_bf16x8(mh[b]), as_bf16x8(rl[s]), acc);
+            acc = mfma_bf16(as_bf16x8(mh[b]), as_bf16x8(rh[s]), acc);
+          };
+#pragma unroll
+          for (int m = 0; m < 4; ++m) U[m] = R[m];
+          tr(U[0], 0, 0);
+          tr(U[1], 1, 0);
+          tr(U[2], 2, 0);
+          tr(U[3], 4, 0);
+          tr(U[2], 3, 1);
+          tr(U[3], 5, 1);
+          // U of this wave's two tiles for the output waves; c U as B operand
+#pragma unroll
+          for (int u = 0; u < 2; ++u) UXF[buf][2 * hf + u][lane] = U[2 * hf + u];
+          f32x4 cU[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float4 c4 = *reinterpret_cast<const float4*>(&SCS[buf][2 * CH + 16 * m + 4 * lg]);
+            cU[m][0] = c4.x * U[m][0];
+            cU[m][1] = c4.y * U[m][1];
+            cU[m][2] = c4.z * U[m][2];
+            cU[m][3] = c4.w * U[m][3];
+          }
+          uint4 ch[2], cl[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            uint2 h0, l0, h1, l1;
+            split4_packed(make_float4(cU[2 * s][0], cU[2 * s][1], cU[2 * s][2], cU[2 * s][3]), h0, l0);
+            split4_packed(make_float4(cU[2 * s + 1][0], cU[2 * s + 1][1], cU[2 * s + 1][2], cU[2 * s + 1][3]), h1, l1);
+            ch[s] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            cl[s] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+          }
+          const float eg = EGS[buf];
+          // K^T blocks of this wave's rows of S (dk tile 4 hf + tt, token
+          // k-step s), read transposed from this chunk's K blocks: addressing
+          // lane (lr, lg) points at token 32 s + 16 h + 4 lg + lr / 4, dk
+          // 16 tt + 4 (lr % 4) .. +3, which sits in block (2 s + h, tt / 2),
+          // block lane 16 (lr % 4) + 4 lg + lr / 4, bytes 8 (tt % 2) ..
+          // (the reads stay next to their MFMAs: hoisted, their results
+          // would be live across the whole chunk)
+          const int kl = kl_lane(16 * (lr & 3) + 4 * lg + (lr >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            uint4 ktb[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const uint2 x0 = lds_tr16(&KLX[hf][2 * (2 * s) + tt / 2][kl + 8 * (tt & 1)]);
+              const uint2 x1 = lds_tr16(&KLX[hf][2 * (2 * s + 1) + tt / 2][kl + 8 * (tt & 1)]);
+              ktb[s] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[tt][i] *= eg;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              S[tt] = mfma_bf16(as_bf16x8(ktb[s]), as_bf16x8(cl[s]), S[tt]);
+              S[tt] = mfma_bf16(as_bf16x8(ktb[s]), as_bf16x8(ch[s]), S[tt]);
+            }
+          }
+        };
+
+        load_k(0);
+        first_half(0);
+        // the last pass also runs first_half for a chunk n that does not exist:
+        // it writes buffers of parity n that nobody reads afterwards
+        for (int c = 0; c < nchunks; ++c) {
+          __syncthreads();                 // B(c)
+          second_half(c);
+          first_half(c + 1);
+        }
+        __syncthreads();                   // B(n): the last U is in LDS
+      }
+      if (ST) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ST[(static_cast<int64_t>(unit) * D + 64 * hf + 16 * tt + 4 * lg + i) * D + col] = S[tt][i];
+      }
+    };
+    if (w == 0)
+      rec_role(std::integral_constant<int, 0>{});
+    else
+      rec_role(std::integral_constant<int, 1>{});
+    return;
   }
 
-  // lane-constant block offsets (bytes). The T block of k-step s is (m, s);
-  // the P block is the turned tile's (3 - m, 1 - s) read in reversed lane
-  // order. Tiles 0 and 1 need only k-step 0 of either: their second block
-  // reads as zeros from past the resource, so no branch guards any load.
-  const uint32_t lo16 = static_cast<uint32_t>(lane * 16);
-  uint32_t xo[2];
+  // ================================================================ output waves
+  if (nchunks == 0) return;
+  const int ow = w - 2;
+  const int mt[2] = {ow, 3 - ow};        // token tiles: one with one P k-step, one with two
+  // P block (tile m, k-step s) is the turned tile's block (3 - m, 1 - s) read
+  // in reversed lane order; slot j holds token 32 s + perm32(lg, 7 - j), kept
+  // where it is <= the row 16 m + lr
+  uint4 pm[3];                           // masks: (tile 0, s 0), (tile 1, s 0), (tile 1, s 1)
+  uint32_t po[3];                        // P block offsets (hi plane; lo is 8 blocks further)
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-    xo[s] = rec ? static_cast<uint32_t>((2 * m + s) * BLK_BYTES) + lo16
-                : static_cast<uint32_t>((2 * (3 - m) + 1 - s) * BLK_BYTES + (63 - lane) * 16);
-  const bool two_k = m >= 2;               // tiles 0, 1 need only k-step 0 of T and P
-  const uint32_t fo = static_cast<uint32_t>(4 * m * BLK_BYTES) + lo16;
-  const uint32_t kto = static_cast<uint32_t>(2 * w * BLK_BYTES) + lo16;
-  // V staging: lane l of instruction i loads token 32i + l / 2, columns 8 (l % 2) .. +7
+  for (int b = 0; b < 3; ++b) {
+    const int m = b == 0 ? mt[0] : mt[1], s = b == 2 ? 1 : 0;
+    const int row = 16 * m + lr;
+    uint32_t mm[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bool lo = 32 * s + perm32(lg, 7 - 2 * d) <= row;
+      const bool hi = 32 * s + perm32(lg, 6 - 2 * d) <= row;
+      mm[d] = (lo ? 0x0000ffffu : 0u) | (hi ? 0xffff0000u : 0u);
+    }
+    pm[b] = make_uint4(mm[0], mm[1], mm[2], mm[3]);
+    po[b] = static_cast<uint32_t>((2 * (3 - m) + 1 - s) * BLK_BYTES + (63 - lane) * 16);
+  }
+  // V staging: lane l of instruction i loads token 32 i + l / 2, columns 8 (l % 2) .. +7
   const uint32_t vo0 = static_cast<uint32_t>(((lane >> 1) * vs + slice * 16 + 8 * (lane & 1)) * 2);
-
-  // group 0: T/P blocks (and the scalar block on the scalar wave); group 1:
-  // K^T blocks (and V on the value wave); group 2: K/Q blocks -- the larger
-  // groups go to the phases with less LDS traffic
-  auto load_chunk = [&](int cc, Prefetch& pf, int part) {
-    const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;    // (chunk, value head)
-    const size_t kt = static_cast<size_t>(cbase + cc) * nk + hk;   // (chunk, key head)
-    if (part == 0) {
-      const rsrc_t rx = make_rsrc(xf + ct * TILE_ELEMS, TILE_ELEMS * 2);
-      pf.x[0] = bload16(rx, xo[0]);
-      pf.x[2] = bload16(rx, xo[0] + 8 * BLK_BYTES);
-      if (two_k) {
-        pf.x[1] = bload16(rx, xo[1]);
-        pf.x[3] = bload16(rx, xo[1] + 8 * BLK_BYTES);
-      }
-      if (w == kScalarWave) {
-        // exp(G_C) through a vector load: a uniform (scalar) load would share
-        // lgkmcnt with LDS traffic and stall the next LDS wait for a full
-        // memory round trip
-        pf.x[1] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
-        pf.x[3].x = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
-      }
-    } else if (part == 1) {
-      const rsrc_t rk = make_rsrc(ktf + kt * TILE_ELEMS, TILE_ELEMS * 2);
-      pf.kt[0] = bload16(rk, kto);
-      pf.kt[1] = bload16(rk, kto + BLK_BYTES);
-      if (w == kValueWave) {
-        // V rows past the sequence end read as zeros (resource sized to the valid rows)
-        const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
-        const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-        const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
-                                    static_cast<uint32_t>(((L - 1) * vs + D) * 2));
-        pf.x[1] = bload16(rv, vo0);
-        pf.x[3] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
-      }
-    } else {
-      const rsrc_t rf = make_rsrc((rec ? kf : qf) + kt * TILE_ELEMS, TILE_ELEMS * 2);
+  // T staging: block (m, s) of the strictly lower part, slot j = token
+  // 32 s + perm32(lg, j) against row 16 m + lr. Blocks (2, 0) and (3, 0) lie
+  // wholly below the diagonal; in the others one half is zero or full and the
+  // other follows this pattern (slot j < 4 kept where 4 lg + j < lr).
+  uint2 dm;
+  {
+    uint32_t mm[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) pf.f[s] = bload16(rf, fo + s * BLK_BYTES);
+    for (int d = 0; d < 2; ++d)
+      mm[d] = (4 * lg + 2 * d < lr ? 0x0000ffffu : 0u) | (4 * lg + 2 * d + 1 < lr ? 0xffff0000u : 0u);
+    dm = make_uint2(mm[0], mm[1]);
+  }
+
+  // One register set: each group is reloaded for the next chunk right after
+  // its last use (Q after Y, P after O, staging loads after staging).
+  uint4 qb[2][4];                        // Q (tile mt[u], dk k-step)
+  uint4 ph[3], pl[3];                    // P blocks as above, hi | lo
+  uint4 sg[12];                          // staging: T blocks (T wave), or scalars, V rows
+  uint32_t eg = 0;                       // staging: exp(G_C)
+  auto load_q = [&](int cc) {
+    const size_t kt = static_cast<size_t>(cbase + cc) * nk + hk;
+    const rsrc_t r = make_rsrc(qf + kt * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qb[u][s] = bload16(r, static_cast<uint32_t>((4 * mt[u] + s) * BLK_BYTES) + lo16);
+  };
+  auto load_p = [&](int cc) {
+    const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;
+    const rsrc_t r = make_rsrc(xf + ct * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      ph[b] = bload16(r, po[b]);
+      pl[b] = bload16(r, po[b] + 8 * BLK_BYTES);
     }
   };
-  // stage a chunk's scalars, exp(G_C) and V slice in LDS buffer `buf`
-  auto commit = [&](const Prefetch& pf, int buf) {
-    if (w == kScalarWave) {
-      *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = pf.x[1];
-      EGS[buf][lane] = bits_f(pf.x[3].x);
+  // Y^T = S^T Q^T of chunk c for both tiles, and a of chunk c
+  auto out_y = [&](int c, f32x4 (&Y)[2], float (&a)[2]) {
+    const int buf = c & 1;
+    uint4 sh[4], sl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sh[s] = SBX[buf][0][s][lane];
+      sl[s] = SBX[buf][1][s][lane];
     }
-    if (w == kValueWave) {
-      // lane holds V[t][8 (lane % 2) + e], e = 0..7, for t = 32i + lane / 2;
-      // slot of (t, c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4& vi = pf.x[2 * i + 1];
-        const uint32_t d[4] = {vi.x, vi.y, vi.z, vi.w};
-        const int t = 32 * i + (lane >> 1);
-        uint16_t* base = &VS[buf][((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3)];
+    for (int u = 0; u < 2; ++u) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          base[(8 * (lane & 1) + e) * 4] = static_cast<uint16_t>((e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xffffu));
+      for (int s = 0; s < 4; ++s) {
+        y = mfma_bf16(as_bf16x8(sl[s]), as_bf16x8(qb[u][s]), y);
+        y = mfma_bf16(as_bf16x8(sh[s]), as_bf16x8(qb[u][s]), y);
       }
+      Y[u] = y;
+      a[u] = SCS[buf][16 * mt[u] + lr];
     }
   };
-  auto publish_S = [&]() { put_tile(SX, SXP, w, lane, S); };
-
-  // The output side runs one phase behind the recurrence side: Y of chunk c
-  // is formed in phase 2 of chunk c and kept in registers with chunk c's
-  // masked P blocks, and the O tile of chunk c in phase 1 of chunk c+1, from
-  // those, U of chunk c (still in LDS) and its scalars. The recurrence chain
-  // X -> R -> U -> S then never waits on output work, and the S reads split
-  // over two phases.
-  f32x4 Yprev = {0.f, 0.f, 0.f, 0.f};
-  uint4 Pprev[4] = {};
-  // O^T tile: lane (lr, lg) holds O[token 16m + lr][columns 16 slice + 4lg + i]
-  const uint32_t oo0 = static_cast<uint32_t>((row * nv * D + slice * 16 + 4 * lg) * sizeof(TO));
-  // O^T = a Y^T + U^T P^T for chunk co (P slots hold tokens in reversed order:
-  // reverse U too), stored at once: the chunk's loads are already issued, and
-  // a store issued before a load would make every wait on that load also wait
-  // for the store (one in-order completion counter)
-  auto out_tile = [&](int co, const uint4 (&xp)[4]) {
-    f32x4 O0, O1 = {0.f, 0.f, 0.f, 0.f};
-    const float ar = SCS[co & 1][row];     // a of this lane's token row
-#pragma unroll
-    for (int i = 0; i < 4; ++i) O0[i] = ar * Yprev[i];
+  // O^T = a Y^T + U^T P^T of chunk c (U_c in LDS), stored
+  const uint32_t oo[2] = {static_cast<uint32_t>(((16 * mt[0] + lr) * nv * D + slice * 16 + 4 * lg) * sizeof(TO)),
+                          static_cast<uint32_t>(((16 * mt[1] + lr) * nv * D + slice * 16 + 4 * lg) * sizeof(TO))};
+  auto out_o = [&](int c, const f32x4 (&Y)[2], const float (&a)[2]) {
+    const int buf = c & 1;
+    // U^T as A operand (token k-steps 0, 1), slots reversed to match the turned P blocks
+    uint4 uh[2], ul[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (s == 1 && !two_k) break;
-      const bf16x8 ah = as_bf16x8(xp[s]), al = as_bf16x8(xp[2 + s]);
-      const bf16x8 bh = as_bf16x8(rev8(lds16(UX + s * BLK_BYTES + lane * 16)));
-      const bf16x8 bl = as_bf16x8(rev8(lds16(UX + TXP + s * BLK_BYTES + lane * 16)));
-      f32x4& Oa = s == 0 ? O0 : O1;
-      Oa = mfma_bf16(bh, al, Oa);
-      Oa = mfma_bf16(bl, ah, Oa);
-      Oa = mfma_bf16(bh, ah, Oa);
+      const f32x4 u0 = UXF[buf][2 * s][lane], u1 = UXF[buf][2 * s + 1][lane];
+      uint2 h0, l0, h1, l1;
+      split4_packed(make_float4(u0[0], u0[1], u0[2], u0[3]), h0, l0);
+      split4_packed(make_float4(u1[0], u1[1], u1[2], u1[3]), h1, l1);
+      uh[s] = rev8(make_uint4(h0.x, h0.y, h1.x, h1.y));
+      ul[s] = rev8(make_uint4(l0.x, l0.y, l1.x, l1.y));
     }
-    float Ov[4];
+    f32x4 O[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ov[i] = O0[i] + O1[i];
-    const int64_t t0 = s_begin + static_cast<int64_t>(co) * CH;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[u][i] = a[u] * Y[u][i];
+    auto up = [&](f32x4& acc, int b, int s) {
+      const bf16x8 bh = as_bf16x8(and4(ph[b], pm[b])), bl = as_bf16x8(and4(pl[b], pm[b]));
+      acc = mfma_bf16(as_bf16x8(uh[s]), bl, acc);
+      acc = mfma_bf16(as_bf16x8(ul[s]), bh, acc);
+      acc = mfma_bf16(as_bf16x8(uh[s]), bh, acc);
+    };
+    up(O[0], 0, 0);
+    up(O[1], 1, 0);
+    up(O[1], 2, 1);
+    const int64_t t0 = s_begin + static_cast<int64_t>(c) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
     const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
                                 static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
-    if constexpr (sizeof(TO) == 4) {
-      bstore16(ro, oo0, make_uint4(__float_as_uint(Ov[0]), __float_as_uint(Ov[1]), __float_as_uint(Ov[2]),
-                                   __float_as_uint(Ov[3])));
-    } else {
-      bstore8(ro, oo0, make_uint2(f32_to_bf16(Ov[0]) | (static_cast<uint32_t>(f32_to_bf16(Ov[1])) << 16),
-                                  f32_to_bf16(Ov[2]) | (static_cast<uint32_t>(f32_to_bf16(Ov[3])) << 16)));
-    }
-  };
-  auto masked = [&](const Prefetch& pf, uint4 (&xa)[4]) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      xa[s] = and4(pf.x[s], msk[s]);
-      xa[2 + s] = and4(pf.x[2 + s], msk[s]);
+    for (int u = 0; u < 2; ++u) {
+      if constexpr (sizeof(TO) == 4) {
+        bstore16(ro, oo[u], make_uint4(__float_as_uint(O[u][0]), __float_as_uint(O[u][1]),
+                                       __float_as_uint(O[u][2]), __float_as_uint(O[u][3])));
+      } else {
+        bstore8(ro, oo[u],
+                make_uint2(f32_to_bf16(O[u][0]) | (static_cast<uint32_t>(f32_to_bf16(O[u][1])) << 16),
+                           f32_to_bf16(O[u][2]) | (static_cast<uint32_t>(f32_to_bf16(O[u][3])) << 16)));
+      }
     }
   };
 
-  // One chunk with `cur`; the loads of chunk cc+2 go into `nxt2` (the set in
-  // between is in flight). Three register sets rotate, so nothing is copied
-  // between chunks and every load has about two chunks of compute to arrive.
-  auto step = [&](int cc, const Prefetch& cur, const Prefetch& nxt, Prefetch& nxt2) {
-    const int ln = min(cc + 2, nchunks - 1);   // past the end the last chunk is re-read
-    const int buf = cc & 1;
-    // masked T or P blocks of this chunk. The k-step 1 blocks of tiles 0 and 1
-    // are not loaded (or carry staging loads) but are consumed here on every
-    // path (their mask is zero).
-    uint4 xa[4];
-    masked(cur, xa);
-    load_chunk(ln, nxt2, 0);
-
-    // phase 1: X = K S and R = beta v - b X (recurrence side); O of the
-    // previous chunk (output side)
-    f32x4 Ra = {0.f, 0.f, 0.f, 0.f};
-    const int srow = 16 * m + 4 * lg;      // first of this lane's 4 accumulator rows
-    if (rec) {
-      f32x4 XH = {0.f, 0.f, 0.f, 0.f}, XL = {0.f, 0.f, 0.f, 0.f};
+  // wave 2 stages the masked T blocks, wave 3 the scalars, exp(G_C) and beta v
+  auto run = [&](auto tstager) {
+    constexpr bool TW = decltype(tstager)::value;
+    auto load_stage = [&](int cc) {
+      const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;
+      if constexpr (TW) {
+        const rsrc_t r = make_rsrc(xf + ct * TILE_ELEMS, TILE_ELEMS * 2);
+        constexpr int blk[6] = {0, 2, 4, 5, 6, 7};   // 2 m + s
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = as_bf16x8(cur.f[s]);
-        XL = mfma_bf16(a, as_bf16x8(lds16(SX + SXP + s * BLK_BYTES + lane * 16)), XL);
-        XH = mfma_bf16(a, as_bf16x8(lds16(SX + s * BLK_BYTES + lane * 16)), XH);
+        for (int b = 0; b < 6; ++b) {
+          sg[b] = bload16(r, blk[b] * BLK_BYTES + lo16);
+          sg[6 + b] = bload16(r, (8 + blk[b]) * BLK_BYTES + lo16);
+        }
+      } else {
+        sg[0] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
+        eg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
+        // V rows past the sequence end read as zeros (resource sized to the valid rows)
+        const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+        const rsrc_t rv =
+            make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D, static_cast<uint32_t>(((L - 1) * vs + D) * 2));
+        sg[1] = bload16(rv, vo0);
+        sg[2] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
       }
-      const float4 bb = *reinterpret_cast<const float4*>(&SCS[buf][CH + srow]);
-      const float4 be = *reinterpret_cast<const float4*>(&SCS[buf][3 * CH + srow]);
-      const uint2 vv = *reinterpret_cast<const uint2*>(&VS[buf][(m * 64 + lane) * 4]);
-      Ra[0] = be.x * bf16_to_f32(static_cast<uint16_t>(vv.x)) - bb.x * (XH[0] + XL[0]);
-      Ra[1] = be.y * bf16_to_f32(static_cast<uint16_t>(vv.x >> 16)) - bb.y * (XH[1] + XL[1]);
-      Ra[2] = be.z * bf16_to_f32(static_cast<uint16_t>(vv.y)) - bb.z * (XH[2] + XL[2]);
-      Ra[3] = be.w * bf16_to_f32(static_cast<uint16_t>(vv.y >> 16)) - bb.w * (XH[3] + XL[3]);
-      put_tile(RX, TXP, m, lane, Ra);
-    } else if (cc > 0) {
-      out_tile(cc - 1, Pprev);
+    };
+    // stage chunk cs (its loads are in sg) in LDS buffer cs & 1
+    auto stage = [&](int cs) {
+      const int buf = cs & 1;
+      if constexpr (TW) {
+        auto lowmask = [&](const uint4& x) { return make_uint4(x.x & dm.x, x.y & dm.y, 0u, 0u); };
+        auto highmask = [&](const uint4& x) { return make_uint4(x.x, x.y, x.z & dm.x, x.w & dm.y); };
+#pragma unroll
+        for (int pl2 = 0; pl2 < 2; ++pl2) {
+          const uint4* t = sg + 6 * pl2;
+          uint4* d = &TSX[buf][6 * pl2][0];
+          d[0 * 64 + lane] = lowmask(t[0]);    // (0, 0)
+          d[1 * 64 + lane] = highmask(t[1]);   // (1, 0)
+          d[2 * 64 + lane] = t[2];             // (2, 0)
+          d[3 * 64 + lane] = lowmask(t[3]);    // (2, 1)
+          d[4 * 64 + lane] = t[4];             // (3, 0)
+          d[5 * 64 + lane] = highmask(t[5]);   // (3, 1)
+        }
+      } else {
+        *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = sg[0];
+        if (lane == 0) EGS[buf] = bits_f(eg);
+        float* bvs = reinterpret_cast<float*>(&BVS[buf][0][0]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int t = 32 * i + (lane >> 1);
+          const float be = SCS[buf][3 * CH + t];   // written above by this wave
+          const uint32_t d[4] = {sg[1 + i].x, sg[1 + i].y, sg[1 + i].z, sg[1 + i].w};
+          // slot of (t, column c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
+          float* base = bvs + ((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t bits = (e & 1) ? (d[e >> 1] & 0xffff0000u) : (d[e >> 1] << 16);
+            base[(8 * (lane & 1) + e) * 4] = be * __uint_as_float(bits);
+          }
+        }
+      }
+    };
+    auto last = [&](int c) { return min(c, nchunks - 1); };
+    load_q(0);
+    load_p(0);
+    load_stage(0);
+    stage(0);
+    load_stage(last(1));
+    __syncthreads();                     // B(0)
+    f32x4 Y[2];
+    float a[2];
+    out_y(0, Y, a);
+    load_q(last(1));
+    stage(1);
+    load_stage(last(2));
+    // the pass with c = nchunks (after B(n)) only stores the last chunk's
+    // output; its other work re-reads chunk n-1 data or stale buffers that
+    // nobody reads afterwards
+    for (int c = 1; c <= nchunks; ++c) {
+      __syncthreads();                   // B(c)
+      f32x4 Yn[2];
+      float an[2];
+      out_y(last(c), Yn, an);
+      load_q(last(c + 1));
+      out_o(c - 1, Y, a);
+      load_p(last(c));
+      stage(c + 1);
+      load_stage(last(c + 2));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        Y[u] = Yn[u];
+        a[u] = an[u];
+      }
     }
-    __syncthreads();
-    load_chunk(ln, nxt2, 1);
-
-    // phase 2: U = R + T_strict R -> U and c U tiles (recurrence side);
-    // Y^T = S^T Q^T of this chunk, hi and lo parts of S in two accumulators
-    // (output side)
-    if (rec) {
-      f32x4 U0 = Ra, U1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s == 1 && !two_k) break;
-        const bf16x8 ah = as_bf16x8(xa[s]), al = as_bf16x8(xa[2 + s]);
-        const bf16x8 bh = as_bf16x8(lds16(RX + s * BLK_BYTES + lane * 16));
-        const bf16x8 bl = as_bf16x8(lds16(RX + TXP + s * BLK_BYTES + lane * 16));
-        f32x4& Ua = s == 0 ? U0 : U1;
-        Ua = mfma_bf16(al, bh, Ua);
-        Ua = mfma_bf16(ah, bl, Ua);
-        Ua = mfma_bf16(ah, bh, Ua);
-      }
-      f32x4 Ua, cU;
-      const float4 cb = *reinterpret_cast<const float4*>(&SCS[buf][2 * CH + srow]);
-      const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Ua[i] = U0[i] + U1[i];
-        cU[i] = cbv[i] * Ua[i];
-      }
-      put_tile(UX, TXP, m, lane, Ua);
-      put_tile(CX, TXP, m, lane, cU);
-    } else {
-      f32x4 YH = {0.f, 0.f, 0.f, 0.f}, YL = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = as_bf16x8(cur.f[s]);
-        YL = mfma_bf16(as_bf16x8(lds16(SX + SXP + s * BLK_BYTES + lane * 16)), a, YL);
-        YH = mfma_bf16(as_bf16x8(lds16(SX + s * BLK_BYTES + lane * 16)), a, YH);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Yprev[i] = YH[i] + YL[i];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Pprev[s] = xa[s];
-    }
-    __syncthreads();
-    load_chunk(ln, nxt2, 2);
-
-    // phase 3: S_w = e^{G_C} S_w + K[:, rows of w]^T (c U), the two token
-    // k-steps in two accumulators
-    {
-      const float eGC = EGS[buf][0];
-      f32x4 S1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[i] *= eGC;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 a = as_bf16x8(cur.kt[s]);
-        const bf16x8 ch = as_bf16x8(lds16(CX + s * BLK_BYTES + lane * 16));
-        const bf16x8 cl = as_bf16x8(lds16(CX + TXP + s * BLK_BYTES + lane * 16));
-        f32x4& Sa = s == 0 ? S : S1;
-        Sa = mfma_bf16(a, cl, Sa);
-        Sa = mfma_bf16(a, ch, Sa);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[i] += S1[i];
-    }
-    // publish S for the next chunk (every wave has read S before the barriers above)
-    publish_S();
-    commit(nxt, buf ^ 1);
-    __syncthreads();
   };
-
-  Prefetch pa{}, pb{}, pc{};
-  if (nchunks > 0) {
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      load_chunk(0, pa, p);
-      load_chunk(min(1, nchunks - 1), pb, p);
-    }
-    commit(pa, 0);
-  }
-  publish_S();
-  __syncthreads();
-  // Whole rotations in the loop, the last one or two chunks after it: a loop
-  // body without early exits lets the compiler count exactly which loads are
-  // still in flight at every wait.
-  int cc = 0;
-  for (; cc + 3 <= nchunks; cc += 3) {
-    step(cc, pa, pb, pc);
-    step(cc + 1, pb, pc, pa);
-    step(cc + 2, pc, pa, pb);
-  }
-  if (cc < nchunks) step(cc, pa, pb, pc);
-  if (cc + 1 < nchunks) step(cc + 1, pb, pc, pa);
-  if (!rec && nchunks > 0) out_tile(nchunks - 1, Pprev);   // the last chunk's output
-
-  if (ST) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ST[(static_cast<int64_t>(unit) * D + 16 * w + 4 * lg + i) * D + col] = S[i];
-  }
+  if (w == 2)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
-
 // ------------------------------------------------------------------ state: generic (fp32 inputs), one wave per 16 columns
 constexpr int KP = 132;    // LDS pitch (floats) of 64 x 128 K/Q tiles
 constexpr int RP = 18;     // LDS pitch of the 64 x 16 R / U tiles
@@ -1184,7 +1237,6 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   float* egc = reinterpret_cast<float*>(base + lay.off_egc);
   uint16_t* kf = BF ? reinterpret_cast<uint16_t*>(base + lay.off_kf) : nullptr;
   uint16_t* qf = BF ? reinterpret_cast<uint16_t*>(base + lay.off_qf) : nullptr;
-  uint16_t* ktf = BF ? reinterpret_cast<uint16_t*>(base + lay.off_ktf) : nullptr;
 
   const int64_t nch = T / CH + n_seqs;
   hipError_t e = hipSuccess;
@@ -1201,7 +1253,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     if (e != hipSuccess) return e;
     kern<<<dim3(static_cast<unsigned>(nv), static_cast<unsigned>(nch)), 64 * PREP_WAVES, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, g, beta, cu, n_seqs, T, nk, nv, scale, l2,
-        chunk_off, tp, sc, egc, kf, qf, ktf);
+        chunk_off, tp, sc, egc, kf, qf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1211,11 +1263,11 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     const float* scp = reinterpret_cast<const float*>(sc);
     const uint16_t* vb = static_cast<const uint16_t*>(v);
     if (o_bf16)
-      chunk_state_bf16_kernel<uint16_t><<<grid, 512, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
-                                                             kf, qf, ktf, S0, ST, static_cast<uint16_t*>(o));
+      chunk_state_bf16_kernel<uint16_t><<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
+                                                         kf, qf, S0, ST, static_cast<uint16_t*>(o));
     else
-      chunk_state_bf16_kernel<float><<<grid, 512, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
-                                                          kf, qf, ktf, S0, ST, static_cast<float*>(o));
+      chunk_state_bf16_kernel<float><<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
+                                                      kf, qf, S0, ST, static_cast<float*>(o));
     return hipGetLastError();
   } else {
     const size_t lds = generic_lds_bytes();
