@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402  (top level imports no GPU library)
 
-BENCH_ARGS = ["--steps", "20", "--warmup", "3", "--skip-cpu-baseline", "--calibrate-copy"]
+BENCH_ARGS = ["--steps", "200", "--warmup", "100", "--skip-cpu-baseline", "--calibrate-copy"]
 COPY_BYTES = 1 << 30
 KERNELS = {  # what one call of each measured entry point launches (bf16 in, fp32 out); the
     # chunk table kernel runs only with cu_seqlens, so it is counted when present
