@@ -71,13 +71,14 @@ __global__ void __launch_bounds__(256) recurrent_kernel(const TIn* __restrict__ 
   // counted in order, so the norms below then wait only for these
   if (t0 < t1) load_token(t0);
 
-  // The state streams through once each way: non-temporal accesses keep it
-  // from displacing anything in the caches.
+  // The state streams through once each way. It is read with ordinary loads
+  // and written back non-temporally (each state is touched once per call);
+  // of the four load/store hint combinations this one streams fastest.
   float* Sp = state + static_cast<int64_t>(unit) * D * D;
   float S[RPT][4];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const f32x4 s4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (rg + RGN * i) * D + col));
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(Sp + (rg + RGN * i) * D + col);
     S[i][0] = s4[0]; S[i][1] = s4[1]; S[i][2] = s4[2]; S[i][3] = s4[3];
   }
 
@@ -166,7 +167,7 @@ template <typename TIn>
 hipError_t rec_dispatch(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
                         const float* g, const float* beta, const int32_t* cu, int n_seqs, int64_t T, int nk,
                         int nv, float scale, int l2, float* state, void* o, int o_bf16, hipStream_t s) {
-  constexpr int NCOL = 64;   // two workgroups per state: twice the workgroups, half the registers
+  constexpr int NCOL = 128;   // one workgroup per state: each wave load covers 1 KB of contiguous rows
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(nv) * (D / NCOL));
   if (o_bf16)
     recurrent_kernel<TIn, uint16_t, NCOL><<<grid, 256, 0, s>>>(
