@@ -208,6 +208,19 @@ __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, uint2 v) {
   d.x = v.x; d.y = v.y;
   __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
 }
+// Non-temporal stores (cache policy bit "nt") for write-once output streams.
+__device__ __forceinline__ void bstore16_nt(rsrc_t r, uint32_t off, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 d;
+  d.x = v.x; d.y = v.y; d.z = v.z; d.w = v.w;
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 2);
+}
+__device__ __forceinline__ void bstore8_nt(rsrc_t r, uint32_t off, uint2 v) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 d;
+  d.x = v.x; d.y = v.y;
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 2);
+}
 
 // ---------------------------------------------------------------- XCD-aware block order
 // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).

@@ -890,7 +890,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
       a[u] = SCS[buf][16 * mt[u] + lr];
     }
   };
-  // O^T = a Y^T + U^T P^T of chunk c (U_c in LDS), stored
+  // O^T = a Y^T + U^T P^T of chunk c (U_c in LDS), stored non-temporally
+  // (the output is written once and not read back here)
   const uint32_t oo[2] = {static_cast<uint32_t>(((16 * mt[0] + lr) * nv * D + slice * 16 + 4 * lg) * sizeof(TO)),
                           static_cast<uint32_t>(((16 * mt[1] + lr) * nv * D + slice * 16 + 4 * lg) * sizeof(TO))};
   auto out_o = [&](int c, const f32x4 (&Y)[2], const float (&a)[2]) {
@@ -927,10 +928,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if constexpr (sizeof(TO) == 4) {
-        bstore16(ro, oo[u], make_uint4(__float_as_uint(O[u][0]), __float_as_uint(O[u][1]),
+        bstore16_nt(ro, oo[u], make_uint4(__float_as_uint(O[u][0]), __float_as_uint(O[u][1]),
                                        __float_as_uint(O[u][2]), __float_as_uint(O[u][3])));
       } else {
-        bstore8(ro, oo[u],
+        bstore8_nt(ro, oo[u],
                 make_uint2(f32_to_bf16(O[u][0]) | (static_cast<uint32_t>(f32_to_bf16(O[u][1])) << 16),
                            f32_to_bf16(O[u][2]) | (static_cast<uint32_t>(f32_to_bf16(O[u][3])) << 16)));
       }
