@@ -690,6 +690,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
         // the rest of chunk c: X, R, U, c U, and the update of this half of S
         auto second_half = [&](int c) {
           const int buf = c & 1;
+          // K^T blocks of this wave's rows of S (dk tile 4 hf + tt, token
+          // k-step s), read transposed from this chunk's K blocks: addressing
+          // lane (lr, lg) points at token 32 s + 16 h + 4 lg + lr / 4, dk
+          // 16 tt + 4 (lr % 4) .. +3, which sits in block (2 s + h, tt / 2),
+          // block lane 16 (lr % 4) + 4 lg + lr / 4, bytes 8 (tt % 2) ..
+          // Issued first: their latency hides under R, U and c U.
+          uint4 kta[4][2];
+          {
+            const int kl = kl_lane(16 * (lr & 3) + 4 * lg + (lr >> 2));
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+              for (int s = 0; s < 2; ++s) {
+                const uint2 x0 = lds_tr16(&KLX[hf][2 * (2 * s) + tt / 2][kl + 8 * (tt & 1)]);
+                const uint2 x1 = lds_tr16(&KLX[hf][2 * (2 * s + 1) + tt / 2][kl + 8 * (tt & 1)]);
+                kta[tt][s] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+              }
+          }
           const int ln = min(c + 1, nchunks - 1);
           f32x4 R[4];
 #pragma unroll
@@ -754,24 +772,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
             cl[s] = make_uint4(l0.x, l0.y, l1.x, l1.y);
           }
           const float eg = EGS[buf];
-          // K^T blocks of this wave's rows of S (dk tile 4 hf + tt, token
-          // k-step s), read transposed from this chunk's K blocks: addressing
-          // lane (lr, lg) points at token 32 s + 16 h + 4 lg + lr / 4, dk
-          // 16 tt + 4 (lr % 4) .. +3, which sits in block (2 s + h, tt / 2),
-          // block lane 16 (lr % 4) + 4 lg + lr / 4, bytes 8 (tt % 2) ..
-          // (the reads stay next to their MFMAs: hoisted, their results
-          // would be live across the whole chunk)
-          const int kl = kl_lane(16 * (lr & 3) + 4 * lg + (lr >> 2));
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            uint4 ktb[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const uint2 x0 = lds_tr16(&KLX[hf][2 * (2 * s) + tt / 2][kl + 8 * (tt & 1)]);
-              const uint2 x1 = lds_tr16(&KLX[hf][2 * (2 * s + 1) + tt / 2][kl + 8 * (tt & 1)]);
-              ktb[s] = make_uint4(x0.x, x0.y, x1.x, x1.y);
-            }
+            const uint4* ktb = kta[tt];
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[tt][i] *= eg;
 #pragma unroll
