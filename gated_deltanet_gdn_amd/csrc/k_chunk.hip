@@ -573,14 +573,18 @@ __device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(
 // The output waves also stage chunk inputs in LDS for the recurrence waves,
 // one chunk ahead: wave 2 the masked T blocks (both recurrence waves use all
 // of them), wave 3 the per-token scalars, exp(G_C) and beta * v in
-// accumulator layout.
+// accumulator layout. The K^T operand of the state update is not loaded:
+// each recurrence wave writes the K blocks it holds for K S to LDS and reads
+// them back transposed.
 //
 // Barrier B(c) separates: the recurrence waves' S_c (as bf16 hi | lo) and
 // partial X_c, and the staged inputs of chunk c, all written before it; after
 // it the recurrence waves finish chunk c and start c+1, and the output waves
 // form Y of chunk c and O of chunk c-1 (U_{c-1} was written before B(c)).
-// Every LDS buffer is double-buffered by chunk parity: a buffer written
-// between B(c-1) and B(c) is read only between B(c) and B(c+1).
+// Every LDS buffer shared between waves is double-buffered by chunk parity:
+// a buffer written between B(c-1) and B(c) is read only between B(c) and
+// B(c+1). The K blocks are private to their wave (written and read back by
+// it in program order).
 
 constexpr int KL_BLK = 64 * 16 + 4 * 64;   // one padded K block in LDS
 
@@ -597,7 +601,7 @@ __device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
 __device__ __forceinline__ int kl_lane(int l) { return 16 * l + 64 * (l >> 4); }
 
 template <typename TO>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) chunk_state_bf16_kernel(
+__global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
     int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
     const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
@@ -708,7 +712,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
                 kta[tt][s] = make_uint4(x0.x, x0.y, x1.x, x1.y);
               }
           }
-          const int ln = min(c + 1, nchunks - 1);
           f32x4 R[4];
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
