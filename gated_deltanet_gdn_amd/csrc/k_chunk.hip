@@ -266,6 +266,13 @@ __device__ __forceinline__ void mm16_regb(f32x4& acc, const float* A, int lda, c
   }
 }
 
+// e^x for a decay exponent x <= 0 held in fp64: x log2(e) is formed in fp64
+// and rounded once to fp32, then the hardware 2^x (about 1 ulp). The result's
+// relative error stays near 1e-7 for every |x| at which it is not negligible.
+__device__ __forceinline__ float exp_nonpos(double x) {
+  return __builtin_amdgcn_exp2f(static_cast<float>(x * 1.4426950408889634));
+}
+
 // ------------------------------------------------------------------ prep
 // Four waves per (chunk, value head). The ten lower 16x16 tile pairs (mi, mj)
 // of the Grams, A and P are dealt round-robin (pair p goes to wave p % 4);
@@ -345,26 +352,16 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   }
   __syncthreads();
 
-  // 2. |q_i|^2: four threads per row, 32 elements each
-  {
-    const int row = tid >> 2, part = tid & 3;
-    float sqq = 0.f;
-#pragma unroll 8
-    for (int e = 0; e < D / 4; ++e) {
-      const float x = tof(Qs[row * EP + part * (D / 4) + e]);
-      sqq = fmaf(x, x, sqq);
-    }
-    sqq += __shfl_xor(sqq, 1, 64);
-    sqq += __shfl_xor(sqq, 2, 64);
-    if (part == 0) rq_s[row] = row < L ? (l2 ? 1.0f / sqrtf(sqq + kEps) : 1.0f) : 0.0f;
-  }
-  // 3. Grams on this wave's lower 16x16 tile pairs p = wv + 4 u, kept in registers
+  // 2. Grams on this wave's lower 16x16 tile pairs p = wv + 4 u, kept in
+  //    registers; on the diagonal pairs also Q Q^T, whose diagonal is |q_i|^2
+  //    (|k_i|^2 is the diagonal of K K^T)
   constexpr int NP = 3;
-  f32x4 gkk[NP], gqk[NP];
+  f32x4 gkk[NP], gqk[NP], gqq[NP];
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
     gkk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     gqk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gqq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int p = wv + 4 * u;
     if (p >= 10) break;
     const int mi = tile_mi(p), mj = tile_mj(p);
@@ -377,6 +374,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
         const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Ks + (16 * mj + lr) * EP + kk);
         gkk[u] = mfma_bf16(ak, bk, gkk[u]);
         gqk[u] = mfma_bf16(aq, bk, gqk[u]);
+        if (mi == mj) gqq[u] = mfma_bf16(aq, aq, gqq[u]);
       } else {
         float ak[KPL], aq[KPL], bk[KPL];
 #pragma unroll
@@ -388,10 +386,11 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
         }
         MG::run(gkk[u], ak, bk);
         MG::run(gqk[u], aq, bk);
+        if (mi == mj) MG::run(gqq[u], aq, aq);
       }
     }
   }
-  // 3b. bf16 inputs: K and Q operand blocks of the state recurrence, once
+  // 3. bf16 inputs: K and Q operand blocks of the state recurrence, once
   //     per key head: K by its first value head, Q by its last; wave wv
   //     writes token tile wv
   if constexpr (BF) {
@@ -400,7 +399,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     if (rho == 0) write_row_blocks<EP>(Ks, L, kf + kt, lane, wv);
     if (rho == r - 1) write_row_blocks<EP>(Qs, L, qf + kt, lane, wv);
   }
-  // 4. |k_i|^2 from the Gram diagonals (pairs 0, 2, 5, 9)
+  // 4. |k_i|^2 and |q_i|^2 from the Gram diagonals (pairs 0, 2, 5, 9)
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
     const int p = wv + 4 * u;
@@ -408,8 +407,9 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     const int mi = tile_mi(p), mj = tile_mj(p);
     if (mi == mj && lr >= 4 * lg && lr < 4 * lg + 4) {
       const int row = 16 * mi + lr;
-      const float skk = gkk[u][lr - 4 * lg];
-      rk_s[row] = row < L ? (l2 ? 1.0f / sqrtf(skk + kEps) : 1.0f) : 0.0f;
+      const float skk = gkk[u][lr - 4 * lg], sqq = gqq[u][lr - 4 * lg];
+      rk_s[row] = row < L ? (l2 ? rsqrtf(skk + kEps) : 1.0f) : 0.0f;
+      rq_s[row] = row < L ? (l2 ? rsqrtf(sqq + kEps) : 1.0f) : 0.0f;
     }
   }
   // 5. chunk-local cumulative decay in fp64 (wave 0, lane = token)
@@ -455,7 +455,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * mi + 4 * lg + ii;
-        const float dec = (j <= i) ? expf(static_cast<float>(Gr[u][ii] - Gc[u])) : 0.0f;
+        const float dec = (j <= i) ? exp_nonpos(Gr[u][ii] - Gc[u]) : 0.0f;
         Aw[i * AP + j] = (j < i) ? ar[u][ii] * rkc[u] * dec * gkk[u][ii] : 0.0f;
         gqk[u][ii] = (j <= i) ? pr[u][ii] * rkc[u] * dec * gqk[u][ii] : 0.0f;
       }
@@ -480,8 +480,11 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
         if ((m & 3) == 0) a0 -= prod; else if ((m & 3) == 1) a1 -= prod; else if ((m & 3) == 2) a2 -= prod; else a3 -= prod;
       }
       t[i] = (a0 + a1) + (a2 + a3);
-      Tw[(16 * I + i) * AP + 16 * I + jc] = t[i];
     }
+    // stored after the loop, so no store sits between the reads of A and
+    // they can all be issued ahead of the arithmetic
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Tw[(16 * I + i) * AP + 16 * I + jc] = t[i];
   }
   __syncthreads();
 #pragma unroll
