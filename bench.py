@@ -53,14 +53,16 @@ def source_hash(part):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(part):
-    """HBM bytes per call from the committed counter summary, or None if absent or stale."""
+def measured_traffic(part, key="bytes_per_call"):
+    """A per-call counter figure (HBM bytes, or executed MFMA flops with key
+    "mfma_flops_per_call") from the committed counter summary, or None if
+    absent or stale."""
     try:
         with open(TRAFFIC_SUMMARY) as fh:
             for line in fh:
                 if line.startswith("traffic_json:"):
                     rec = json.loads(line.split(":", 1)[1])[part]
-                    return rec["bytes_per_call"] if rec["source_hash"] == source_hash(part) else None
+                    return rec[key] if rec["source_hash"] == source_hash(part) else None
     except (OSError, KeyError, ValueError):
         pass
     return None
@@ -176,6 +178,12 @@ def main():
                     frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("chunk"),
                     avg_ms=round(chunk_ms, 4), algorithmic_flops=flops, algorithmic_bytes=cbytes,
                     hbm_gbps_algorithmic=round(cbytes / (chunk_ms * 1e-3) / 1e9, 1))
+    # MFMA work as the hardware counted it (hi/lo precision passes included):
+    # SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per call, from the same counter summary
+    executed = measured_traffic("chunk", "mfma_flops_per_call")
+    roofline["mfma_executed_flops"] = executed
+    roofline["mfma_counter_frac"] = (round(executed / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                                     if executed else None)
 
     # ---------------------------------------------------------------- decode step
     decode = None
