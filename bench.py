@@ -42,7 +42,8 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_t8k_decode_256seq.md")
 CSRC = os.path.join(ROOT, "gated_deltanet_gdn_amd", "csrc")
 # kernel sources each measured figure depends on
-SOURCES = {"chunk": ["k_chunk.hip", "gdn_device.hpp"], "recurrent": ["k_recurrent.hip", "gdn_device.hpp"]}
+SOURCES = {"chunk": ["k_chunk.hip", "gdn_device.hpp"], "recurrent": ["k_recurrent.hip", "gdn_device.hpp"],
+           "fused": ["k_recurrent.hip", "gdn_device.hpp"]}
 
 
 def source_hash(part):
@@ -95,6 +96,56 @@ def recurrent_bytes(n, nk, nv, dk=128, dv=128, in_bytes=2):
     return b
 
 
+def fused_decode_bytes(n_tok, n_seqs, nk, nv, dk=128, dv=128, state_len=3, K=4, io_bytes=2):
+    """Algorithmic bytes of one fused decode step: recurrent and conv states read and written once,
+    x, a, b read, o written (fp32), conv weights read."""
+    C = 2 * nk * dk + nv * dv
+    return (2 * n_seqs * nv * dk * dv * 4 + 2 * n_seqs * C * state_len * io_bytes + n_tok * C * io_bytes
+            + 2 * n_tok * nv * io_bytes + n_tok * nv * dv * 4 + C * K * 4)
+
+
+def time_fused_decode(gdn, W, name, steps, warmup, stream, dev, tokens_per_seq=None):
+    """Fused decode step (one launch): HIP events around every launch on its stream, and wall time."""
+    import torch
+    wl = W.WORKLOADS[name]
+    n = wl.n_seqs
+    if tokens_per_seq is None:
+        x = {k: v.to(dev) for k, v in W.decode_inputs(wl).items()}
+        cu, n_tok = None, n
+    else:
+        x = {k: v.to(dev) for k, v in W.decode_mtp_inputs(wl, [tokens_per_seq] * n).items()}
+        cu, n_tok = x["cu_seqlens"], n * tokens_per_seq
+    o = torch.empty((n_tok, wl.nv, wl.dv), device=dev, dtype=torch.float32)
+
+    def fstep(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gdn.gdn_decode_step_fused(x["x"], x["conv_state"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"],
+                                  x["state"], wl.nk, cu_seqlens=cu, o=o, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        fstep()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fstep(evs[i])
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    k_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nbytes = fused_decode_bytes(n_tok, n, wl.nk, wl.nv, state_len=wl.state_len)
+    gbps = nbytes / (k_ms * 1e-3) / 1e9
+    return dict(workload=f"{name}: {n} seqs x {tokens_per_seq or 1} token(s), {wl.nk}->{wl.nv} heads, "
+                         f"conv update + gating + recurrent in one launch, states in place",
+                step_ms=round(step_ms, 4), tokens_per_s=round(n_tok / (step_ms * 1e-3), 1),
+                roofline=dict(bound="hbm", kernel="decode_fused_kernel", achieved=round(gbps, 1),
+                              peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
+                              traffic=measured_traffic("fused") if tokens_per_seq is None else None,
+                              avg_ms=round(k_ms, 4), algorithmic_bytes=nbytes))
+
+
 def cpu_baseline(x, threads):
     import numpy as np
     import oracle
@@ -122,6 +173,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-mtp", action="store_true", help="skip the 1 + 3 token fused decode measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with one plain 1 GiB device copy (counter calibration runs only)")
     args = ap.parse_args()
@@ -229,6 +281,14 @@ def main():
                                     traffic=measured_traffic("recurrent"), avg_ms=round(rec_ms, 4),
                                     algorithmic_bytes=rbytes))
 
+    decode_fused = decode_mtp = None
+    if not args.skip_decode:
+        decode_fused = time_fused_decode(gdn, W, "decode_256seq", args.steps, args.warmup, stream, dev)
+        decode_fused["separate_launches_step_ms"] = decode["step_ms"]
+        if not args.skip_mtp:
+            decode_mtp = time_fused_decode(gdn, W, "decode_mtp_256x4", args.steps, args.warmup, stream, dev,
+                                           tokens_per_seq=W.WORKLOADS["decode_mtp_256x4"].extra["tokens_per_seq"])
+
     if args.calibrate_copy:   # known-size reference for the FETCH_SIZE / WRITE_SIZE counters
         src = torch.ones(1 << 28, device=dev, dtype=torch.float32)
         dst = torch.empty_like(src)
@@ -260,6 +320,8 @@ def main():
                    "global_batch": 1, "seq_len": T, "parallelism": "single GPU"},
         "roofline": roofline,
         "decode": decode,
+        "decode_fused": decode_fused,
+        "decode_mtp_fused": decode_mtp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

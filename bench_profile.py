@@ -34,12 +34,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402  (top level imports no GPU library)
 
-BENCH_ARGS = ["--steps", "200", "--warmup", "100", "--skip-cpu-baseline", "--calibrate-copy"]
+BENCH_ARGS = ["--steps", "200", "--warmup", "100", "--skip-cpu-baseline", "--skip-mtp", "--calibrate-copy"]
 COPY_BYTES = 1 << 30
 KERNELS = {  # what one call of each measured entry point launches (bf16 in, fp32 out); the
     # chunk table kernel runs only with cu_seqlens, so it is counted when present
     "chunk": ["chunk_offsets_kernel?", "chunk_prep_kernel<unsigned short>", "chunk_state_bf16_kernel<float>"],
     "recurrent": ["recurrent_kernel<unsigned short, float"],
+    "fused": ["decode_fused_kernel<unsigned short, float"],
 }
 
 
@@ -111,7 +112,7 @@ def summarize(out):
     # ---- kernel trace
     ks = kernel_stats(d1)
     by_name = {r["Name"]: r for r in ks}
-    lines = ["# Kernel trace: bench.py, prefill T=8192 (16->32 heads, bf16) and decode 256 seqs", "",
+    lines = ["# Kernel trace: bench.py, prefill T=8192 (16->32 heads, bf16) and decode 256 seqs (separate and fused)", "",
              "Command (from /tmp, TMPDIR=/tmp; written by `python bench_profile.py run`, summarised by",
              "`python bench_profile.py summarize`):", "", "    " + cmd1, "",
              "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
@@ -121,10 +122,13 @@ def summarize(out):
     chunk_names = launched(by_name, KERNELS["chunk"])
     chunk_sum = sum(float(by_name[pick(by_name, k)]["AverageNs"]) for k in chunk_names) / 1e3
     rec_avg = float(by_name[pick(by_name, KERNELS["recurrent"][0])]["AverageNs"]) / 1e3
+    fus_avg = float(by_name[pick(by_name, KERNELS["fused"][0])]["AverageNs"]) / 1e3
     lines += ["", "Agreement with the HIP-event figures bench.py printed in the same run:", "",
               f"- gdn_chunk_fwd = {' + '.join(k.split('<')[0] for k in chunk_names)}: sum of averages {chunk_sum:.1f} us; "
               f"events {b1['roofline']['avg_ms'] * 1e3:.1f} us per call",
               f"- recurrent_kernel: average {rec_avg:.1f} us; events {b1['decode']['roofline']['avg_ms'] * 1e3:.1f} us",
+              f"- decode_fused_kernel: average {fus_avg:.1f} us; events "
+              f"{b1['decode_fused']['roofline']['avg_ms'] * 1e3:.1f} us",
               "", "bench.py line of this run:", "", "    " + json.dumps(b1), ""]
     with open(os.path.join(ROOT, "profiles", "bench_prefill_t8k_decode_256seq_kernel_stats.md"), "w") as fh:
         fh.write("\n".join(lines))
@@ -161,7 +165,9 @@ def summarize(out):
              f"{rec['chunk']['mfma_flops_per_call'] / 1e9:.2f} GFLOP executed (hi/lo passes included) vs "
              f"{bench.chunk_flops_per_token_head() * 8192 * 32 / 1e9:.2f} GFLOP algorithmic",
              f"- recurrent_kernel: {rec['recurrent']['bytes_per_call'] / 1e6:.1f} MB per call "
-             f"(algorithmic {bench.recurrent_bytes(256, 16, 32) / 1e6:.1f} MB)", "",
+             f"(algorithmic {bench.recurrent_bytes(256, 16, 32) / 1e6:.1f} MB)",
+             f"- decode_fused_kernel: {rec['fused']['bytes_per_call'] / 1e6:.1f} MB per call "
+             f"(algorithmic {bench.fused_decode_bytes(256, 256, 16, 32) / 1e6:.1f} MB)", "",
              "Source hashes are of the kernel sources the counters were taken on; bench.py reports traffic",
              "only while they match.", "",
              "traffic_json: " + json.dumps(rec), ""]

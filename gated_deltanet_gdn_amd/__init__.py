@@ -19,7 +19,7 @@ __all__ = [
     "GdnError", "lib", "F32", "BF16",
     "gdn_abi_version", "gdn_status_string", "gdn_last_error",
     "gdn_gating", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_recurrent_fwd",
-    "gdn_causal_conv1d", "gdn_causal_conv1d_update", "gdn_gated_rmsnorm",
+    "gdn_causal_conv1d", "gdn_causal_conv1d_update", "gdn_gated_rmsnorm", "gdn_decode_step_fused",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -57,6 +57,8 @@ def lib():
         "gdn_causal_conv1d": (i32, [vp, i32, i64, vp, vp, vp, i32, i64, i32, i32, vp, vp, i32, i32, vp, vp]),
         "gdn_causal_conv1d_update": (i32, [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp]),
         "gdn_gated_rmsnorm": (i32, [vp, i32, vp, i32, vp, i64, i32, f32, vp, i32, vp]),
+        "gdn_decode_step_fused": (i32, [vp, i32, i64, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                        i32, i32, f32, i32, vp, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -250,3 +252,33 @@ def gdn_gated_rmsnorm(x, z, weight, eps=1e-6, y=None, y_dtype=torch.float32, str
                                  _ptr(y), _dt(y, "y"), _stream(stream))
     _check("gdn_gated_rmsnorm", st)
     return y
+
+
+def gdn_decode_step_fused(x, conv_state, conv_weight, a, b, A_log, dt_bias, state, nk, cu_seqlens=None,
+                          conv_bias=None, o=None, o_dtype=torch.float32, scale=None, qk_l2norm=True, stream=None):
+    """Conv update + SiLU, gating and the recurrent rule in one launch.
+
+    x: [T, conv_dim] (token-strided view allowed) with conv_dim = 2*nk*128 + nv*128 packed q|k|v;
+    conv_state [n, conv_dim, state_len] and state [n, nv, 128, 128] are updated in place;
+    a, b: [T, nv]. Returns o [T, nv, 128].
+    """
+    _need(x, "x", contiguous=False)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x: expected a [T, C] view with dense channels")
+    _need(conv_state, "conv_state", x.dtype); _need(conv_weight, "conv_weight", torch.float32)
+    _need(a, "a", x.dtype); _need(b, "b", x.dtype)
+    _need(A_log, "A_log", torch.float32); _need(dt_bias, "dt_bias", torch.float32)
+    _need(state, "state", torch.float32)
+    T = x.shape[0]
+    n, nv, dk, dv = state.shape
+    cu, ncu = _cu(cu_seqlens, T)
+    if cu is not None and ncu != n:
+        raise ValueError(f"cu_seqlens describes {ncu} sequences, state holds {n}")
+    if o is None:
+        o = torch.empty((T, nv, dv), device=x.device, dtype=o_dtype)
+    st = lib().gdn_decode_step_fused(_ptr(x), _dt(x, "x"), x.stride(0), _ptr(conv_state), conv_state.shape[2],
+                                     _ptr(conv_weight), _ptr(conv_bias), conv_weight.shape[1], _ptr(a), _ptr(b),
+                                     _ptr(A_log), _ptr(dt_bias), _ptr(cu), n, T, nk, nv, dk, dv, float(scale or 0.0),
+                                     int(bool(qk_l2norm)), _ptr(state), _ptr(o), _dt(o, "o"), _stream(stream))
+    _check("gdn_decode_step_fused", st)
+    return o

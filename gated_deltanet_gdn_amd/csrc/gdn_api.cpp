@@ -156,6 +156,50 @@ int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
                   fn);
 }
 
+int gdn_decode_step_fused(const void* x, int dtype, int64_t x_tok_stride, void* conv_state, int state_len,
+                          const float* conv_weight, const float* conv_bias, int K, const void* a, const void* b,
+                          const float* A_log, const float* dt_bias, const int32_t* cu_seqlens, int n_seqs,
+                          int64_t T_tot, int nk, int nv, int dk, int dv, float scale, int qk_l2norm, float* state,
+                          void* o, int o_dtype, void* stream) {
+  const char* fn = "gdn_decode_step_fused";
+  if (!valid_dtype(dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not f32/bf16", fn, dtype);
+  if (!valid_dtype(o_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: o_dtype %d is not f32/bf16", fn, o_dtype);
+  if (n_seqs <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: n_seqs must be >= 1 (got %d)", fn, n_seqs);
+  if (T_tot < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: T_tot must be >= 0", fn);
+  if (nk <= 0 || nv <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: head counts must be positive", fn);
+  if (nv % nk != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: nv (%d) must be a multiple of nk (%d)", fn, nv, nk);
+  if (dk <= 0 || dv <= 0 || K <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dk, dv and K must be positive", fn);
+  if (state_len < K - 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_len (%d) < K - 1", fn, state_len);
+  if (!cu_seqlens && T_tot != n_seqs)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: without cu_seqlens T_tot must equal n_seqs (one token each)", fn);
+  if (!conv_state || !conv_weight || !A_log || !dt_bias || !state)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: conv_state, conv_weight, A_log, dt_bias and state are required", fn);
+  if (T_tot > 0 && (!x || !a || !b || !o))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, a, b and o are required", fn);
+  if (dk != 128 || dv != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: only dk = dv = 128 is built (got %d, %d)", fn, dk, dv);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: only K = 4 is built (got %d)", fn, K);
+  const int r = nv / nk;
+  if (r != 1 && r != 2 && r != 4)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: nv / nk must be 1, 2 or 4 (got %d)", fn, r);
+  const int64_t conv_dim = static_cast<int64_t>(2 * nk) * dk + static_cast<int64_t>(nv) * dv;
+  if (conv_dim > INT32_MAX / 8) return fail(GDN_ERR_UNSUPPORTED, "%s: conv_dim too large", fn);
+  if (x_tok_stride == 0) x_tok_stride = conv_dim;
+  if (x_tok_stride < conv_dim)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x token stride smaller than conv_dim (%lld)", fn,
+                static_cast<long long>(conv_dim));
+  if (T_tot > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: T_tot above 2^31-1", fn);
+  if (static_cast<int64_t>(n_seqs) * nk > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: too many workgroups", fn);
+  if (!aligned(state, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: state must be 16-byte aligned", fn);
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
+  return launched(gdn::launch_decode_fused(x, dtype == GDN_BF16, x_tok_stride, conv_state, state_len, conv_weight,
+                                           conv_bias, a, b, A_log, dt_bias, cu_seqlens, n_seqs, T_tot, nk, nv, scale,
+                                           qk_l2norm != 0, state, o, o_dtype == GDN_BF16,
+                                           static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 int gdn_causal_conv1d(const void* x, int dtype, int64_t x_tok_stride, const float* weight, const float* bias,
                       const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int conv_dim, int K,
                       const void* conv_state_in, void* conv_state_out, int state_len, int silu, void* y,

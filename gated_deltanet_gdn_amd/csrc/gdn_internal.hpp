@@ -30,10 +30,18 @@ hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf1
                             const int32_t* cu, int n_seqs, int64_t T, int nk, int nv, float scale, int l2,
                             float* state, void* o, int o_bf16, hipStream_t s);
 
+// Fused decode step (conv update + SiLU, gating, recurrent rule); nv / nk must
+// be 1, 2 or 4.
+hipError_t launch_decode_fused(const void* x, int bf16, int64_t x_stride, void* conv_state, int state_len,
+                               const float* conv_w, const float* conv_b, const void* a, const void* b,
+                               const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs,
+                               int64_t T_tot, int nk, int nv, float scale, int l2, float* state, void* o,
+                               int o_bf16, hipStream_t s);
+
 // Chunked path. The workspace holds, per chunk and value head, the packed
 // 64x64 tile [T strictly lower | P turned by 180 degrees on and above the
 // diagonal] and the per-token scalars, and for bf16 inputs per chunk and key
-// head the K, Q and K^T operand tiles; see k_chunk.hip.
+// head the K and Q operand tiles; see k_chunk.hip.
 size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nk, int nv, int bf16);
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf16,
                             int64_t qs, int64_t ks, int64_t vs, const float* g, const float* beta,

@@ -129,6 +129,47 @@ int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
                       float* state, void* o, int o_dtype, void* stream);
 
 /*
+ * One fused decode step of the layer core: conv update with SiLU over the
+ * packed q|k|v channels, gating, and the recurrent gated delta rule with
+ * L2-normalised q and k, in a single launch ("Qwen3.5 Dense Model
+ * Architecture", Linear Attention, decode branch of the minimal example and
+ * its cache table: conv state and recurrent state are updated in place;
+ * "Qwen3.5 Simulation Support Design Document", 2.2 ops 1, 3 and 5 and 2.3:
+ * single-token and 1 + num_mtp_tokens (MTP) decode batches take the
+ * recurrent path; "Qwen3.5 / Qwen3.6 Inference Path on vLLM Ascend", step
+ * execution and graph capture: decode steps run as captured device graphs).
+ *
+ * The result is that of gdn_causal_conv1d_update (gdn_causal_conv1d with
+ * conv_state_in/out for several tokens per sequence), gdn_gating and
+ * gdn_recurrent_fwd run one after the other, with q, k, v the views of the
+ * conv output at channel offsets 0, nk*dk and 2*nk*dk, and the conv output
+ * rounded to the activation dtype in between as a stored tensor would be.
+ * For one token per sequence the fused step reproduces those three launches
+ * bit for bit.
+ *   x          : [T_tot, conv_dim] of dtype, channels dense, token stride
+ *                x_tok_stride (0 = conv_dim); conv_dim = 2*nk*dk + nv*dv
+ *   conv_state : [n_seqs, conv_dim, state_len] of dtype, updated in place to
+ *                the last state_len entries of [conv_state, x of the sequence]
+ *   conv_weight: [conv_dim, K] fp32;  conv_bias : [conv_dim] fp32 or NULL
+ *   a, b       : [T_tot, nv] of dtype, dense;  A_log, dt_bias : [nv] fp32
+ *   cu_seqlens : device int32 [n_seqs + 1] (tokens of each sequence, 0 allowed),
+ *                or NULL for exactly one token per sequence (T_tot == n_seqs)
+ *   scale      : <= 0 selects dk^-1/2
+ *   state      : [n_seqs, nv, dk, dv] fp32, updated in place
+ *   o          : [T_tot, nv, dv] of o_dtype
+ * Supported: dk = dv = 128, K = 4, nv / nk in {1, 2, 4}, dtype f32 or bf16.
+ * Calls that share conv_state or state rows must not overlap in time.
+ */
+int gdn_decode_step_fused(const void* x, int dtype, int64_t x_tok_stride,
+                          void* conv_state, int state_len,
+                          const float* conv_weight, const float* conv_bias, int K,
+                          const void* a, const void* b,
+                          const float* A_log, const float* dt_bias,
+                          const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                          int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                          float* state, void* o, int o_dtype, void* stream);
+
+/*
  * Causal depthwise conv1d with optional SiLU over packed sequences, the
  * prefill conv body ("Qwen3.5 Simulation Support Design Document", 2.4;
  * "Qwen3.5 Dense Model Architecture", Linear Attention: depthwise Conv1d of

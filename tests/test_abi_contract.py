@@ -180,3 +180,43 @@ def test_python_binding_requires_device_tensors():
     x = torch.zeros(4, 2)
     with pytest.raises(ValueError):
         gdn.gdn_gating(x, x, torch.zeros(2), torch.zeros(2))
+
+
+def _fused(L, **kw):
+    a = dict(x=P, dtype=1, xs=0, cst=P, sl=3, w=P, bias=NULL, K=4, a=P, b=P, alog=P, dtb=P, cu=NULL, n=4, T=4,
+             nk=2, nv=4, dk=128, dv=128, scale=0.0, l2=1, state=P2, o=P, o_dtype=0, stream=NULL)
+    a.update(kw)
+    return L.gdn_decode_step_fused(a["x"], a["dtype"], a["xs"], a["cst"], a["sl"], a["w"], a["bias"], a["K"], a["a"],
+                                   a["b"], a["alog"], a["dtb"], a["cu"], a["n"], a["T"], a["nk"], a["nv"], a["dk"],
+                                   a["dv"], a["scale"], a["l2"], a["state"], a["o"], a["o_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nk=3, nv=4), INVALID),            # nv % nk != 0
+    (dict(dtype=3), INVALID),
+    (dict(o_dtype=2), INVALID),
+    (dict(n=0), INVALID),
+    (dict(T=5), INVALID),                   # one token per sequence without cu_seqlens
+    (dict(sl=2), INVALID),                  # state_len < K - 1
+    (dict(cst=NULL), INVALID),
+    (dict(w=NULL), INVALID),
+    (dict(state=NULL), INVALID),
+    (dict(alog=NULL), INVALID),
+    (dict(x=NULL), INVALID),
+    (dict(o=NULL), INVALID),
+    (dict(xs=1000), INVALID),               # token stride below conv_dim = (2*2 + 4) * 128
+    (dict(nk=1, nv=8), UNSUPPORTED),        # eight value heads per key head
+    (dict(nk=2, nv=6), UNSUPPORTED),        # three value heads per key head
+    (dict(dk=64), UNSUPPORTED),
+    (dict(K=3, sl=2), UNSUPPORTED),
+    (dict(state=MIS), UNSUPPORTED),
+])
+def test_decode_step_fused_argument_errors(L, kw, status):
+    assert _fused(L, **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
+def test_decode_step_fused_empty_batch_needs_no_inputs(L):
+    # no tokens: x, a, b and o may be NULL; the call is still a valid (state-preserving) launch
+    # request, so only argument checks run here -- with T = 0 and cu_seqlens NULL it must fail
+    assert _fused(L, T=0, x=NULL, a=NULL, b=NULL, o=NULL) == INVALID

@@ -1,0 +1,204 @@
+"""GPU parity of the fused decode step (conv update + SiLU, gating and the
+recurrent rule in one launch).
+
+One token per sequence: the fused step must equal the three separate
+launches bit for bit. Several tokens per sequence (1 + draft tokens, ragged,
+with empty sequences): equal to the separate prefill-conv, gating and
+recurrent launches bit for bit. In both cases the outputs also meet the parity
+bar against the fp64 oracle pipeline (conv output checked against the oracle
+conv, the delta rule on the conv output as rounded to the activation dtype),
+and the conv state equals the oracle's exactly. The decode workload itself runs at full size
+against the separate launches, and a captured device graph of the step is
+replayed against eager steps. Each test prints its case before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_gdn_amd as gdn
+import oracle
+import workloads as W
+from gpu_common import TOL, assert_close, assert_conv_close, conv_abs_sum, dev, f64
+
+pytestmark = pytest.mark.gpu
+DK = 128
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _to(d):
+    return {k: (v.to(dev()) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def _qkv(y, nk, nv):
+    kd = nk * DK
+    T = y.shape[0]
+    return y[:, :kd].view(T, nk, DK), y[:, kd:2 * kd].view(T, nk, DK), y[:, 2 * kd:].view(T, nv, DK)
+
+
+def _separate(d, nk, cu=None):
+    """The same step as separate launches: conv (update, or prefill conv with state in/out), gating, recurrent."""
+    state = d["state"].clone()
+    nv = state.shape[1]
+    if cu is None:
+        conv_state = d["conv_state"].clone()
+        y = gdn.gdn_causal_conv1d_update(d["x"], conv_state, d["conv_w"])
+    else:
+        y, conv_state = gdn.gdn_causal_conv1d(d["x"], d["conv_w"], cu_seqlens=cu, conv_state_in=d["conv_state"])
+    q, k, v = _qkv(y, nk, nv)
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    o = gdn.gdn_recurrent_fwd(q, k, v, g, beta, state, cu_seqlens=cu)
+    return o, state, conv_state, y
+
+
+def _fused(d, nk, cu=None):
+    conv_state, state = d["conv_state"].clone(), d["state"].clone()
+    o = gdn.gdn_decode_step_fused(d["x"], conv_state, d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], state,
+                                  nk, cu_seqlens=cu)
+    return o, state, conv_state
+
+
+def _oracle(x, nk, nv, dtype, cu, y_gpu):
+    """fp64 pipeline, one stage at a time. The conv output is checked against the oracle conv; the
+    delta rule then runs on the conv output the GPU produced. (In bf16 a one-ulp rounding flip of a
+    single v element moves the state by more than the parity bar; in fp32 the conv's own rounding,
+    about 1e-7 relative, uses up the core's 1e-5 bar. Each stage is therefore held to its own bar on
+    the same inputs, as the separate-launch decode test does.)"""
+    y, cs = oracle.causal_conv1d(f64(x["x"]), f64(x["conv_w"]), cu_seqlens=cu, conv_state=f64(x["conv_state"]))
+    if dtype == "bf16":
+        hist = f64(x["conv_state"])[:, :, -3:]
+        s_abs = np.concatenate([conv_abs_sum(np.concatenate([hist[n].T, f64(x["x"])[cu[n]:cu[n + 1]]]),
+                                             f64(x["conv_w"])) for n in range(len(cu) - 1)])
+        assert_conv_close(y_gpu, y, s_abs, "conv output")
+    else:
+        assert_close(y_gpu, y, TOL["f32"], "conv output")
+    y = f64(y_gpu)
+    kd = nk * DK
+    T = y.shape[0]
+    g, beta = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    o, st = oracle.delta_rule(y[:, :kd].reshape(T, nk, DK), y[:, kd:2 * kd].reshape(T, nk, DK),
+                              y[:, 2 * kd:].reshape(T, nv, DK), g, beta, cu_seqlens=cu,
+                              initial_state=f64(x["state"]))
+    return o, st, cs
+
+
+def _same(a, b, what):
+    diff = (a.double() - b.double()).abs().max().item() if a.numel() else 0.0
+    print(f"[exact] {what}: max |fused - separate| = {diff:.3e}", flush=True)
+    assert torch.equal(a, b), f"{what}: fused step differs from the separate launches"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nk,nv", [(4, 8), (2, 2), (2, 8)])
+def test_fused_single_token(dtype, nk, nv):
+    _say("fused decode, one token per sequence", dtype, nk, nv)
+    wl = W.Workload("fused_1tok", 11, "decode", dtype, n_seqs=24, nk=nk, nv=nv, s0_std=0.02)
+    x = W.decode_inputs(wl)
+    d = _to(x)
+    o, st, cs = _fused(d, nk)
+    o2, st2, cs2, y = _separate(d, nk)
+    torch.cuda.synchronize()
+    _same(o, o2, "o"); _same(st, st2, "state"); _same(cs, cs2, "conv state")
+    n = wl.n_seqs
+    o_ref, s_ref, cs_ref = _oracle(x, nk, nv, dtype, np.arange(n + 1), y)
+    assert_close(o, o_ref, TOL[dtype], "fused o")
+    assert_close(st, s_ref, TOL[dtype], "fused state")
+    np.testing.assert_array_equal(f64(cs), cs_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nk,nv,lengths", [
+    (2, 4, [4, 1, 0, 4, 2, 4, 3]),      # 1 + 3 draft tokens, ragged, one empty sequence
+    (1, 4, [4, 4, 1]),
+    (2, 2, [3, 0, 4, 5]),
+])
+def test_fused_multi_token(dtype, nk, nv, lengths):
+    _say("fused decode, several tokens per sequence", dtype, nk, nv, lengths)
+    wl = W.Workload("fused_mtp", 12, "decode", dtype, nk=nk, nv=nv, s0_std=0.02)
+    x = W.decode_mtp_inputs(wl, lengths)
+    d = _to(x)
+    cu = d["cu_seqlens"]
+    o, st, cs = _fused(d, nk, cu)
+    o2, st2, cs2, y = _separate(d, nk, cu)
+    torch.cuda.synchronize()
+    _same(o, o2, "o"); _same(st, st2, "state"); _same(cs, cs2, "conv state")
+    o_ref, s_ref, cs_ref = _oracle(x, nk, nv, dtype, x["cu_seqlens"].numpy(), y)
+    assert_close(o, o_ref, TOL[dtype], "fused mtp o")
+    assert_close(st, s_ref, TOL[dtype], "fused mtp state")
+    np.testing.assert_array_equal(f64(cs), cs_ref)
+
+
+def test_fused_state_len_above_window():
+    _say("fused decode, conv state of 5 entries")
+    nk, nv, lengths = 2, 4, [1, 2, 7, 0]
+    wl = W.Workload("fused_sl5", 13, "decode", "bf16", nk=nk, nv=nv, s0_std=0.02, state_len=5)
+    x = W.decode_mtp_inputs(wl, lengths)
+    d = _to(x)
+    o, st, cs = _fused(d, nk, d["cu_seqlens"])
+    o2, st2, cs2, y = _separate(d, nk, d["cu_seqlens"])
+    torch.cuda.synchronize()
+    _same(o, o2, "o"); _same(st, st2, "state"); _same(cs, cs2, "conv state")
+    o_ref, s_ref, cs_ref = _oracle(x, nk, nv, "bf16", x["cu_seqlens"].numpy(), y)
+    assert_close(o, o_ref, TOL["bf16"], "fused sl5 o")
+    assert_close(st, s_ref, TOL["bf16"], "fused sl5 state")
+    np.testing.assert_array_equal(f64(cs), cs_ref)
+
+
+def test_fused_decode_workload_full_size():
+    wl = W.WORKLOADS["decode_256seq"]
+    _say(wl.name, "fused vs separate launches, full size")
+    d = _to(W.decode_inputs(wl))
+    o, st, cs = _fused(d, wl.nk)
+    o2, st2, cs2, _ = _separate(d, wl.nk)
+    torch.cuda.synchronize()
+    _same(o, o2, "o"); _same(st, st2, "state"); _same(cs, cs2, "conv state")
+
+
+def test_fused_mtp_workload_full_size():
+    wl = W.WORKLOADS["decode_mtp_256x4"]
+    lengths = [wl.extra["tokens_per_seq"]] * wl.n_seqs
+    _say(wl.name, "fused vs separate launches, full size")
+    d = _to(W.decode_mtp_inputs(wl, lengths))
+    o, st, cs = _fused(d, wl.nk, d["cu_seqlens"])
+    o2, st2, cs2, _ = _separate(d, wl.nk, d["cu_seqlens"])
+    torch.cuda.synchronize()
+    _same(o, o2, "o"); _same(st, st2, "state"); _same(cs, cs2, "conv state")
+
+
+def test_fused_step_in_a_device_graph():
+    """Capture one step, replay it three times with eager work and syncs in between; every replay must
+    equal the same step run eagerly on identical buffers."""
+    _say("fused decode step captured in a graph")
+    nk, nv = 4, 8
+    wl = W.Workload("fused_graph", 14, "decode", "bf16", n_seqs=32, nk=nk, nv=nv, s0_std=0.02)
+    d = _to(W.decode_inputs(wl))
+    cs_g, st_g = d["conv_state"].clone(), d["state"].clone()
+    o_g = torch.empty((wl.n_seqs, nv, DK), device=dev())
+    cs_e, st_e = d["conv_state"].clone(), d["state"].clone()
+
+    def step(cs, st, o, stream=None):
+        gdn.gdn_decode_step_fused(d["x"], cs, d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], st, nk,
+                                  o=o, stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(cs_g, st_g, o_g, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # capture does not run the step: the buffers still hold their inputs
+    _same(st_g, d["state"], "state after capture")
+    for rep in range(3):
+        o_e = torch.empty_like(o_g)
+        step(cs_e, st_e, o_e)
+        filler = torch.randn(1 << 20, device=dev()).sum()     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(filler)
+        _same(o_g, o_e, f"replay {rep} o"); _same(st_g, st_e, f"replay {rep} state")
+        _same(cs_g, cs_e, f"replay {rep} conv state")

@@ -62,6 +62,9 @@ WORKLOADS = {
     "decode_256seq": Workload("decode_256seq", 4, "decode", "bf16", n_seqs=256, nk=16, nv=32,
                               s0_std=0.02),
     "long_fused_t256k": Workload("long_fused_t256k", 5, "fused", "bf16", T=262144, nk=16, nv=64),
+    # decode with multi-token prediction: each sequence carries 1 + 3 draft tokens
+    "decode_mtp_256x4": Workload("decode_mtp_256x4", 6, "decode", "bf16", n_seqs=256, nk=16, nv=32,
+                                 s0_std=0.02, extra=dict(tokens_per_seq=4)),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -148,6 +151,26 @@ def decode_inputs(wl: Workload, device="cpu", n_seqs=None):
         A_log=a_log(wl.nv, s, device),
         dt_bias=randn((wl.nv,), s, IDX["dt_bias"], "f32", std=0.1, device=device),
         state=randn((n, wl.nv, wl.dk, wl.dv), s, IDX["S0"], "f32", std=wl.s0_std, device=device),
+    )
+
+
+def decode_mtp_inputs(wl: Workload, lengths, device="cpu"):
+    """Inputs of a decode step with lengths[n] tokens for sequence n (1 + draft tokens):
+    packed x [sum, conv_dim], a, b [sum, nv], per-sequence conv and recurrent states, cu_seqlens."""
+    n, T = len(lengths), int(sum(lengths))
+    s, dt = wl.seed, wl.dtype
+    C = wl.conv_dim
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+    return dict(
+        x=randn((T, C), s, IDX["x"], dt, device=device),
+        conv_state=randn((n, C, wl.state_len), s, IDX["conv_state"], dt, device=device),
+        conv_w=uniform((C, wl.conv_k), s, IDX["conv_w"], -0.5, 0.5, device),
+        a=randn((T, wl.nv), s, IDX["a"], dt, device=device),
+        b=randn((T, wl.nv), s, IDX["b"], dt, device=device),
+        A_log=a_log(wl.nv, s, device),
+        dt_bias=randn((wl.nv,), s, IDX["dt_bias"], "f32", std=0.1, device=device),
+        state=randn((n, wl.nv, wl.dk, wl.dv), s, IDX["S0"], "f32", std=wl.s0_std, device=device),
+        cu_seqlens=cu.to(device),
     )
 
 
