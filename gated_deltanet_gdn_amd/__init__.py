@@ -58,7 +58,7 @@ def lib():
         "gdn_causal_conv1d_update": (i32, [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp]),
         "gdn_gated_rmsnorm": (i32, [vp, i32, vp, i32, vp, i64, i32, f32, vp, i32, vp]),
         "gdn_decode_step_fused": (i32, [vp, i32, i64, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, i32, i64, i32, i32,
-                                        i32, i32, f32, i32, vp, vp, i32, vp]),
+                                        i32, i32, f32, i32, vp, vp, i32, vp, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -255,12 +255,15 @@ def gdn_gated_rmsnorm(x, z, weight, eps=1e-6, y=None, y_dtype=torch.float32, str
 
 
 def gdn_decode_step_fused(x, conv_state, conv_weight, a, b, A_log, dt_bias, state, nk, cu_seqlens=None,
-                          conv_bias=None, o=None, o_dtype=torch.float32, scale=None, qk_l2norm=True, stream=None):
+                          conv_bias=None, state_indices=None, state_snapshots=None, o=None, o_dtype=torch.float32,
+                          scale=None, qk_l2norm=True, stream=None):
     """Conv update + SiLU, gating and the recurrent rule in one launch.
 
     x: [T, conv_dim] (token-strided view allowed) with conv_dim = 2*nk*128 + nv*128 packed q|k|v;
-    conv_state [n, conv_dim, state_len] and state [n, nv, 128, 128] are updated in place;
-    a, b: [T, nv]. Returns o [T, nv, 128].
+    conv_state [slots, conv_dim, state_len] and state [slots, nv, 128, 128] are updated in place;
+    a, b: [T, nv]. state_indices (int32 [n]) maps sequence n to its slot (negative = padding, skipped);
+    without it sequence n uses slot n. state_snapshots ([T, nv, 128, 128] fp32) receives the state
+    after every token. Returns o [T, nv, 128].
     """
     _need(x, "x", contiguous=False)
     if x.dim() != 2 or x.stride(1) != 1:
@@ -270,15 +273,27 @@ def gdn_decode_step_fused(x, conv_state, conv_weight, a, b, A_log, dt_bias, stat
     _need(A_log, "A_log", torch.float32); _need(dt_bias, "dt_bias", torch.float32)
     _need(state, "state", torch.float32)
     T = x.shape[0]
-    n, nv, dk, dv = state.shape
-    cu, ncu = _cu(cu_seqlens, T)
-    if cu is not None and ncu != n:
-        raise ValueError(f"cu_seqlens describes {ncu} sequences, state holds {n}")
+    n_slots, nv, dk, dv = state.shape
+    if conv_state.shape[0] != n_slots:
+        raise ValueError("conv_state and state must hold the same number of slots")
+    cu, n = _cu(cu_seqlens, T)
+    if state_indices is not None:
+        _need(state_indices, "state_indices", torch.int32)
+        if cu is not None and state_indices.numel() != n:
+            raise ValueError(f"state_indices has {state_indices.numel()} entries, cu_seqlens {n} sequences")
+        n = state_indices.numel()
+    elif cu is None:
+        n = n_slots
+    elif n != n_slots:
+        raise ValueError(f"cu_seqlens describes {n} sequences, state holds {n_slots} slots")
+    if state_snapshots is not None:
+        _need(state_snapshots, "state_snapshots", torch.float32)
     if o is None:
         o = torch.empty((T, nv, dv), device=x.device, dtype=o_dtype)
     st = lib().gdn_decode_step_fused(_ptr(x), _dt(x, "x"), x.stride(0), _ptr(conv_state), conv_state.shape[2],
                                      _ptr(conv_weight), _ptr(conv_bias), conv_weight.shape[1], _ptr(a), _ptr(b),
                                      _ptr(A_log), _ptr(dt_bias), _ptr(cu), n, T, nk, nv, dk, dv, float(scale or 0.0),
-                                     int(bool(qk_l2norm)), _ptr(state), _ptr(o), _dt(o, "o"), _stream(stream))
+                                     int(bool(qk_l2norm)), _ptr(state), _ptr(state_indices), n_slots,
+                                     _ptr(state_snapshots), _ptr(o), _dt(o, "o"), _stream(stream))
     _check("gdn_decode_step_fused", st)
     return o

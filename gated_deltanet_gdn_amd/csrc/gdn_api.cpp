@@ -160,7 +160,8 @@ int gdn_decode_step_fused(const void* x, int dtype, int64_t x_tok_stride, void* 
                           const float* conv_weight, const float* conv_bias, int K, const void* a, const void* b,
                           const float* A_log, const float* dt_bias, const int32_t* cu_seqlens, int n_seqs,
                           int64_t T_tot, int nk, int nv, int dk, int dv, float scale, int qk_l2norm, float* state,
-                          void* o, int o_dtype, void* stream) {
+                          const int32_t* state_indices, int n_slots, float* state_snapshots, void* o, int o_dtype,
+                          void* stream) {
   const char* fn = "gdn_decode_step_fused";
   if (!valid_dtype(dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not f32/bf16", fn, dtype);
   if (!valid_dtype(o_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: o_dtype %d is not f32/bf16", fn, o_dtype);
@@ -192,11 +193,18 @@ int gdn_decode_step_fused(const void* x, int dtype, int64_t x_tok_stride, void* 
   if (T_tot > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: T_tot above 2^31-1", fn);
   if (static_cast<int64_t>(n_seqs) * nk > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: too many workgroups", fn);
   if (!aligned(state, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: state must be 16-byte aligned", fn);
+  if (state_indices) {
+    if (n_slots <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: n_slots must be >= 1 with state_indices", fn);
+  } else if (n_slots != n_seqs) {
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: without state_indices n_slots must equal n_seqs", fn);
+  }
+  if (state_snapshots && !aligned(state_snapshots, 16))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: state_snapshots must be 16-byte aligned", fn);
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
   return launched(gdn::launch_decode_fused(x, dtype == GDN_BF16, x_tok_stride, conv_state, state_len, conv_weight,
                                            conv_bias, a, b, A_log, dt_bias, cu_seqlens, n_seqs, T_tot, nk, nv, scale,
-                                           qk_l2norm != 0, state, o, o_dtype == GDN_BF16,
-                                           static_cast<hipStream_t>(stream)),
+                                           qk_l2norm != 0, state, state_indices, n_slots, state_snapshots, o,
+                                           o_dtype == GDN_BF16, static_cast<hipStream_t>(stream)),
                   fn);
 }
 

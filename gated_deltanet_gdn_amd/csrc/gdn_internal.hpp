@@ -35,8 +35,9 @@ hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf1
 hipError_t launch_decode_fused(const void* x, int bf16, int64_t x_stride, void* conv_state, int state_len,
                                const float* conv_w, const float* conv_b, const void* a, const void* b,
                                const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs,
-                               int64_t T_tot, int nk, int nv, float scale, int l2, float* state, void* o,
-                               int o_bf16, hipStream_t s);
+                               int64_t T_tot, int nk, int nv, float scale, int l2, float* state,
+                               const int32_t* slots, int n_slots, float* snap, void* o, int o_bf16,
+                               hipStream_t s);
 
 // Chunked path. The workspace holds, per chunk and value head, the packed
 // 64x64 tile [T strictly lower | P turned by 180 degrees on and above the

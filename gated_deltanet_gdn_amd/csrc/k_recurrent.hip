@@ -202,13 +202,14 @@ recurrent_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
 // heads R hk .. R hk + R - 1; one or two channels per thread. The gating
 // inputs are wave-uniform (one value head per wave), so every thread computes
 // g and beta itself from scalar loads.
-template <typename T, typename TO, int R>
+template <typename T, typename TO, int R, bool SNAP>
 __global__ void __launch_bounds__(256 * R) __attribute__((amdgpu_waves_per_eu(R == 1 ? 3 : 4)))
 decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, int state_len,
                     const float* __restrict__ cw, const float* __restrict__ cb, const T* __restrict__ a,
                     const T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                     const int32_t* __restrict__ cu, int64_t T_tot, int nk, int nv, float scale, int l2,
-                    float* __restrict__ state, TO* __restrict__ o) {
+                    float* __restrict__ state, const int32_t* __restrict__ slots, int n_slots,
+                    float* __restrict__ snap, TO* __restrict__ o) {
   constexpr int NCH = (2 + R) * D;
   constexpr int NT = 256 * R;
   constexpr int CPT = (NCH + NT - 1) / NT;
@@ -217,6 +218,10 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
   __shared__ float red[2][R][4][2][D];  // [parity][value head][wave][a|b][column]
 
   const int n = blockIdx.x / nk, hk = blockIdx.x % nk;
+  // the sequence's slot in the state pools; a negative slot (padding) or one
+  // past the pool leaves the sequence untouched (the whole workgroup returns)
+  const int slot = slots ? slots[n] : n;
+  if (slot < 0 || slot >= n_slots) return;
   const int tid = threadIdx.x, t256 = tid & 255;
   const int rho = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int h = hk * R + rho;
@@ -239,7 +244,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
   for (int u = 0; u < CPT; ++u) {
     const int j = tid + u * NT;
     if (j < NCH) {
-      const T* sp = cst + (static_cast<int64_t>(n) * conv_dim + chan(j)) * state_len + (state_len - (KW - 1));
+      const T* sp = cst + (static_cast<int64_t>(slot) * conv_dim + chan(j)) * state_len + (state_len - (KW - 1));
 #pragma unroll
       for (int i = 0; i < KW - 1; ++i) hist[u][i] = Elem<T>::load(sp, i);
       if (t0 < t1) x_n[u] = x[t0 * xs + chan(j)];
@@ -249,7 +254,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
   T a_n{}, b_n{};
   if (t0 < t1) { a_n = a[t0 * nv + h]; b_n = b[t0 * nv + h]; }
 
-  float* Sp = state + (static_cast<int64_t>(n) * nv + h) * D * D;
+  float* Sp = state + (static_cast<int64_t>(slot) * nv + h) * D * D;
   // the state stream, as in the recurrent kernel
   float S[RPT][4];
   {
@@ -291,6 +296,16 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
     const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
     rec_token<TO>(S, &kqv_s[par][D], &kqv_s[par][0], vv, gt, bt, &red[par][rho][0][0][0], t256, scale, l2, o,
                   t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
+    if constexpr (SNAP) {   // the state after this token, for rolling back rejected draft tokens
+      // (buffer stores off one per-lane offset: the row addresses are not kept live)
+      const rsrc_t rs = make_rsrc(snap + (t * nv + h) * static_cast<int64_t>(D) * D, D * D * 4);
+      const uint32_t vo = static_cast<uint32_t>(((t256 / CGN) * D + col) * 4);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        bstore16_nt(rs, vo + static_cast<uint32_t>(RGN * D * 4 * i),
+                    make_uint4(__float_as_uint(S[i][0]), __float_as_uint(S[i][1]), __float_as_uint(S[i][2]),
+                               __float_as_uint(S[i][3])));
+    }
   }
   {
     const int rg = t256 / CGN;
@@ -311,7 +326,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
       const int j = tid + u * NT;
       if (j < NCH) {
         const int c = chan(j);
-        T* sp = cst + (static_cast<int64_t>(n) * conv_dim + c) * state_len;
+        T* sp = cst + (static_cast<int64_t>(slot) * conv_dim + c) * state_len;
         for (int s = 0; s < state_len; ++s) {
           const int64_t idx = L + s;
           sp[s] = idx < state_len ? sp[idx] : x[(t0 + idx - state_len) * xs + c];
@@ -351,12 +366,15 @@ hipError_t rec_dispatch(const void* q, const void* k, const void* v, int64_t qs,
 template <typename T, typename TO, int R>
 hipError_t fused_launch(const void* x, int64_t xs, void* cst, int state_len, const float* cw, const float* cb,
                         const void* a, const void* b, const float* A_log, const float* dt_bias, const int32_t* cu,
-                        int n_seqs, int64_t T_tot, int nk, int nv, float scale, int l2, float* state, void* o,
-                        hipStream_t s) {
+                        int n_seqs, int64_t T_tot, int nk, int nv, float scale, int l2, float* state,
+                        const int32_t* slots, int n_slots, float* snap, void* o, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(nk));
-  decode_fused_kernel<T, TO, R><<<grid, 256 * R, 0, s>>>(
-      static_cast<const T*>(x), xs, static_cast<T*>(cst), state_len, cw, cb, static_cast<const T*>(a),
-      static_cast<const T*>(b), A_log, dt_bias, cu, T_tot, nk, nv, scale, l2, state, static_cast<TO*>(o));
+  // snapshots are a separate instantiation: their stores inside the token
+  // loop would otherwise cost the plain step about 30 spilled VGPRs
+  auto kern = snap ? decode_fused_kernel<T, TO, R, true> : decode_fused_kernel<T, TO, R, false>;
+  kern<<<grid, 256 * R, 0, s>>>(static_cast<const T*>(x), xs, static_cast<T*>(cst), state_len, cw, cb,
+                                static_cast<const T*>(a), static_cast<const T*>(b), A_log, dt_bias, cu, T_tot, nk, nv,
+                                scale, l2, state, slots, n_slots, snap, static_cast<TO*>(o));
   return hipGetLastError();
 }
 
@@ -364,14 +382,14 @@ template <typename T, typename TO>
 hipError_t fused_dispatch_r(int r, const void* x, int64_t xs, void* cst, int state_len, const float* cw,
                             const float* cb, const void* a, const void* b, const float* A_log, const float* dt_bias,
                             const int32_t* cu, int n_seqs, int64_t T_tot, int nk, int nv, float scale, int l2,
-                            float* state, void* o, hipStream_t s) {
+                            float* state, const int32_t* slots, int n_slots, float* snap, void* o, hipStream_t s) {
   switch (r) {
     case 1: return fused_launch<T, TO, 1>(x, xs, cst, state_len, cw, cb, a, b, A_log, dt_bias, cu, n_seqs, T_tot,
-                                          nk, nv, scale, l2, state, o, s);
+                                          nk, nv, scale, l2, state, slots, n_slots, snap, o, s);
     case 2: return fused_launch<T, TO, 2>(x, xs, cst, state_len, cw, cb, a, b, A_log, dt_bias, cu, n_seqs, T_tot,
-                                          nk, nv, scale, l2, state, o, s);
+                                          nk, nv, scale, l2, state, slots, n_slots, snap, o, s);
     case 4: return fused_launch<T, TO, 4>(x, xs, cst, state_len, cw, cb, a, b, A_log, dt_bias, cu, n_seqs, T_tot,
-                                          nk, nv, scale, l2, state, o, s);
+                                          nk, nv, scale, l2, state, slots, n_slots, snap, o, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -381,20 +399,22 @@ hipError_t fused_dispatch_r(int r, const void* x, int64_t xs, void* cst, int sta
 hipError_t launch_decode_fused(const void* x, int bf16, int64_t x_stride, void* conv_state, int state_len,
                                const float* conv_w, const float* conv_b, const void* a, const void* b,
                                const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs, int64_t T_tot,
-                               int nk, int nv, float scale, int l2, float* state, void* o, int o_bf16,
-                               hipStream_t s) {
+                               int nk, int nv, float scale, int l2, float* state, const int32_t* slots, int n_slots,
+                               float* snap, void* o, int o_bf16, hipStream_t s) {
   const int r = nv / nk;
   if (bf16)
     return o_bf16 ? fused_dispatch_r<uint16_t, uint16_t>(r, x, x_stride, conv_state, state_len, conv_w, conv_b, a, b,
                                                          A_log, dt_bias, cu, n_seqs, T_tot, nk, nv, scale, l2, state,
-                                                         o, s)
+                                                         slots, n_slots, snap, o, s)
                   : fused_dispatch_r<uint16_t, float>(r, x, x_stride, conv_state, state_len, conv_w, conv_b, a, b,
-                                                      A_log, dt_bias, cu, n_seqs, T_tot, nk, nv, scale, l2, state, o,
-                                                      s);
+                                                      A_log, dt_bias, cu, n_seqs, T_tot, nk, nv, scale, l2, state,
+                                                      slots, n_slots, snap, o, s);
   return o_bf16 ? fused_dispatch_r<float, uint16_t>(r, x, x_stride, conv_state, state_len, conv_w, conv_b, a, b,
-                                                    A_log, dt_bias, cu, n_seqs, T_tot, nk, nv, scale, l2, state, o, s)
+                                                    A_log, dt_bias, cu, n_seqs, T_tot, nk, nv, scale, l2, state, slots,
+                                                    n_slots, snap, o, s)
                 : fused_dispatch_r<float, float>(r, x, x_stride, conv_state, state_len, conv_w, conv_b, a, b, A_log,
-                                                 dt_bias, cu, n_seqs, T_tot, nk, nv, scale, l2, state, o, s);
+                                                 dt_bias, cu, n_seqs, T_tot, nk, nv, scale, l2, state, slots, n_slots,
+                                                 snap, o, s);
 }
 
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf16, int64_t qs, int64_t ks,

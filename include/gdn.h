@@ -148,14 +148,24 @@ int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
  * bit for bit.
  *   x          : [T_tot, conv_dim] of dtype, channels dense, token stride
  *                x_tok_stride (0 = conv_dim); conv_dim = 2*nk*dk + nv*dv
- *   conv_state : [n_seqs, conv_dim, state_len] of dtype, updated in place to
- *                the last state_len entries of [conv_state, x of the sequence]
+ *   conv_state : [n_slots, conv_dim, state_len] of dtype pool, updated in place
+ *                to the last state_len entries of [conv_state, x of the sequence]
  *   conv_weight: [conv_dim, K] fp32;  conv_bias : [conv_dim] fp32 or NULL
  *   a, b       : [T_tot, nv] of dtype, dense;  A_log, dt_bias : [nv] fp32
  *   cu_seqlens : device int32 [n_seqs + 1] (tokens of each sequence, 0 allowed),
  *                or NULL for exactly one token per sequence (T_tot == n_seqs)
  *   scale      : <= 0 selects dk^-1/2
- *   state      : [n_seqs, nv, dk, dv] fp32, updated in place
+ *   state      : [n_slots, nv, dk, dv] fp32 pool, updated in place
+ *   state_indices : device int32 [n_seqs] or NULL. Sequence n uses slot
+ *                state_indices[n] of both pools (state and conv_state, whose
+ *                first dimension is then n_slots); a slot < 0 or >= n_slots
+ *                marks padding: that sequence is skipped, its o rows are not
+ *                written. NULL means slot n (and n_slots must equal n_seqs).
+ *                Non-negative slots must be distinct.
+ *   state_snapshots : [T_tot, nv, dk, dv] fp32 or NULL: when given, the state
+ *                after every token is also written there (row t = the state
+ *                after token t), so a caller can roll back to the state after
+ *                any accepted draft token.
  *   o          : [T_tot, nv, dv] of o_dtype
  * Supported: dk = dv = 128, K = 4, nv / nk in {1, 2, 4}, dtype f32 or bf16.
  * Calls that share conv_state or state rows must not overlap in time.
@@ -167,7 +177,8 @@ int gdn_decode_step_fused(const void* x, int dtype, int64_t x_tok_stride,
                           const float* A_log, const float* dt_bias,
                           const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
                           int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
-                          float* state, void* o, int o_dtype, void* stream);
+                          float* state, const int32_t* state_indices, int n_slots,
+                          float* state_snapshots, void* o, int o_dtype, void* stream);
 
 /*
  * Causal depthwise conv1d with optional SiLU over packed sequences, the

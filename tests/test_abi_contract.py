@@ -184,11 +184,13 @@ def test_python_binding_requires_device_tensors():
 
 def _fused(L, **kw):
     a = dict(x=P, dtype=1, xs=0, cst=P, sl=3, w=P, bias=NULL, K=4, a=P, b=P, alog=P, dtb=P, cu=NULL, n=4, T=4,
-             nk=2, nv=4, dk=128, dv=128, scale=0.0, l2=1, state=P2, o=P, o_dtype=0, stream=NULL)
+             nk=2, nv=4, dk=128, dv=128, scale=0.0, l2=1, state=P2, idx=NULL, n_slots=4, snap=NULL, o=P, o_dtype=0,
+             stream=NULL)
     a.update(kw)
     return L.gdn_decode_step_fused(a["x"], a["dtype"], a["xs"], a["cst"], a["sl"], a["w"], a["bias"], a["K"], a["a"],
                                    a["b"], a["alog"], a["dtb"], a["cu"], a["n"], a["T"], a["nk"], a["nv"], a["dk"],
-                                   a["dv"], a["scale"], a["l2"], a["state"], a["o"], a["o_dtype"], a["stream"])
+                                   a["dv"], a["scale"], a["l2"], a["state"], a["idx"], a["n_slots"], a["snap"], a["o"],
+                                   a["o_dtype"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -210,6 +212,9 @@ def _fused(L, **kw):
     (dict(dk=64), UNSUPPORTED),
     (dict(K=3, sl=2), UNSUPPORTED),
     (dict(state=MIS), UNSUPPORTED),
+    (dict(n_slots=5), INVALID),             # without state_indices the pool has one slot per sequence
+    (dict(idx=P, n_slots=0), INVALID),
+    (dict(snap=MIS), UNSUPPORTED),
 ])
 def test_decode_step_fused_argument_errors(L, kw, status):
     assert _fused(L, **kw) == status

@@ -202,3 +202,68 @@ def test_fused_step_in_a_device_graph():
         assert torch.isfinite(filler)
         _same(o_g, o_e, f"replay {rep} o"); _same(st_g, st_e, f"replay {rep} state")
         _same(cs_g, cs_e, f"replay {rep} conv state")
+
+
+def test_fused_state_pool_slots():
+    """Sequences address their states through slots of a larger pool; slot -1 is padding."""
+    _say("fused decode with a state pool and a padding slot")
+    nk, nv, lengths = 2, 4, [1, 4, 2, 0, 3]
+    slots = [6, 0, -1, 3, 7]
+    n_slots = 8
+    wl = W.Workload("fused_pool", 15, "decode", "bf16", nk=nk, nv=nv, s0_std=0.02)
+    x = W.decode_mtp_inputs(wl, lengths)
+    d = _to(x)
+    C = wl.conv_dim
+    pool_st = W.randn((n_slots, nv, DK, DK), 15, 20, "f32", std=0.02, device=dev())
+    pool_cs = W.randn((n_slots, C, wl.state_len), 15, 21, "bf16", device=dev())
+    idx = torch.tensor(slots, dtype=torch.int32, device=dev())
+    # reference: the same step on states gathered into per-sequence order (padding gets slot 0's copy)
+    gather = torch.tensor([max(s, 0) for s in slots], device=dev(), dtype=torch.long)
+    ref = dict(d, state=pool_st[gather].clone(), conv_state=pool_cs[gather].clone())
+    o_ref, st_ref, cs_ref = _fused(ref, nk, d["cu_seqlens"])
+    st, cs = pool_st.clone(), pool_cs.clone()
+    T = sum(lengths)
+    o = torch.full((T, nv, DK), 7.0, device=dev())
+    gdn.gdn_decode_step_fused(d["x"], cs, d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], st, nk,
+                              cu_seqlens=d["cu_seqlens"], state_indices=idx, o=o)
+    torch.cuda.synchronize()
+    cu = x["cu_seqlens"].tolist()
+    for n, s in enumerate(slots):
+        rows = slice(cu[n], cu[n + 1])
+        if s < 0:
+            assert torch.all(o[rows] == 7.0), "padding sequence wrote o"
+            continue
+        _same(st[s], st_ref[n], f"slot {s} state"); _same(cs[s], cs_ref[n], f"slot {s} conv state")
+        _same(o[rows], o_ref[rows], f"sequence {n} o")
+    for s in set(range(n_slots)) - {s for s in slots if s >= 0}:
+        _same(st[s], pool_st[s], f"untouched slot {s} state"); _same(cs[s], pool_cs[s], f"untouched slot {s} conv")
+
+
+def test_fused_state_snapshots():
+    """With snapshots, row t holds the state after token t: the final state of the same step run on
+    each sequence's first tokens up to t."""
+    _say("fused decode with per-token state snapshots")
+    nk, nv, lengths = 2, 4, [4, 1, 3, 0, 2]
+    wl = W.Workload("fused_snap", 16, "decode", "bf16", nk=nk, nv=nv, s0_std=0.02)
+    x = W.decode_mtp_inputs(wl, lengths)
+    d = _to(x)
+    T = sum(lengths)
+    snap = torch.full((T, nv, DK, DK), float("nan"), device=dev())
+    cs, st = d["conv_state"].clone(), d["state"].clone()
+    o = gdn.gdn_decode_step_fused(d["x"], cs, d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], st, nk,
+                                  cu_seqlens=d["cu_seqlens"], state_snapshots=snap)
+    o_plain, st_plain, cs_plain = _fused(d, nk, d["cu_seqlens"])
+    torch.cuda.synchronize()
+    _same(o, o_plain, "o with snapshots"); _same(st, st_plain, "state with snapshots")
+    _same(cs, cs_plain, "conv state with snapshots")
+    cu = x["cu_seqlens"].tolist()
+    for p in range(1, max(lengths) + 1):
+        keep = [min(L, p) for L in lengths]
+        rows = torch.tensor([cu[n] + j for n in range(len(lengths)) for j in range(keep[n])], device=dev())
+        sub = dict(d, x=d["x"][rows].contiguous(), a=d["a"][rows].contiguous(), b=d["b"][rows].contiguous(),
+                   cu_seqlens=torch.tensor(np.concatenate([[0], np.cumsum(keep)]), dtype=torch.int32, device=dev()))
+        _, st_p, _ = _fused(sub, nk, sub["cu_seqlens"])
+        torch.cuda.synchronize()
+        for n, L in enumerate(lengths):
+            if L >= p:
+                _same(snap[cu[n] + p - 1], st_p[n], f"snapshot seq {n} token {p - 1}")
