@@ -146,6 +146,84 @@ def time_fused_decode(gdn, W, name, steps, warmup, stream, dev, tokens_per_seq=N
                               avg_ms=round(k_ms, 4), algorithmic_bytes=nbytes))
 
 
+def _timed(fn, reps, warmup, stream):
+    """Average ms per call of fn(): one pair of HIP events on its stream around reps back-to-back calls
+    (warm-up calls first), so that a short kernel is not charged the per-event overhead."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _hbm_row(workload, ms, nbytes, kernel):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return dict(workload=workload, kernel=kernel, bound="hbm", avg_ms=round(ms, 4), algorithmic_bytes=int(nbytes),
+                achieved=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4))
+
+
+def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
+    """The neighbours of the core on their own workloads at full size: causal conv + SiLU, gating,
+    the chunked rule and gated RMSNorm on the long prefill (T=262144, 16 -> 64 heads), conv update
+    on the 256-sequence decode batch. HIP events around each launch; algorithmic bytes each."""
+    import torch
+    rows = {}
+    wl = W.WORKLOADS["long_fused_t256k"]
+    x = W.fused_inputs(wl, device=dev)
+    T, C = x["x"].shape
+    kd = wl.nk * wl.dk
+    ms = _timed(lambda: gdn.gdn_causal_conv1d(x["x"], x["conv_w"], state_len=wl.state_len, stream=stream),
+                reps, warmup, stream)
+    rows["causal_conv1d"] = _hbm_row(f"long_fused_t256k: x [{T}, {C}] bf16 -> y, SiLU, conv state out", ms,
+                                     2 * T * C * 2 + C * wl.conv_k * 4 + C * wl.state_len * 2, "causal_conv1d_kernel")
+    y, _ = gdn.gdn_causal_conv1d(x["x"], x["conv_w"], state_len=wl.state_len, stream=stream)
+    g = torch.empty((T, wl.nv), device=dev)
+    beta = torch.empty_like(g)
+    ms = _timed(lambda: gdn.gdn_gating(x["a"], x["b"], x["A_log"], x["dt_bias"], g=g, beta=beta, stream=stream),
+                4 * reps, warmup, stream)
+    rows["gating"] = _hbm_row(f"long_fused_t256k: a, b [{T}, {wl.nv}] bf16 -> g, beta fp32", ms,
+                              T * wl.nv * 12 + wl.nv * 8, "gating_kernel")
+    q, k, v = y[:, :kd].view(T, wl.nk, wl.dk), y[:, kd:2 * kd].view(T, wl.nk, wl.dk), y[:, 2 * kd:].view(T, wl.nv, wl.dv)
+    o = torch.empty((T, wl.nv, wl.dv), device=dev)
+    st = torch.empty((1, wl.nv, wl.dk, wl.dv), device=dev)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(T, 1, wl.nk, wl.nv), device=dev, dtype=torch.uint8)
+    ms = _timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, final_state=st, o=o, workspace=ws, stream=stream),
+                max(2, reps // 2), 1, stream)
+    r = wl.nv // wl.nk
+    flops = chunk_flops_per_token_head(r=r) * T * wl.nv
+    cb = chunk_bytes(T, wl.nk, wl.nv)
+    tf = flops / (ms * 1e-3) / 1e12
+    rows["chunk_fwd"] = dict(workload=f"long_fused_t256k core: T={T}, {wl.nk}->{wl.nv} heads, q/k/v views of the "
+                                      f"conv output, zero initial state", kernel="chunk_prep + chunk_state",
+                             bound="mfma", avg_ms=round(ms, 4), algorithmic_flops=flops, achieved=round(tf, 2),
+                             peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(tf / PEAK_BF16_TFLOPS, 4),
+                             algorithmic_bytes=cb, hbm_gbps_algorithmic=round(cb / (ms * 1e-3) / 1e9, 1),
+                             tokens_per_s=round(T / (ms * 1e-3), 1))
+    del ws, y, q, k, v, g, beta
+    out = torch.empty((T, wl.nv, wl.dv), device=dev)
+    ms = _timed(lambda: gdn.gdn_gated_rmsnorm(o, x["z"], x["norm_w"], eps=1e-6, y=out, stream=stream),
+                reps, warmup, stream)
+    rows["gated_rmsnorm"] = _hbm_row(f"long_fused_t256k: {T * wl.nv} rows of {wl.dv}, x fp32, z bf16 -> y fp32", ms,
+                                     T * wl.nv * wl.dv * (4 + 2 + 4) + wl.dv * 4, "gated_rmsnorm_kernel")
+    del x, o, out, st
+    dw = W.WORKLOADS["decode_256seq"]
+    dx = {kk: vv.to(dev) for kk, vv in W.decode_inputs(dw).items()}
+    yd = torch.empty_like(dx["x"])
+    n, Cd = dx["x"].shape
+    ms = _timed(lambda: gdn.gdn_causal_conv1d_update(dx["x"], dx["conv_state"], dx["conv_w"], y=yd, stream=stream),
+                20 * reps, warmup, stream)
+    rows["causal_conv1d_update"] = _hbm_row(f"decode_256seq: x [{n}, {Cd}] bf16, conv state [{n}, {Cd}, 3] in place",
+                                            ms, n * Cd * (2 + 2 * 3 * 2 + 2) + Cd * 4 * 4, "conv_update_kernel")
+    torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(x, threads):
     import numpy as np
     import oracle
@@ -174,6 +252,9 @@ def main():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-mtp", action="store_true", help="skip the 1 + 3 token fused decode measurement")
+    ap.add_argument("--skip-rows", action="store_true", help="skip the per-row kernels on their own workloads")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="only the per-row kernels (one JSON line with them; used for their kernel trace)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with one plain 1 GiB device copy (counter calibration runs only)")
     args = ap.parse_args()
@@ -189,6 +270,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.rows_only:
+        print(json.dumps({"rows": time_rows(gdn, W, stream, dev)}), flush=True)
+        return
 
     # ---------------------------------------------------------------- prefill step
     wl = W.WORKLOADS["prefill_chunk_t8k"]
@@ -289,6 +373,8 @@ def main():
             decode_mtp = time_fused_decode(gdn, W, "decode_mtp_256x4", args.steps, args.warmup, stream, dev,
                                            tokens_per_seq=W.WORKLOADS["decode_mtp_256x4"].extra["tokens_per_seq"])
 
+    rows = None if args.skip_rows else time_rows(gdn, W, stream, dev)
+
     if args.calibrate_copy:   # known-size reference for the FETCH_SIZE / WRITE_SIZE counters
         src = torch.ones(1 << 28, device=dev, dtype=torch.float32)
         dst = torch.empty_like(src)
@@ -322,6 +408,7 @@ def main():
         "decode": decode,
         "decode_fused": decode_fused,
         "decode_mtp_fused": decode_mtp,
+        "rows": rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

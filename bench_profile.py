@@ -10,6 +10,7 @@ with tracing:
   2. --pmc FETCH_SIZE                          HBM read KiB per dispatch
   3. --pmc WRITE_SIZE                          HBM write KiB per dispatch
   4. --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA   MFMA work per dispatch
+  5. --kernel-trace --stats of bench.py --rows-only     the per-row kernels on their workloads
 The copy gives the calibration factors: true bytes / counter reading for a
 copy of known size, applied to every kernel's reading.
 
@@ -17,6 +18,7 @@ Writes
   profiles/bench_prefill_t8k_decode_256seq_kernel_stats.md
   profiles/hbm_traffic_prefill_t8k_decode_256seq.md   (its traffic_json line is
       read by bench.py, with the hash of the kernel sources it was taken on)
+  profiles/rows_long_prefill_t256k_decode_256seq_kernel_stats.md
 This process itself never touches the GPU.
 """
 from __future__ import annotations
@@ -27,6 +29,7 @@ import csv
 import glob
 import json
 import os
+import re
 import subprocess
 import sys
 
@@ -34,7 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402  (top level imports no GPU library)
 
-BENCH_ARGS = ["--steps", "200", "--warmup", "100", "--skip-cpu-baseline", "--skip-mtp", "--calibrate-copy"]
+BENCH_ARGS = ["--steps", "200", "--warmup", "100", "--skip-cpu-baseline", "--skip-mtp", "--skip-rows",
+              "--calibrate-copy"]
 COPY_BYTES = 1 << 30
 KERNELS = {  # what one call of each measured entry point launches (bf16 in, fp32 out); the
     # chunk table kernel runs only with cu_seqlens, so it is counted when present
@@ -53,18 +57,24 @@ PASSES = [  # name, rocprofv3 arguments
     ("fetch", ["--pmc", "FETCH_SIZE"]),
     ("write", ["--pmc", "WRITE_SIZE"]),
     ("mfma", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA"]),
+    ("rows", ["--kernel-trace", "--stats"]),     # bench.py --rows-only
 ]
+ROWS_SUMMARY = os.path.join(ROOT, "profiles", "rows_long_prefill_t256k_decode_256seq_kernel_stats.md")
+
+
+def bench_args(name):
+    return ["--rows-only"] if name == "rows" else BENCH_ARGS
 
 
 def pass_command(name, prof_args):
     return " ".join(["rocprofv3", *prof_args, "-f", "csv", "-d", f"<out>/{name}", "-o", name, "--",
-                     "python3", "bench.py", *BENCH_ARGS])
+                     "python3", "bench.py", *bench_args(name)])
 
 
 def run_pass(out, name, prof_args, timeout):
     d = os.path.join(out, name)
     cmd = ["rocprofv3", *prof_args, "-f", "csv", "-d", d, "-o", name, "--",
-           sys.executable, os.path.join(ROOT, "bench.py"), *BENCH_ARGS]
+           sys.executable, os.path.join(ROOT, "bench.py"), *bench_args(name)]
     print("[pass]", name, " ".join(cmd), flush=True)
     env = dict(os.environ, TMPDIR="/tmp")
     r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=timeout)
@@ -104,9 +114,42 @@ def avg(v):
     return sum(v) / len(v)
 
 
+def summarize_rows(out):
+    """Kernel trace of the per-row measurements: each row kernel launched on its own workload."""
+    d = os.path.join(out, "rows")
+    b = bench_line(out, "rows")["rows"]
+    ks = kernel_stats(d)
+    by_name = {r["Name"]: r for r in ks}
+    lines = ["# Kernel trace: the per-row kernels on their own workloads (bench.py --rows-only)", "",
+             "Long prefill T=262144 (16->64 heads, conv_dim 12288, bf16) for the conv, gating, chunk and",
+             "gated RMSNorm; the 256-sequence decode batch for the conv update. Command (from /tmp,",
+             "TMPDIR=/tmp; `python bench_profile.py run`, summarised by `python bench_profile.py summarize`):", "",
+             "    " + pass_command("rows", dict(PASSES)["rows"]), "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in sorted(ks, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", "Agreement with the HIP-event figures bench.py printed in the same run:", ""]
+    for row, key in (("causal_conv1d", "causal_conv1d_kernel"), ("gating", "gating_kernel"),
+                     ("gated_rmsnorm", "gated_rmsnorm_kernel"), ("causal_conv1d_update", "conv_update")):
+        names = [n for n in by_name if key in n]
+        avg_us = sum(float(by_name[n]["TotalDurationNs"]) for n in names) / max(1, sum(int(by_name[n]["Calls"]) for n in names)) / 1e3
+        kn = sorted({re.search(r"(\w+)<", n).group(1) for n in names})
+        lines.append(f"- {row}: trace average {avg_us:.1f} us over {', '.join(kn)}"
+                     f" (all its launches in the run); events {b[row]['avg_ms'] * 1e3:.1f} us, "
+                     f"{b[row]['achieved']:.0f} GB/s = {100 * b[row]['frac']:.1f} % of HBM peak")
+    c = b["chunk_fwd"]
+    lines.append(f"- chunk_fwd: events {c['avg_ms'] * 1e3:.1f} us per call, {c['achieved']:.1f} TFLOP/s algorithmic "
+                 f"({100 * c['frac']:.2f} % of the bf16 MFMA peak), {c['tokens_per_s'] / 1e6:.2f} M tokens/s")
+    lines += ["", "bench.py line of this run:", "", "    " + json.dumps({"rows": b}), ""]
+    with open(ROWS_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines))
+    print("[profile] wrote", ROWS_SUMMARY, flush=True)
+
+
 def summarize(out):
-    d1, d2, d3, d4 = (os.path.join(out, n) for n, _ in PASSES)
-    cmd1, cmd2, cmd3, cmd4 = (pass_command(n, a) for n, a in PASSES)
+    d1, d2, d3, d4 = (os.path.join(out, n) for n, _ in PASSES[:4])
+    cmd1, cmd2, cmd3, cmd4 = (pass_command(n, a) for n, a in PASSES[:4])
     b1 = bench_line(out, "ktrace")
 
     # ---- kernel trace
@@ -174,6 +217,7 @@ def summarize(out):
     with open(bench.TRAFFIC_SUMMARY, "w") as fh:
         fh.write("\n".join(lines))
     print("[profile] wrote", bench.TRAFFIC_SUMMARY, flush=True)
+    summarize_rows(out)
 
 
 def main():

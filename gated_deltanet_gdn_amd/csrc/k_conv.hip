@@ -26,8 +26,34 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int n_seqs, int64_t t
   return lo;
 }
 
+constexpr int UB = 1;        // tokens whose loads are issued together (more measured slower)
+
 template <typename T>
 __device__ __forceinline__ void load_vec(const T* p, float (&v)[CPT]) { load8(p, v); }
+
+// CPT elements as raw 16-byte words (1 for bf16, 2 for fp32), converted later
+__device__ __forceinline__ void load_raw(const uint16_t* p, uint4 (&r)[1]) { r[0] = *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void load_raw(const float* p, uint4 (&r)[2]) {
+  r[0] = *reinterpret_cast<const uint4*>(p);
+  r[1] = *reinterpret_cast<const uint4*>(p + 4);
+}
+__device__ __forceinline__ void unpack_raw(const uint4 (&r)[1], float (&v)[CPT]) {
+  const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack_raw(const uint4 (&r)[2], float (&v)[CPT]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v[4 * h] = __uint_as_float(r[h].x);
+    v[4 * h + 1] = __uint_as_float(r[h].y);
+    v[4 * h + 2] = __uint_as_float(r[h].z);
+    v[4 * h + 3] = __uint_as_float(r[h].w);
+  }
+}
 
 template <typename T>
 __device__ __forceinline__ void store_vec(T* p, const float (&v)[CPT]);
@@ -102,29 +128,41 @@ __global__ void __launch_bounds__(256) causal_conv1d_kernel(const T* __restrict_
     }
   }
 
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    if (t >= s_end) {  // next non-empty sequence starts at t
-      while (n + 1 < n_seqs && cu[n + 1] <= t) ++n;
-      seq_bounds(cu, n, T_tot, s_begin, s_end);
-      history_from_state(st_in, n, C, c0, state_len, win);
-    }
-    float xv[CPT];
-    load_vec(x + t * xs + c0, xv);
-    float out[CPT];
+  // UB tokens' inputs are loaded before any of them is used, so every wave
+  // keeps UB loads in flight (t is uniform over the workgroup: the branches
+  // below do not diverge)
+  for (int64_t tb = t_begin; tb < t_end; tb += UB) {
+    uint4 raw[UB][CPT * sizeof(T) / 16];
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      float acc = bs[e];
+    for (int u = 0; u < UB; ++u)
+      if (tb + u < t_end) load_raw(x + (tb + u) * xs + c0, raw[u]);
 #pragma unroll
-      for (int j = 0; j < KW - 1; ++j) acc = fmaf(wt[j][e], win[j][e], acc);
-      acc = fmaf(wt[KW - 1][e], xv[e], acc);
-      out[e] = silu ? siluf_(acc) : acc;
-    }
-    store_vec(y + t * static_cast<int64_t>(C) + c0, out);
+    for (int u = 0; u < UB; ++u) {
+      const int64_t t = tb + u;
+      if (t >= t_end) break;
+      if (t >= s_end) {  // next non-empty sequence starts at t
+        while (n + 1 < n_seqs && cu[n + 1] <= t) ++n;
+        seq_bounds(cu, n, T_tot, s_begin, s_end);
+        history_from_state(st_in, n, C, c0, state_len, win);
+      }
+      float xv[CPT];
+      unpack_raw(raw[u], xv);
+      float out[CPT];
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
+      for (int e = 0; e < CPT; ++e) {
+        float acc = bs[e];
 #pragma unroll
-      for (int j = 0; j < KW - 2; ++j) win[j][e] = win[j + 1][e];
-      win[KW - 2][e] = xv[e];
+        for (int j = 0; j < KW - 1; ++j) acc = fmaf(wt[j][e], win[j][e], acc);
+        acc = fmaf(wt[KW - 1][e], xv[e], acc);
+        out[e] = silu ? siluf_(acc) : acc;
+      }
+      store_vec(y + t * static_cast<int64_t>(C) + c0, out);
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+#pragma unroll
+        for (int j = 0; j < KW - 2; ++j) win[j][e] = win[j + 1][e];
+        win[KW - 2][e] = xv[e];
+      }
     }
   }
 }
@@ -173,6 +211,57 @@ __global__ void __launch_bounds__(256) conv_update_kernel(const T* __restrict__ 
   sp[state_len - 1] = xr;
 }
 
+// The same update for state_len == K - 1, one thread per (sequence, 8
+// channels): x, the 8 x 3 state entries (contiguous) and the 8 x 4 weights
+// move as 16-byte vectors. Same per-channel arithmetic as above.
+template <typename T>
+__global__ void __launch_bounds__(256) conv_update_vec_kernel(const T* __restrict__ x, T* __restrict__ st,
+                                                              const float* __restrict__ w,
+                                                              const float* __restrict__ bias, int64_t n_vec, int C,
+                                                              int silu, T* __restrict__ y) {
+  constexpr int SL = KW - 1;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // (sequence, 8 channels)
+  if (i >= n_vec) return;
+  const int64_t e0 = i * CPT;                  // first (sequence, channel) element
+  const int c0 = static_cast<int>(e0 % C);
+  float xv[CPT], sv[CPT * SL], wv[CPT * KW], bv[CPT];
+  load_vec(x + e0, xv);
+#pragma unroll
+  for (int q = 0; q < SL; ++q) {
+    float t8[CPT];
+    load_vec(st + e0 * SL + q * CPT, t8);
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) sv[q * CPT + e] = t8[e];
+  }
+#pragma unroll
+  for (int q = 0; q < CPT * KW / 4; ++q) {
+    const float4 f = *reinterpret_cast<const float4*>(w + static_cast<int64_t>(c0) * KW + 4 * q);
+    wv[4 * q] = f.x; wv[4 * q + 1] = f.y; wv[4 * q + 2] = f.z; wv[4 * q + 3] = f.w;
+  }
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) bv[e] = bias ? bias[c0 + e] : 0.0f;
+  float out[CPT], ns[CPT * SL];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+    float acc = bv[e];
+#pragma unroll
+    for (int j = 0; j < SL; ++j) acc = fmaf(wv[e * KW + j], sv[e * SL + j], acc);
+    acc = fmaf(wv[e * KW + KW - 1], xv[e], acc);
+    out[e] = silu ? siluf_(acc) : acc;
+#pragma unroll
+    for (int j = 0; j + 1 < SL; ++j) ns[e * SL + j] = sv[e * SL + j + 1];
+    ns[e * SL + SL - 1] = xv[e];
+  }
+  store_vec(y + e0, out);
+#pragma unroll
+  for (int q = 0; q < SL; ++q) {
+    float t8[CPT];
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) t8[e] = ns[q * CPT + e];
+    store_vec(st + e0 * SL + q * CPT, t8);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_causal_conv1d(const void* x, int bf16, int64_t x_stride, const float* w, const float* bias,
@@ -210,6 +299,20 @@ hipError_t launch_causal_conv1d(const void* x, int bf16, int64_t x_stride, const
 hipError_t launch_causal_conv1d_update(const void* x, int bf16, void* state, int state_len, const float* w,
                                        const float* bias, int n_seqs, int C, int silu, void* y, hipStream_t s) {
   const int64_t units = static_cast<int64_t>(n_seqs) * C;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(state) |
+                       reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(w);
+  if (state_len == KW - 1 && C % CPT == 0 && (al & 15) == 0) {
+    const int64_t nvec = units / CPT;
+    const dim3 grid(static_cast<unsigned>((nvec + 255) / 256));
+    if (bf16)
+      conv_update_vec_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x),
+                                                            static_cast<uint16_t*>(state), w, bias, nvec, C, silu,
+                                                            static_cast<uint16_t*>(y));
+    else
+      conv_update_vec_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), static_cast<float*>(state), w,
+                                                         bias, nvec, C, silu, static_cast<float*>(y));
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((units + 255) / 256));
   if (bf16)
     conv_update_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x),

@@ -289,7 +289,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
     // gating, as the separate gating kernel computes it
     const float av = Elem<T>::cvt(a_n), bv = Elem<T>::cvt(b_n);
     if (t + 1 < t1) { a_n = a[(t + 1) * nv + h]; b_n = b[(t + 1) * nv + h]; }
-    const float gt = -expf(alog) * softplusf_(av + dtb);
+    const float gt = -exp_(alog) * softplusf_(av + dtb);
     const float bt = sigmoidf_(bv);
     __syncthreads();
     const float4 v4 = *reinterpret_cast<const float4*>(&kqv_s[par][2 * D + rho * D + col]);

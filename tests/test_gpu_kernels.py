@@ -34,9 +34,10 @@ def _to(d, device):
 # ------------------------------------------------------------------ gating
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_gating(dtype):
-    _say("gating", dtype)
-    x = _inputs(dtype, [300], 2, 6)
+@pytest.mark.parametrize("nk,nv", [(2, 6), (1, 4), (3, 12), (4, 32)])   # one, four or eight heads per thread
+def test_gating(dtype, nk, nv):
+    _say("gating", dtype, nk, nv)
+    x = _inputs(dtype, [300], nk, nv)
     d = _to(x, dev())
     g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
     torch.cuda.synchronize()
@@ -44,6 +45,20 @@ def test_gating(dtype):
     # fp32 evaluation of exp / log1p / sigmoid: a few ulps of the result
     np.testing.assert_allclose(f64(g), g_ref, rtol=4e-6, atol=0)
     np.testing.assert_allclose(f64(beta), b_ref, rtol=4e-6, atol=0)
+
+
+def test_gating_unaligned_views():
+    _say("gating on views that start one token in (not 16-byte aligned)")
+    x = _inputs("bf16", [101], 1, 8)
+    d = _to(x, dev())
+    a, b = d["a"][1:], d["b"][1:]                        # 16 bytes in for bf16 x 8 heads: aligned
+    a2 = torch.empty((a.shape[0] * 8 + 1,), device=a.device, dtype=a.dtype)[1:].view(a.shape)
+    a2.copy_(a)                                           # 2 bytes off a 16-byte boundary
+    g2 = torch.empty((a.shape[0] * 8 + 1,), device=a.device)[1:].view(a.shape)
+    g, beta = gdn.gdn_gating(a2, b, d["A_log"], d["dt_bias"], g=g2)
+    g_ref, b_ref = oracle.gating(f64(x["a"][1:]), f64(x["b"][1:]), f64(x["A_log"]), f64(x["dt_bias"]))
+    np.testing.assert_allclose(f64(g), g_ref, rtol=4e-6)
+    np.testing.assert_allclose(f64(beta), b_ref, rtol=4e-6)
 
 
 def test_gating_odd_head_count():
@@ -124,10 +139,10 @@ def test_causal_conv1d_strided_view_and_long_state():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("state_len", [3, 4])
-def test_causal_conv1d_update(dtype, state_len):
-    _say("conv update", dtype, state_len)
-    n, C = 37, 200
+@pytest.mark.parametrize("state_len,C", [(3, 200), (4, 200), (3, 36)])   # 8-channel vector path when C % 8 == 0
+def test_causal_conv1d_update(dtype, state_len, C):
+    _say("conv update", dtype, state_len, C)
+    n = 37
     x = W.randn((n, C), 8, 1, dtype)
     st = W.randn((n, C, state_len), 8, 2, dtype)
     w = W.uniform((C, 4), 8, 3, -0.5, 0.5)
