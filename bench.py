@@ -80,10 +80,11 @@ def chunk_flops_per_token_head(C=64, dk=128, dv=128, r=2):
     return 2 * ((2 / r) * C * dk + C * (dk + 2 * dv) + 3 * dk * dv)
 
 
-def chunk_bytes(T, nk, nv, dk=128, dv=128, n_seqs=1, in_bytes=2, o_bytes=4, state_in=False):
-    """Algorithmic HBM bytes of one chunk_fwd call (inputs read once, outputs written once)."""
+def chunk_bytes(T, nk, nv, dk=128, dv=128, n_seqs=1, in_bytes=2, o_bytes=4, state_in=False, gate_bytes=8):
+    """Algorithmic HBM bytes of one chunk_fwd call (inputs read once, outputs written once); gate_bytes per
+    (token, head): 8 for fp32 g and beta, 4 for bf16 a and b when the gating is folded in."""
     b = T * nk * dk * in_bytes * 2 + T * nv * dv * in_bytes      # q, k, v
-    b += T * nv * 4 * 2                                          # g, beta
+    b += T * nv * gate_bytes                                     # g, beta (or a, b)
     b += T * nv * dv * o_bytes                                   # o
     b += n_seqs * nv * dk * dv * 4 * (2 if state_in else 1)      # final (+ initial) state
     return b
@@ -128,12 +129,15 @@ def time_fused_decode(gdn, W, name, steps, warmup, stream, dev, tokens_per_seq=N
     for _ in range(warmup):
         fstep()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
+    for _ in range(steps):
+        fstep()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         fstep(evs[i])
     torch.cuda.synchronize()
-    step_ms = (time.perf_counter() - t0) * 1e3 / steps
     k_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     nbytes = fused_decode_bytes(n_tok, n, wl.nk, wl.nv, state_len=wl.state_len)
     gbps = nbytes / (k_ms * 1e-3) / 1e9
@@ -146,14 +150,32 @@ def time_fused_decode(gdn, W, name, steps, warmup, stream, dev, tokens_per_seq=N
                               avg_ms=round(k_ms, 4), algorithmic_bytes=nbytes))
 
 
-def _timed(fn, reps, warmup, stream):
+def _timed(fn, reps, warmup, stream, graph=False):
     """Average ms per call of fn(): one pair of HIP events on its stream around reps back-to-back calls
-    (warm-up calls first), so that a short kernel is not charged the per-event overhead."""
+    (warm-up calls first), so that a short kernel is not charged the per-event overhead. With graph=True
+    the reps calls are captured once in a device graph and replayed between the events, so that a kernel
+    shorter than its host-side launch is timed on the GPU, not at the launch rate."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side), torch.cuda.graph(gr, stream=side):
+            for _ in range(reps):
+                fn(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        gr.replay()                     # first replay outside the timed pair
+        torch.cuda.synchronize()
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
     e0.record(stream)
     for _ in range(reps):
         fn()
@@ -185,8 +207,9 @@ def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
     y, _ = gdn.gdn_causal_conv1d(x["x"], x["conv_w"], state_len=wl.state_len, stream=stream)
     g = torch.empty((T, wl.nv), device=dev)
     beta = torch.empty_like(g)
-    ms = _timed(lambda: gdn.gdn_gating(x["a"], x["b"], x["A_log"], x["dt_bias"], g=g, beta=beta, stream=stream),
-                4 * reps, warmup, stream)
+    ms = _timed(lambda st=stream: gdn.gdn_gating(x["a"], x["b"], x["A_log"], x["dt_bias"], g=g, beta=beta,
+                                                 stream=st),
+                4 * reps, warmup, stream, graph=True)
     rows["gating"] = _hbm_row(f"long_fused_t256k: a, b [{T}, {wl.nv}] bf16 -> g, beta fp32", ms,
                               T * wl.nv * 12 + wl.nv * 8, "gating_kernel")
     q, k, v = y[:, :kd].view(T, wl.nk, wl.dk), y[:, kd:2 * kd].view(T, wl.nk, wl.dk), y[:, 2 * kd:].view(T, wl.nv, wl.dv)
@@ -216,8 +239,9 @@ def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
     dx = {kk: vv.to(dev) for kk, vv in W.decode_inputs(dw).items()}
     yd = torch.empty_like(dx["x"])
     n, Cd = dx["x"].shape
-    ms = _timed(lambda: gdn.gdn_causal_conv1d_update(dx["x"], dx["conv_state"], dx["conv_w"], y=yd, stream=stream),
-                20 * reps, warmup, stream)
+    ms = _timed(lambda st=stream: gdn.gdn_causal_conv1d_update(dx["x"], dx["conv_state"], dx["conv_w"], y=yd,
+                                                                stream=st),
+                20 * reps, warmup, stream, graph=True)
     rows["causal_conv1d_update"] = _hbm_row(f"decode_256seq: x [{n}, {Cd}] bf16, conv state [{n}, {Cd}, 3] in place",
                                             ms, n * Cd * (2 + 2 * 3 * 2 + 2) + Cd * 4 * 4, "conv_update_kernel")
     torch.cuda.empty_cache()
@@ -285,31 +309,53 @@ def main():
     st = torch.empty((1, wl.nv, wl.dk, wl.dv), device=dev, dtype=torch.float32)
     ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(T, 1, wl.nk, wl.nv), device=dev, dtype=torch.uint8)
 
+    # one step = gating + the chunked rule, as one call with the gating folded into the chunk preparation
+    # (bit for bit the same as gdn_gating followed by gdn_chunk_fwd, which is timed below for reference)
     def step(ev=None):
-        gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], g=g, beta=beta, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, final_state=st, o=o, workspace=ws, stream=stream)
+        gdn.gdn_chunk_fwd_gated(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], final_state=st,
+                                o=o, workspace=ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
+    def step_separate():
+        gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], g=g, beta=beta, stream=stream)
+        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, final_state=st, o=o, workspace=ws, stream=stream)
+
+    # timed region: K steps between synchronisations, nothing else in the stream
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / args.steps
+    # the kernel time: HIP events on the launch stream around every call of K more steps (the event
+    # records add a few microseconds of stream gaps, so they stay out of the timed region above)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     chunk_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    # the same step as two calls (gating, then the chunk rule), for reference
+    for _ in range(max(10, args.warmup // 4)):
+        step_separate()
+    torch.cuda.synchronize()
+    t_sep = time.perf_counter()
+    for _ in range(args.steps):
+        step_separate()
+    torch.cuda.synchronize()
+    ms_separate = (time.perf_counter() - t_sep) * 1e3 / args.steps
 
     r = wl.nv // wl.nk
     flops = chunk_flops_per_token_head(r=r) * T * wl.nv
-    cbytes = chunk_bytes(T, wl.nk, wl.nv)
+    cbytes = chunk_bytes(T, wl.nk, wl.nv, gate_bytes=4)
     achieved_tflops = flops / (chunk_ms * 1e-3) / 1e12
-    roofline = dict(bound="mfma", kernel="gdn_chunk_fwd (chunk_prep + chunk_state launches)",
+    roofline = dict(bound="mfma", kernel="gdn_chunk_fwd_gated (chunk_prep with the gating + chunk_state launches)",
                     achieved=round(achieved_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("chunk"),
                     avg_ms=round(chunk_ms, 4), algorithmic_flops=flops, algorithmic_bytes=cbytes,
@@ -348,13 +394,16 @@ def main():
         for _ in range(args.warmup):
             dstep()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dstep()
+        torch.cuda.synchronize()
+        dstep_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.steps)]
-        t0 = time.perf_counter()
         for i in range(args.steps):
             dstep(devs[i])
         torch.cuda.synchronize()
-        dstep_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         rec_ms = sum(a.elapsed_time(b) for a, b in devs) / args.steps
         rbytes = recurrent_bytes(n, dw.nk, dw.nv)
         gbps = rbytes / (rec_ms * 1e-3) / 1e9
@@ -396,13 +445,14 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_separate_gating": round(ms_separate, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k,v,a,b ~ N(0,1) bf16, A_log = log U[1,16], dt_bias ~ N(0,0.1))",
         "config": {"workload": "prefill_chunk_t8k: B=1, T=8192, 16 key heads -> 32 value heads, Dk=Dv=128, "
-                               "chunk 64, zero initial state, fp32 output + final state",
+                               "chunk 64, zero initial state, gating + chunked rule, fp32 output + final state",
                    "global_batch": 1, "seq_len": T, "parallelism": "single GPU"},
         "roofline": roofline,
         "decode": decode,

@@ -42,7 +42,7 @@ BENCH_ARGS = ["--steps", "200", "--warmup", "100", "--skip-cpu-baseline", "--ski
 COPY_BYTES = 1 << 30
 KERNELS = {  # what one call of each measured entry point launches (bf16 in, fp32 out); the
     # chunk table kernel runs only with cu_seqlens, so it is counted when present
-    "chunk": ["chunk_offsets_kernel?", "chunk_prep_kernel<unsigned short>", "chunk_state_bf16_kernel<float>"],
+    "chunk": ["chunk_offsets_kernel?", "chunk_prep_kernel<unsigned short, 1>", "chunk_state_bf16_kernel<float>"],
     "recurrent": ["recurrent_kernel<unsigned short, float"],
     "fused": ["decode_fused_kernel<unsigned short, float"],
 }
@@ -167,7 +167,7 @@ def summarize(out):
     rec_avg = float(by_name[pick(by_name, KERNELS["recurrent"][0])]["AverageNs"]) / 1e3
     fus_avg = float(by_name[pick(by_name, KERNELS["fused"][0])]["AverageNs"]) / 1e3
     lines += ["", "Agreement with the HIP-event figures bench.py printed in the same run:", "",
-              f"- gdn_chunk_fwd = {' + '.join(k.split('<')[0] for k in chunk_names)}: sum of averages {chunk_sum:.1f} us; "
+              f"- gdn_chunk_fwd_gated = {' + '.join(k.split('<')[0] for k in chunk_names)}: sum of averages {chunk_sum:.1f} us; "
               f"events {b1['roofline']['avg_ms'] * 1e3:.1f} us per call",
               f"- recurrent_kernel: average {rec_avg:.1f} us; events {b1['decode']['roofline']['avg_ms'] * 1e3:.1f} us",
               f"- decode_fused_kernel: average {fus_avg:.1f} us; events "
@@ -203,8 +203,8 @@ def summarize(out):
              f"- FETCH_SIZE read {copy_f:.1f} KiB for {COPY_BYTES // 1024} KiB: read bytes = {kf:.4f} x 1024 x FETCH_SIZE",
              f"- WRITE_SIZE read {copy_w:.1f} KiB for {COPY_BYTES // 1024} KiB: write bytes = {kw:.4f} x 1024 x WRITE_SIZE",
              "", *rows, "",
-             f"- gdn_chunk_fwd (all its launches): {rec['chunk']['bytes_per_call'] / 1e6:.1f} MB per call "
-             f"(algorithmic {bench.chunk_bytes(8192, 16, 32) / 1e6:.1f} MB); MFMA work "
+             f"- gdn_chunk_fwd_gated (all its launches): {rec['chunk']['bytes_per_call'] / 1e6:.1f} MB per call "
+             f"(algorithmic {bench.chunk_bytes(8192, 16, 32, gate_bytes=4) / 1e6:.1f} MB); MFMA work "
              f"{rec['chunk']['mfma_flops_per_call'] / 1e9:.2f} GFLOP executed (hi/lo passes included) vs "
              f"{bench.chunk_flops_per_token_head() * 8192 * 32 / 1e9:.2f} GFLOP algorithmic",
              f"- recurrent_kernel: {rec['recurrent']['bytes_per_call'] / 1e6:.1f} MB per call "

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "GdnError", "lib", "F32", "BF16",
     "gdn_abi_version", "gdn_status_string", "gdn_last_error",
-    "gdn_gating", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_recurrent_fwd",
+    "gdn_gating", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_recurrent_fwd",
     "gdn_causal_conv1d", "gdn_causal_conv1d_update", "gdn_gated_rmsnorm", "gdn_decode_step_fused",
 ]
 
@@ -52,6 +52,8 @@ def lib():
         "gdn_chunk_fwd_workspace_size": (sz, [i64, i32, i32, i32, i32, i32, i32]),
         "gdn_chunk_fwd": (i32, [vp, vp, vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                 f32, i32, vp, vp, vp, i32, vp, sz, vp]),
+        "gdn_chunk_fwd_gated": (i32, [vp, vp, vp, i32, i64, i64, i64, vp, vp, i32, vp, vp, vp, i32, i64, i32, i32,
+                                      i32, i32, f32, i32, vp, vp, vp, i32, vp, sz, vp]),
         "gdn_recurrent_fwd": (i32, [vp, vp, vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                     f32, i32, vp, vp, i32, vp]),
         "gdn_causal_conv1d": (i32, [vp, i32, i64, vp, vp, vp, i32, i64, i32, i32, vp, vp, i32, i32, vp, vp]),
@@ -175,6 +177,37 @@ def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_
                              _ptr(initial_state), _ptr(final_state), _ptr(o), _dt(o, "o"),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("gdn_chunk_fwd", st)
+    return o, final_state
+
+
+def gdn_chunk_fwd_gated(q, k, v, a, b, A_log, dt_bias, cu_seqlens=None, initial_state=None,
+                        output_final_state=True, final_state=None, o=None, o_dtype=torch.float32, scale=None,
+                        qk_l2norm=True, workspace=None, stream=None):
+    """gdn_chunk_fwd with the gating folded in: a, b [T, nv] (raw) and A_log, dt_bias [nv] fp32 in place
+    of g and beta. Returns (o, final_state) like gdn_chunk_fwd."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, contiguous=False)
+    qs, ks, vs = _tok_view(q, "q"), _tok_view(k, "k"), _tok_view(v, "v")
+    _need(a, "a"); _need(b, "b", a.dtype)
+    _need(A_log, "A_log", torch.float32); _need(dt_bias, "dt_bias", torch.float32)
+    T, nk, dk = q.shape
+    nv, dv = v.shape[1], v.shape[2]
+    cu, n = _cu(cu_seqlens, T)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, nv, dk, dv), device=q.device, dtype=torch.float32)
+    if o is None:
+        o = torch.empty((T, nv, dv), device=q.device, dtype=o_dtype)
+    need = gdn_chunk_fwd_workspace_size(T, n, nk, nv, dk, dv, _dt(q, "q"))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    st = lib().gdn_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _dt(q, "q"), qs, ks, vs, _ptr(a), _ptr(b),
+                                   _dt(a, "a"), _ptr(A_log), _ptr(dt_bias), _ptr(cu), n, T, nk, nv, dk, dv,
+                                   float(scale or 0.0), int(bool(qk_l2norm)), _ptr(initial_state),
+                                   _ptr(final_state), _ptr(o), _dt(o, "o"), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gdn_chunk_fwd_gated", st)
     return o, final_state
 
 

@@ -130,9 +130,38 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype, int
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
-  return launched(gdn::launch_chunk_fwd(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, g, beta, cu_seqlens, n_seqs, T_tot,
-                                        nk, nv, scale, qk_l2norm != 0, initial_state, final_state, o,
-                                        o_dtype == GDN_BF16, workspace, static_cast<hipStream_t>(stream)),
+  return launched(gdn::launch_chunk_fwd(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, g, beta, 0, nullptr, nullptr,
+                                        cu_seqlens, n_seqs, T_tot, nk, nv, scale, qk_l2norm != 0, initial_state,
+                                        final_state, o, o_dtype == GDN_BF16, workspace,
+                                        static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtype, int64_t q_tok_stride,
+                        int64_t k_tok_stride, int64_t v_tok_stride, const void* a, const void* b, int ab_dtype,
+                        const float* A_log, const float* dt_bias, const int32_t* cu_seqlens, int n_seqs,
+                        int64_t T_tot, int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                        const float* initial_state, float* final_state, void* o, int o_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_chunk_fwd_gated";
+  int64_t qs = q_tok_stride, ks = k_tok_stride, vs = v_tok_stride;
+  if (!valid_dtype(ab_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: ab_dtype %d is not f32/bf16", fn, ab_dtype);
+  // a and b stand where g and beta stand in the shared checks
+  const int st = check_core(fn, q, k, v, in_dtype, qs, ks, vs, static_cast<const float*>(a),
+                            static_cast<const float*>(b), n_seqs, T_tot, nk, nv, dk, dv, o, o_dtype);
+  if (st != GDN_OK) return st;
+  if (!A_log || !dt_bias) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: A_log and dt_bias are required", fn);
+  if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
+  if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, in_dtype == GDN_BF16);
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
+  return launched(gdn::launch_chunk_fwd(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, a, b, ab_dtype == GDN_BF16 ? 1 : 2,
+                                        A_log, dt_bias, cu_seqlens, n_seqs, T_tot, nk, nv, scale, qk_l2norm != 0,
+                                        initial_state, final_state, o, o_dtype == GDN_BF16, workspace,
+                                        static_cast<hipStream_t>(stream)),
                   fn);
 }
 

@@ -44,10 +44,12 @@ hipError_t launch_decode_fused(const void* x, int bf16, int64_t x_stride, void* 
 // diagonal] and the per-token scalars, and for bf16 inputs per chunk and key
 // head the K and Q operand tiles; see k_chunk.hip.
 size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nk, int nv, int bf16);
+// Gating inputs: gm = 0: ga, gb are g and beta (fp32); gm = 1 / 2: ga, gb are
+// the raw a and b (bf16 / fp32), gated inside the prep kernel with A_log, dt_bias.
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf16,
-                            int64_t qs, int64_t ks, int64_t vs, const float* g, const float* beta,
-                            const int32_t* cu, int n_seqs, int64_t T, int nk, int nv, float scale,
-                            int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
-                            hipStream_t s);
+                            int64_t qs, int64_t ks, int64_t vs, const void* ga, const void* gb, int gm,
+                            const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs,
+                            int64_t T, int nk, int nv, float scale, int l2, const float* S0, float* ST,
+                            void* o, int o_bf16, void* ws, hipStream_t s);
 
 }  // namespace gdn

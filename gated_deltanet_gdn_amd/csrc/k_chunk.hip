@@ -290,10 +290,14 @@ constexpr int PREP_WAVES = 4;
 
 // (at most 128 VGPRs: four waves per SIMD, i.e. four blocks per CU, which is
 // also what the LDS holds)
-template <typename TIn>
+// GM selects the per-token gating inputs: 0 = g and beta (fp32) given;
+// 1 / 2 = the raw a and b (bf16 / fp32), gated here exactly as the separate
+// gating kernel does (same expressions), so both routes give the same bits.
+template <typename TIn, int GM>
 __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_per_eu(4))) chunk_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t qs, int64_t ks,
-    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    const void* __restrict__ ga, const void* __restrict__ gb, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, const int32_t* __restrict__ cu,
     int n_seqs, int64_t T, int nk, int nv, float scale, int l2, const int32_t* __restrict__ chunk_off,
     float* __restrict__ tp, float4* __restrict__ sc, float* __restrict__ egc, uint16_t* __restrict__ kf,
     uint16_t* __restrict__ qf) {
@@ -331,10 +335,12 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // per-token g and beta (wave 0, lane = token), issued first so their
+  // per-token gating inputs (wave 0, lane = token), issued first so their
   // latency overlaps the tile loads and the Grams
-  const float g_ld = g[(t0 + min(lane, L - 1)) * nv + h];
-  const float b_ld = beta[(t0 + min(lane, L - 1)) * nv + h];
+  using TA = std::conditional_t<GM == 1, uint16_t, float>;
+  const int64_t gi = (t0 + min(lane, L - 1)) * nv + h;
+  const TA ga_ld = static_cast<const TA*>(ga)[gi];
+  const TA gb_ld = static_cast<const TA*>(gb)[gi];
 
   // 1. K and Q tiles into LDS; rows past the sequence end re-read the last
   //    valid row: their norms are forced to 0 below, so they contribute
@@ -415,6 +421,14 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   // 5. chunk-local cumulative decay in fp64 (wave 0, lane = token)
   if (wv == 0) {
     const bool valid = lane < L;
+    float g_ld, b_ld;
+    if constexpr (GM == 0) {
+      g_ld = ga_ld;
+      b_ld = gb_ld;
+    } else {
+      g_ld = -exp_(A_log[h]) * softplusf_(Elem<TA>::cvt(ga_ld) + dt_bias[h]);
+      b_ld = sigmoidf_(Elem<TA>::cvt(gb_ld));
+    }
     double G = valid ? g_ld : 0.0f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1235,7 +1249,8 @@ constexpr size_t generic_lds_bytes() {
 
 template <typename TIn>
 hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
-                          const float* g, const float* beta, const int32_t* cu, int n_seqs, int64_t T, int nk,
+                          const void* ga, const void* gb, int gm, const float* A_log, const float* dt_bias,
+                          const int32_t* cu, int n_seqs, int64_t T, int nk,
                           int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
                           hipStream_t s) {
   constexpr bool BF = sizeof(TIn) == 2;
@@ -1256,14 +1271,14 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     if (e != hipSuccess) return e;
   }
   {
-    auto kern = chunk_prep_kernel<TIn>;
+    auto kern = gm == 1 ? chunk_prep_kernel<TIn, 1> : gm == 2 ? chunk_prep_kernel<TIn, 2> : chunk_prep_kernel<TIn, 0>;
     const size_t lds = prep_lds_bytes<TIn>();
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
     kern<<<dim3(static_cast<unsigned>(nv), static_cast<unsigned>(nch)), 64 * PREP_WAVES, lds, s>>>(
-        static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, g, beta, cu, n_seqs, T, nk, nv, scale, l2,
-        chunk_off, tp, sc, egc, kf, qf);
+        static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, ga, gb, A_log, dt_bias, cu, n_seqs, T, nk, nv,
+        scale, l2, chunk_off, tp, sc, egc, kf, qf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1301,14 +1316,15 @@ size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nk, int nv, int bf16) {
 }
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf16, int64_t qs, int64_t ks,
-                            int64_t vs, const float* g, const float* beta, const int32_t* cu, int n_seqs,
-                            int64_t T, int nk, int nv, float scale, int l2, const float* S0, float* ST, void* o,
-                            int o_bf16, void* ws, hipStream_t s) {
+                            int64_t vs, const void* ga, const void* gb, int gm, const float* A_log,
+                            const float* dt_bias, const int32_t* cu, int n_seqs, int64_t T, int nk, int nv,
+                            float scale, int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
+                            hipStream_t s) {
   if (bf16)
-    return chunk_dispatch<uint16_t>(q, k, v, qs, ks, vs, g, beta, cu, n_seqs, T, nk, nv, scale, l2, S0, ST, o,
-                                    o_bf16, ws, s);
-  return chunk_dispatch<float>(q, k, v, qs, ks, vs, g, beta, cu, n_seqs, T, nk, nv, scale, l2, S0, ST, o, o_bf16,
-                               ws, s);
+    return chunk_dispatch<uint16_t>(q, k, v, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2,
+                                    S0, ST, o, o_bf16, ws, s);
+  return chunk_dispatch<float>(q, k, v, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2, S0,
+                               ST, o, o_bf16, ws, s);
 }
 
 }  // namespace gdn

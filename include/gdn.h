@@ -110,6 +110,27 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_chunk_fwd with the gating folded in: takes the raw a and b ([T_tot, nv]
+ * of ab_dtype, dense) with A_log and dt_bias ([nv] fp32) where gdn_chunk_fwd
+ * takes g and beta, and computes g and beta as gdn_gating does, inside the
+ * chunk preparation ("Qwen3.5 Dense Model Architecture", Linear Attention:
+ * the beta and g lines of the minimal example feed the chunk rule directly;
+ * "Qwen3.5 Simulation Support Design Document", 2.2 ops 3 and 4). One launch
+ * fewer and no g/beta round trip; the results are bit for bit those of
+ * gdn_gating followed by gdn_chunk_fwd. All other arguments, the workspace
+ * size and the supported shapes are those of gdn_chunk_fwd.
+ */
+int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtype,
+                        int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                        const void* a, const void* b, int ab_dtype,
+                        const float* A_log, const float* dt_bias,
+                        const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                        int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                        const float* initial_state, float* final_state,
+                        void* o, int o_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Recurrent gated delta rule, the decode path ("Qwen3.5 Simulation Support
  * Design Document", 2.2 op 5 and 2.3: decode batches, including multi-token
  * MTP decode, take the token-by-token path; "Qwen3.5 Dense Model

@@ -225,3 +225,31 @@ def test_decode_step_fused_empty_batch_needs_no_inputs(L):
     # no tokens: x, a, b and o may be NULL; the call is still a valid (state-preserving) launch
     # request, so only argument checks run here -- with T = 0 and cu_seqlens NULL it must fail
     assert _fused(L, T=0, x=NULL, a=NULL, b=NULL, o=NULL) == INVALID
+
+
+def _gated(L, **kw):
+    a = dict(q=P, k=P, v=P, in_dtype=1, qs=0, ks=0, vs=0, a=P, b=P, ab_dtype=1, alog=P, dtb=P, cu=NULL, n=1, T=256,
+             nk=1, nv=2, dk=128, dv=128, scale=0.0, l2=1, s0=NULL, st=NULL, o=P, o_dtype=0, ws=P2, ws_bytes=1 << 40,
+             stream=NULL)
+    a.update(kw)
+    return L.gdn_chunk_fwd_gated(a["q"], a["k"], a["v"], a["in_dtype"], a["qs"], a["ks"], a["vs"], a["a"], a["b"],
+                                 a["ab_dtype"], a["alog"], a["dtb"], a["cu"], a["n"], a["T"], a["nk"], a["nv"],
+                                 a["dk"], a["dv"], a["scale"], a["l2"], a["s0"], a["st"], a["o"], a["o_dtype"],
+                                 a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ab_dtype=4), INVALID),
+    (dict(a=NULL), INVALID),
+    (dict(b=NULL), INVALID),
+    (dict(alog=NULL), INVALID),
+    (dict(dtb=NULL), INVALID),
+    (dict(nk=3, nv=4), INVALID),
+    (dict(n=2), INVALID),
+    (dict(ws=NULL), INVALID),
+    (dict(ws_bytes=16), WS_SMALL),
+    (dict(dk=64), UNSUPPORTED),
+])
+def test_chunk_fwd_gated_argument_errors(L, kw, status):
+    assert _gated(L, **kw) == status
+    assert gdn.gdn_last_error() != ""

@@ -195,6 +195,23 @@ def test_recurrent_multi_token_varlen(dtype):
     assert_close(state, S_ref, TOL[dtype], "recurrent varlen state")
 
 
+# ------------------------------------------------------------------ chunk with the gating folded in
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lengths,nk,nv", [([200], 2, 4), ([1, 63, 64, 65, 130, 0, 7], 1, 2), ([300], 1, 4)])
+def test_chunk_fwd_gated_equals_gating_then_chunk(dtype, lengths, nk, nv):
+    _say("chunk with gating folded in", dtype, lengths, nk, nv)
+    x = _inputs(dtype, lengths, nk, nv, s0_std=0.5)
+    d = _to(x, dev())
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    o1, s1 = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, cu_seqlens=d["cu_seqlens"], initial_state=d["S0"])
+    o2, s2 = gdn.gdn_chunk_fwd_gated(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                     cu_seqlens=d["cu_seqlens"], initial_state=d["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), f"o differs by {(o1 - o2).abs().max().item():.3e}"
+    assert torch.equal(s1, s2), f"state differs by {(s1 - s2).abs().max().item():.3e}"
+
+
 # ------------------------------------------------------------------ chunk (prefill)
 
 def _run_chunk(x, dtype, with_s0=True, alias=False, o_dtype=torch.float32):
@@ -309,3 +326,42 @@ def test_chunk_reset_and_orthonormal_keys():
                               qk_l2norm=False)
     assert_close(o[:, 0], f64(v)[:, 0], TOL["f32"], "orthonormal read-back")
     assert_close(keys[:, 0].double().numpy() @ f64(fs)[0, 0], f64(v)[:, 0], TOL["f32"], "values retrievable")
+
+
+# ------------------------------------------------------------------ device graphs of the small kernels
+
+def test_gating_and_conv_update_in_a_device_graph():
+    """The bench times these two short kernels as captured graph replays: every replay (with eager work and
+    syncs in between) must equal the eager calls on the same buffers."""
+    _say("gating + conv update captured in a graph")
+    d = dev()
+    x = _to(_inputs("bf16", [96], 2, 8), d)
+    n, C = 16, 256
+    xc = W.randn((n, C), 9, 1, "bf16").to(d)
+    w = W.uniform((C, 4), 9, 2, -0.5, 0.5).to(d)
+    cs_g = W.randn((n, C, 3), 9, 3, "bf16").to(d)
+    cs_e = cs_g.clone()
+    g_g, b_g = torch.empty((96, 8), device=d), torch.empty((96, 8), device=d)
+    y_g = torch.empty_like(xc)
+
+    def calls(cs, g, b, y, stream=None):
+        gdn.gdn_gating(x["a"], x["b"], x["A_log"], x["dt_bias"], g=g, beta=b, stream=stream)
+        gdn.gdn_causal_conv1d_update(xc, cs, w, y=y, stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side), torch.cuda.graph(graph, stream=side):
+        calls(cs_g, g_g, b_g, y_g, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g_e, b_e, y_e = torch.empty_like(g_g), torch.empty_like(b_g), torch.empty_like(y_g)
+        calls(cs_e, g_e, b_e, y_e)
+        filler = torch.randn(1 << 20, device=d).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(filler)
+        for a, b, nm in ((g_g, g_e, "g"), (b_g, b_e, "beta"), (y_g, y_e, "conv y"), (cs_g, cs_e, "conv state")):
+            assert torch.equal(a, b), f"replay {rep}: {nm} differs from the eager call"
