@@ -229,6 +229,28 @@ def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
                              algorithmic_bytes=cb, hbm_gbps_algorithmic=round(cb / (ms * 1e-3) / 1e9, 1),
                              tokens_per_s=round(T / (ms * 1e-3), 1))
     del ws, y, q, k, v, g, beta
+    # the varlen prefill batch: 8 packed sequences with nonzero initial states, gating folded in
+    vw = W.WORKLOADS["varlen_prefill_8seq"]
+    vx = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in W.chunk_inputs(vw).items()}
+    Tv, nseq = int(vx["cu_seqlens"][-1].item()), len(vx["lengths"])
+    vo = torch.empty((Tv, vw.nv, vw.dv), device=dev)
+    vst = torch.empty((nseq, vw.nv, vw.dk, vw.dv), device=dev)
+    vws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(Tv, nseq, vw.nk, vw.nv), device=dev, dtype=torch.uint8)
+    ms = _timed(lambda: gdn.gdn_chunk_fwd_gated(vx["q"], vx["k"], vx["v"], vx["a"], vx["b"], vx["A_log"], vx["dt_bias"],
+                                                cu_seqlens=vx["cu_seqlens"], initial_state=vx["S0"], final_state=vst,
+                                                o=vo, workspace=vws, stream=stream),
+                reps, warmup, stream)
+    vflops = chunk_flops_per_token_head(r=vw.nv // vw.nk) * Tv * vw.nv
+    vb = chunk_bytes(Tv, vw.nk, vw.nv, n_seqs=nseq, state_in=True, gate_bytes=4)
+    tf = vflops / (ms * 1e-3) / 1e12
+    rows["chunk_fwd_varlen"] = dict(
+        workload=f"varlen_prefill_8seq: {nseq} sequences, lengths {[int(l) for l in vx['lengths']]} ({Tv} tokens), "
+                 f"{vw.nk}->{vw.nv} heads, initial states, gating folded in",
+        kernel="chunk_offsets + chunk_prep + chunk_state", bound="mfma", avg_ms=round(ms, 4),
+        algorithmic_flops=vflops, achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+        frac=round(tf / PEAK_BF16_TFLOPS, 4), algorithmic_bytes=vb, hbm_gbps_algorithmic=round(vb / (ms * 1e-3) / 1e9, 1),
+        tokens_per_s=round(Tv / (ms * 1e-3), 1))
+    del vx, vo, vst, vws
     out = torch.empty((T, wl.nv, wl.dv), device=dev)
     ms = _timed(lambda: gdn.gdn_gated_rmsnorm(o, x["z"], x["norm_w"], eps=1e-6, y=out, stream=stream),
                 reps, warmup, stream)

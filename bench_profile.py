@@ -138,9 +138,10 @@ def summarize_rows(out):
         lines.append(f"- {row}: trace average {avg_us:.1f} us over {', '.join(kn)}"
                      f" (all its launches in the run); events {b[row]['avg_ms'] * 1e3:.1f} us, "
                      f"{b[row]['achieved']:.0f} GB/s = {100 * b[row]['frac']:.1f} % of HBM peak")
-    c = b["chunk_fwd"]
-    lines.append(f"- chunk_fwd: events {c['avg_ms'] * 1e3:.1f} us per call, {c['achieved']:.1f} TFLOP/s algorithmic "
-                 f"({100 * c['frac']:.2f} % of the bf16 MFMA peak), {c['tokens_per_s'] / 1e6:.2f} M tokens/s")
+    for key in ("chunk_fwd", "chunk_fwd_varlen"):
+        c = b[key]
+        lines.append(f"- {key}: events {c['avg_ms'] * 1e3:.1f} us per call, {c['achieved']:.1f} TFLOP/s algorithmic "
+                     f"({100 * c['frac']:.2f} % of the bf16 MFMA peak), {c['tokens_per_s'] / 1e6:.2f} M tokens/s")
     lines += ["", "bench.py line of this run:", "", "    " + json.dumps({"rows": b}), ""]
     with open(ROWS_SUMMARY, "w") as fh:
         fh.write("\n".join(lines))

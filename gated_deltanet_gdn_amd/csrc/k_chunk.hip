@@ -57,11 +57,11 @@ constexpr float kEps = 1e-6f;
 
 constexpr int TILE_ELEMS = CH * D;   // bf16 elements of one 16 KB operand tile
 
-// Workspace: chunk table | per (chunk, value head): 16 KB tile, 1 KB of
+// Workspace: chunk table | sequence order | per (chunk, value head): 16 KB tile, 1 KB of
 // per-token scalars, exp(G_C) | bf16 inputs only, per (chunk, key head): K and
 // Q operand tiles of 16 KB each.
 struct WsLayout {
-  size_t off_chunk_off, off_tp, off_sc, off_egc, off_kf, off_qf, total;
+  size_t off_chunk_off, off_order, off_tp, off_sc, off_egc, off_kf, off_qf, total;
 };
 inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
   const int64_t nch = T / CH + n_seqs;   // >= sum_n ceil(len_n / 64)
@@ -69,6 +69,7 @@ inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
   WsLayout w{};
   size_t o = 0;
   w.off_chunk_off = o; o += (static_cast<size_t>(n_seqs) + 1) * sizeof(int32_t); o = (o + 255) & ~size_t(255);
+  w.off_order = o;     o += static_cast<size_t>(n_seqs) * sizeof(int32_t); o = (o + 255) & ~size_t(255);
   w.off_tp = o;        o += static_cast<size_t>(nch) * nv * tile_bytes;
   w.off_sc = o;        o += static_cast<size_t>(nch) * nv * CH * sizeof(float4);
   w.off_egc = o;       o += static_cast<size_t>(nch) * nv * sizeof(float); o = (o + 255) & ~size_t(255);
@@ -84,9 +85,12 @@ inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
 // ------------------------------------------------------------------ chunk table
 // Capped at nch (the workspace's chunk capacity) so a malformed cu_seqlens can
 // never index past the workspace.
+constexpr int ORDER_MAX = 512;   // batches up to this many sequences are ordered longest first
 __global__ void __launch_bounds__(256) chunk_offsets_kernel(const int32_t* __restrict__ cu, int n_seqs,
-                                                            int64_t T, int32_t nch, int32_t* __restrict__ off) {
+                                                            int64_t T, int32_t nch, int32_t* __restrict__ off,
+                                                            int32_t* __restrict__ order) {
   __shared__ int32_t part[256];
+  __shared__ int32_t cnt[ORDER_MAX];
   const int tid = threadIdx.x;
   int32_t carry = 0;
   for (int base = 0; base < n_seqs; base += 256) {
@@ -110,6 +114,26 @@ __global__ void __launch_bounds__(256) chunk_offsets_kernel(const int32_t* __res
     __syncthreads();
   }
   if (tid == 0) off[n_seqs] = min(carry, nch);
+
+  // The state kernel takes the sequences in this order: by chunk count,
+  // longest first, so that the longest recurrences start first and the short
+  // ones fill in behind them (ties by index; a permutation either way).
+  if (n_seqs <= ORDER_MAX) {
+    for (int n = tid; n < n_seqs; n += 256) {
+      int64_t b, e;
+      seq_bounds(cu, n, T, b, e);
+      cnt[n] = static_cast<int32_t>((e - b + CH - 1) / CH);
+    }
+    __syncthreads();
+    for (int n = tid; n < n_seqs; n += 256) {
+      const int32_t c = cnt[n];
+      int rank = 0;
+      for (int m = 0; m < n_seqs; ++m) rank += (cnt[m] > c) || (cnt[m] == c && m < n);
+      order[rank] = n;
+    }
+  } else {
+    for (int n = tid; n < n_seqs; n += 256) order[n] = n;
+  }
 }
 
 __device__ __forceinline__ int find_le(const int32_t* a, int n, int64_t x) {
@@ -561,6 +585,29 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   }
 }
 
+// Workgroup -> (unit = sequence slot x nv + value head, 16-column slice) for
+// the state kernels. Workgroup b runs on XCD b % 8. The 8 slices of a unit,
+// and the r value heads of one key head, go to one XCD (they share that
+// chunk's operand blocks in its L2); consecutive key-head groups go to
+// consecutive XCDs, so every XCD gets its share of each sequence's units
+// (taken longest sequence first). Unit counts that do not split that way fall
+// back to one unit per XCD in turn, then to contiguous blocks of units.
+__device__ __forceinline__ void state_unit_slice(int b, int n_units, int r, int& unit_slot, int& slice) {
+  const int j = b >> 3;          // this workgroup's position on its XCD
+  if (n_units % (8 * r) == 0) {
+    slice = j & 7;
+    const int k = j >> 3;        // unit position on the XCD
+    unit_slot = ((k / r) * 8 + (b & 7)) * r + k % r;
+  } else if (n_units % 8 == 0) {
+    slice = j & 7;
+    unit_slot = ((j >> 3) << 3) + (b & 7);
+  } else {
+    const int bid = xcd_swizzle(b, n_units * 8);
+    slice = bid & 7;
+    unit_slot = bid >> 3;
+  }
+}
+
 constexpr int BLK_BYTES = BLK_ELEMS * 2;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
@@ -622,7 +669,7 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
     int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
     const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
-    const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
+    const int32_t* __restrict__ order, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
   __shared__ f32x4 XPX[2][2][4][64];     // partial X: [parity][half][token tile][lane]
   __shared__ uint4 SBX[2][2][4][64];     // S as B operand: [parity][hi | lo][dk k-step][lane]
   __shared__ f32x4 UXF[2][4][64];        // U, accumulator layout: [parity][token tile][lane]
@@ -635,10 +682,11 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float SCS[2][4 * CH];   // planes a | b | c | beta
   __shared__ float EGS[2];               // exp(G_C)
 
-  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int slice = bid & 7;
-  const int unit = bid >> 3;             // n * nv + h
-  const int n = unit / nv, h = unit % nv;
+  int slot, slice;
+  state_unit_slice(blockIdx.x, gridDim.x / 8, nv / nk, slot, slice);
+  // sequences in the chunk table's order (longest first), value heads fastest
+  const int n = cu ? order[slot / nv] : 0, h = slot % nv;
+  const int unit = n * nv + h;
   const int hk = h / (nv / nk);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -1087,8 +1135,8 @@ __global__ void __launch_bounds__(64) chunk_state_generic_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, int64_t qs,
     int64_t ks, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk, int nv,
     const int32_t* __restrict__ chunk_off, const float* __restrict__ tp, const float4* __restrict__ sc,
-    const float* __restrict__ egc, const float* __restrict__ S0, float* __restrict__ ST,
-    TO* __restrict__ o) {
+    const float* __restrict__ egc, const int32_t* __restrict__ order, const float* __restrict__ S0,
+    float* __restrict__ ST, TO* __restrict__ o) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int KS = Mma<BF, true, true>::KS, KPL = Mma<BF, true, true>::KPL;
 
@@ -1100,10 +1148,10 @@ __global__ void __launch_bounds__(64) chunk_state_generic_kernel(
   float4* SCs = reinterpret_cast<float4*>(Vs + CH * 16);   // [64]
   float* Rw = reinterpret_cast<float*>(SCs + CH);           // [64][RP]
 
-  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int nb = bid & 7;
-  const int unit = bid >> 3;
-  const int n = unit / nv, h = unit % nv;
+  int slot, nb;
+  state_unit_slice(blockIdx.x, gridDim.x / 8, nv / nk, slot, nb);
+  const int n = cu ? order[slot / nv] : 0, h = slot % nv;   // as in the bf16 kernel
+  const int unit = n * nv + h;
   const int hk = h / (nv / nk);
   const int lane = threadIdx.x;
   const int lr = lane & 15, lg = lane >> 4;
@@ -1257,6 +1305,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   const WsLayout lay = ws_layout(T, n_seqs, nk, nv, BF);
   char* base = static_cast<char*>(ws);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + lay.off_chunk_off);
+  int32_t* order = reinterpret_cast<int32_t*>(base + lay.off_order);
   float* tp = reinterpret_cast<float*>(base + lay.off_tp);
   float4* sc = reinterpret_cast<float4*>(base + lay.off_sc);
   float* egc = reinterpret_cast<float*>(base + lay.off_egc);
@@ -1266,7 +1315,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   const int64_t nch = T / CH + n_seqs;
   hipError_t e = hipSuccess;
   if (cu) {   // varlen chunk table (one sequence needs none)
-    chunk_offsets_kernel<<<1, 256, 0, s>>>(cu, n_seqs, T, static_cast<int32_t>(nch), chunk_off);
+    chunk_offsets_kernel<<<1, 256, 0, s>>>(cu, n_seqs, T, static_cast<int32_t>(nch), chunk_off, order);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1289,10 +1338,10 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     const uint16_t* vb = static_cast<const uint16_t*>(v);
     if (o_bf16)
       chunk_state_bf16_kernel<uint16_t><<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
-                                                         kf, qf, S0, ST, static_cast<uint16_t*>(o));
+                                                         kf, qf, order, S0, ST, static_cast<uint16_t*>(o));
     else
       chunk_state_bf16_kernel<float><<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
-                                                      kf, qf, S0, ST, static_cast<float*>(o));
+                                                      kf, qf, order, S0, ST, static_cast<float*>(o));
     return hipGetLastError();
   } else {
     const size_t lds = generic_lds_bytes();
@@ -1301,7 +1350,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (err != hipSuccess) return err;
       kern<<<grid, 64, lds, s>>>(static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v),
-                                 qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, S0, ST, optr);
+                                 qs, ks, vs, cu, n_seqs, T, nk, nv, chunk_off, tp, sc, egc, order, S0, ST, optr);
       return hipGetLastError();
     };
     if (o_bf16) return launch(chunk_state_generic_kernel<TIn, uint16_t>, static_cast<uint16_t*>(o));
