@@ -365,3 +365,34 @@ def test_gating_and_conv_update_in_a_device_graph():
         assert torch.isfinite(filler)
         for a, b, nm in ((g_g, g_e, "g"), (b_g, b_e, "beta"), (y_g, y_e, "conv y"), (cs_g, cs_e, "conv state")):
             assert torch.equal(a, b), f"replay {rep}: {nm} differs from the eager call"
+
+
+# ------------------------------------------------------------------ degenerate batches
+
+def test_batches_without_tokens():
+    """Sequences with no tokens at all (T_tot = 0): every entry point leaves the states as they were."""
+    _say("batches of empty sequences")
+    d = dev()
+    nk, nv, n = 2, 4, 3
+    cu = torch.zeros(n + 1, dtype=torch.int32, device=d)
+    S0 = W.randn((n, nv, 128, 128), 21, 1, "f32", std=0.5).to(d)
+    q = torch.empty((0, nk, 128), device=d, dtype=torch.bfloat16)
+    v = torch.empty((0, nv, 128), device=d, dtype=torch.bfloat16)
+    ab = torch.empty((0, nv), device=d, dtype=torch.bfloat16)
+    gb = torch.empty((0, nv), device=d)
+    A_log, dt_bias = torch.zeros(nv, device=d), torch.zeros(nv, device=d)
+    o, st = gdn.gdn_chunk_fwd(q, q, v, gb, gb, cu_seqlens=cu, initial_state=S0)
+    o2, st2 = gdn.gdn_chunk_fwd_gated(q, q, v, ab, ab, A_log, dt_bias, cu_seqlens=cu, initial_state=S0)
+    rs = S0.clone()
+    gdn.gdn_recurrent_fwd(q, q, v, gb, gb, rs, cu_seqlens=cu)
+    C = (2 * nk + nv) * 128
+    cs0 = W.randn((n, C, 3), 21, 2, "bf16").to(d)
+    cs, fs = cs0.clone(), S0.clone()
+    gdn.gdn_decode_step_fused(torch.empty((0, C), device=d, dtype=torch.bfloat16), cs,
+                              W.uniform((C, 4), 21, 3, -0.5, 0.5).to(d), ab, ab, A_log, dt_bias, fs, nk, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and o2.shape[0] == 0
+    for t, nm in ((st, "chunk final state"), (st2, "gated chunk final state"), (rs, "recurrent state"),
+                  (fs, "fused decode state")):
+        assert torch.equal(t, S0), f"{nm} changed without tokens"
+    assert torch.equal(cs, cs0), "conv state changed without tokens"
