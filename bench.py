@@ -228,7 +228,27 @@ def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
                              peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(tf / PEAK_BF16_TFLOPS, 4),
                              algorithmic_bytes=cb, hbm_gbps_algorithmic=round(cb / (ms * 1e-3) / 1e9, 1),
                              tokens_per_s=round(T / (ms * 1e-3), 1))
-    del ws, y, q, k, v, g, beta
+    # the same core with the conv and the gating folded in (one call), against conv + gated chunk launches
+    cso = torch.empty((1, C, wl.state_len), device=dev, dtype=x["x"].dtype)
+    ms_f = _timed(lambda: gdn.gdn_prefill_fused(x["x"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"], wl.nk,
+                                                wl.nv, state_len=wl.state_len, conv_state_out=cso, final_state=st, o=o,
+                                                workspace=ws, stream=stream),
+                  max(2, reps // 2), 1, stream)
+    ms_s = _timed(lambda: (gdn.gdn_causal_conv1d(x["x"], x["conv_w"], state_len=wl.state_len, y=y, conv_state_out=cso,
+                                                 stream=stream),
+                           gdn.gdn_chunk_fwd_gated(q, k, v, x["a"], x["b"], x["A_log"], x["dt_bias"], final_state=st,
+                                                   o=o, workspace=ws, stream=stream)),
+                  max(2, reps // 2), 1, stream)
+    fb = T * C * 2 + T * wl.nv * 2 * 2 + T * wl.nv * wl.dv * 4 + wl.nv * wl.dk * wl.dv * 4 + C * wl.state_len * 2
+    tf = flops / (ms_f * 1e-3) / 1e12
+    rows["prefill_fused"] = dict(
+        workload=f"long_fused_t256k: x [{T}, {C}] bf16 through conv + SiLU, gating and the chunked rule in one call",
+        kernel="chunk_prep (conv on q, k) + chunk_state (conv on v) + conv state out", bound="mfma",
+        avg_ms=round(ms_f, 4), avg_ms_separate_conv_then_gated_chunk=round(ms_s, 4), algorithmic_flops=flops,
+        achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(tf / PEAK_BF16_TFLOPS, 4),
+        algorithmic_bytes=fb, hbm_gbps_algorithmic=round(fb / (ms_f * 1e-3) / 1e9, 1),
+        tokens_per_s=round(T / (ms_f * 1e-3), 1))
+    del ws, y, q, k, v, g, beta, cso
     # the varlen prefill batch: 8 packed sequences with nonzero initial states, gating folded in
     vw = W.WORKLOADS["varlen_prefill_8seq"]
     vx = {kk: (vv.to(dev) if isinstance(vv, torch.Tensor) else vv) for kk, vv in W.chunk_inputs(vw).items()}

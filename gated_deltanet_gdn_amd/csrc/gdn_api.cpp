@@ -165,6 +165,60 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtyp
                   fn);
 }
 
+int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const float* conv_weight,
+                      const float* conv_bias, int K, const void* conv_state_in, void* conv_state_out, int state_len,
+                      const void* a, const void* b, int ab_dtype, const float* A_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv,
+                      float scale, int qk_l2norm, const float* initial_state, float* final_state, void* o,
+                      int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_prefill_fused";
+  if (!valid_dtype(dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not f32/bf16", fn, dtype);
+  if (dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: only bf16 x is built", fn);
+  if (!valid_dtype(ab_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: ab_dtype %d is not f32/bf16", fn, ab_dtype);
+  if (K <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: K must be positive", fn);
+  if (state_len < K - 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: state_len (%d) < K - 1", fn, state_len);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: only K = 4 is built (got %d)", fn, K);
+  if (nk <= 0 || nv <= 0 || dk <= 0 || dv <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s: head counts and dims must be positive", fn);
+  const int64_t conv_dim = 2 * static_cast<int64_t>(nk) * dk + static_cast<int64_t>(nv) * dv;
+  if (x_tok_stride == 0) x_tok_stride = conv_dim;
+  if (x_tok_stride < conv_dim) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x token stride smaller than conv_dim", fn);
+  // q, k, v are the views of x at channel offsets 0, nk dk and 2 nk dk
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const void* qv = xb;
+  const void* kv = xb ? xb + static_cast<int64_t>(nk) * dk : nullptr;
+  const void* vv = xb ? xb + 2 * static_cast<int64_t>(nk) * dk : nullptr;
+  int64_t qs = x_tok_stride, ks = x_tok_stride, vs = x_tok_stride;
+  const int st = check_core(fn, qv, kv, vv, dtype, qs, ks, vs, static_cast<const float*>(a),
+                            static_cast<const float*>(b), n_seqs, T_tot, nk, nv, dk, dv, o, o_dtype);
+  if (st != GDN_OK) return st;
+  if (!conv_weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: conv_weight is required", fn);
+  if (!A_log || !dt_bias) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: A_log and dt_bias are required", fn);
+  if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
+  if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, 1);
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (conv_state_in && conv_state_out) {
+    const size_t bytes = static_cast<size_t>(n_seqs) * conv_dim * state_len * 2;
+    const char* a0 = static_cast<const char*>(conv_state_in);
+    const char* b0 = static_cast<const char*>(conv_state_out);
+    if (a0 < b0 + bytes && b0 < a0 + bytes)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s: conv_state_out must not overlap conv_state_in", fn);
+  }
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_chunk_fwd_conv(x, x_tok_stride, conv_weight, conv_bias, conv_state_in, state_len, a, b,
+                                            ab_dtype == GDN_BF16 ? 1 : 2, A_log, dt_bias, cu_seqlens, n_seqs, T_tot,
+                                            nk, nv, scale, qk_l2norm != 0, initial_state, final_state, o,
+                                            o_dtype == GDN_BF16, workspace, s);
+  if (e == hipSuccess && conv_state_out)   // after the chunk kernels, which read conv_state_in
+    e = gdn::launch_conv_state_out(x, 1, x_tok_stride, cu_seqlens, n_seqs, T_tot, static_cast<int>(conv_dim),
+                                   conv_state_in, conv_state_out, state_len, s);
+  return launched(e, fn);
+}
+
 int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype, int64_t q_tok_stride,
                       int64_t k_tok_stride, int64_t v_tok_stride, const float* g, const float* beta,
                       const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv,

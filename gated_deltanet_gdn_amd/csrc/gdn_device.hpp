@@ -58,6 +58,45 @@ __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rc
 __device__ __forceinline__ float softplusf_(float s) { return fmaxf(s, 0.0f) + log1pf(exp_neg_(fabsf(s))); }
 __device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + exp_neg_(x)); }
 
+// ---------------------------------------------------------------- conv taps
+// Element e (0..7) of 8 packed bf16.
+__device__ __forceinline__ float bf16_elem(const uint4& u, int e) {
+  const uint32_t d = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+  return __uint_as_float((e & 1) ? (d & 0xffff0000u) : (d << 16));
+}
+// Causal depthwise conv (4 taps) + SiLU of 8 channels of one token from its
+// raw bf16 window rows (w[3] the token, w[0] three tokens back), rounded to
+// bf16 as a stored conv output is. The bias comes first, then the taps
+// oldest first, one fma each: the order of the prefill conv kernel, so both
+// give the same bits.
+__device__ __forceinline__ void conv4_silu8_bf16(const uint4 (&w)[4], const float (&wt)[4][8], const float (&bs)[8],
+                                                 float (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float acc = bs[e];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = fmaf(wt[j][e], bf16_elem(w[j], e), acc);
+    out[e] = bf16_to_f32(f32_to_bf16(siluf_(acc)));
+  }
+}
+// 8 bf16 values at stride `stride` elements, packed as a row of 8.
+__device__ __forceinline__ uint4 gather8_bf16(const uint16_t* p, int64_t stride) {
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d[i] = static_cast<uint32_t>(p[2 * i * stride]) | (static_cast<uint32_t>(p[(2 * i + 1) * stride]) << 16);
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+// 8 fp32 values rounded to bf16 (nearest even) and packed, element 0 lowest.
+__device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2 * i], v[2 * i + 1]}, b2));
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
 // ---------------------------------------------------------------- wave helpers (wave64)
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

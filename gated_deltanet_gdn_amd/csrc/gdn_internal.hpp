@@ -21,6 +21,11 @@ hipError_t launch_causal_conv1d(const void* x, int bf16, int64_t x_stride, const
                                 int C, const void* st_in, void* st_out, int state_len, int silu,
                                 void* y, hipStream_t s);
 
+// Only the conv_state_out part of launch_causal_conv1d: the last state_len
+// inputs of every sequence (for callers that apply the conv elsewhere).
+hipError_t launch_conv_state_out(const void* x, int bf16, int64_t x_stride, const int32_t* cu, int n_seqs,
+                                 int64_t T, int C, const void* st_in, void* st_out, int state_len, hipStream_t s);
+
 hipError_t launch_causal_conv1d_update(const void* x, int bf16, void* state, int state_len,
                                        const float* w, const float* bias, int n_seqs, int C,
                                        int silu, void* y, hipStream_t s);
@@ -51,5 +56,14 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf1
                             const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs,
                             int64_t T, int nk, int nv, float scale, int l2, const float* S0, float* ST,
                             void* o, int o_bf16, void* ws, hipStream_t s);
+
+// The chunked path with the causal conv1d (4 taps) + SiLU folded in, bf16 x
+// [T, (2 nk + nv) 128] with token stride xs; gating inputs as for gm = 1 / 2.
+// The conv state out is not written here (launch_conv_state_out).
+hipError_t launch_chunk_fwd_conv(const void* x, int64_t xs, const float* conv_w, const float* conv_b,
+                                 const void* conv_st, int state_len, const void* a, const void* b, int gm,
+                                 const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs, int64_t T,
+                                 int nk, int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16,
+                                 void* ws, hipStream_t s);
 
 }  // namespace gdn

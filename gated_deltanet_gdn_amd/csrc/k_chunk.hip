@@ -312,19 +312,34 @@ constexpr size_t prep_lds_bytes() {
 }
 constexpr int PREP_WAVES = 4;
 
+// Causal conv1d (4 taps) + SiLU folded into the chunk kernels: x holds the
+// packed q | k | v channels (conv_dim = 2 nk D + nv D, bf16); the conv state
+// [n_seqs, conv_dim, state_len] (or none: zero history) supplies the three
+// inputs before each sequence's first token.
+struct ConvIn {
+  const float* w;          // [conv_dim, 4]
+  const float* b;          // [conv_dim] or null
+  const uint16_t* st;      // conv state in, or null
+  int state_len;
+  int conv_dim;
+};
+
 // (at most 128 VGPRs: four waves per SIMD, i.e. four blocks per CU, which is
 // also what the LDS holds)
 // GM selects the per-token gating inputs: 0 = g and beta (fp32) given;
 // 1 / 2 = the raw a and b (bf16 / fp32), gated here exactly as the separate
 // gating kernel does (same expressions), so both routes give the same bits.
-template <typename TIn, int GM>
+// CV: q is the conv input x (channel 0 of the packed q | k | v) with token
+// stride qs; k and ks are unused. The K and Q tiles are then the conv + SiLU
+// outputs, rounded to bf16 as a stored conv output would be.
+template <typename TIn, int GM, bool CV>
 __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_per_eu(4))) chunk_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t qs, int64_t ks,
     const void* __restrict__ ga, const void* __restrict__ gb, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, const int32_t* __restrict__ cu,
     int n_seqs, int64_t T, int nk, int nv, float scale, int l2, const int32_t* __restrict__ chunk_off,
     float* __restrict__ tp, float4* __restrict__ sc, float* __restrict__ egc, uint16_t* __restrict__ kf,
-    uint16_t* __restrict__ qf) {
+    uint16_t* __restrict__ qf, ConvIn cv) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int EP = prep_pitch<TIn>();
   using MG = Mma<BF, true, true>;
@@ -367,9 +382,67 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   const TA gb_ld = static_cast<const TA*>(gb)[gi];
 
   // 1. K and Q tiles into LDS; rows past the sequence end re-read the last
-  //    valid row: their norms are forced to 0 below, so they contribute
-  //    nothing to A, P or the scalars
-  {
+  //    valid row (or are zero after the conv): their norms are forced to 0
+  //    below, so they contribute nothing to A, P or the scalars
+  if constexpr (CV) {
+    static_assert(BF, "the conv prologue takes bf16 inputs");
+    // thread -> (K | Q, 8-channel segment, block of 8 rows); its window runs
+    // over rows 8 rb - 3 .. 8 rb + 7 of the chunk
+    const int grp = tid & 31, rb = tid >> 5;
+    const int zq = grp >> 4, seg = grp & 15;
+    const int ch0 = (zq ? 0 : nk * D) + hk * D + 8 * seg;
+    float wt[4][8], bs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wt[j][e] = cv.w[(ch0 + e) * 4 + j];
+      bs[e] = cv.b ? cv.b[ch0 + e] : 0.0f;
+    }
+    uint4 raw[11];
+#pragma unroll
+    for (int u = 0; u < 11; ++u) {
+      const int r = 8 * rb - 3 + u;
+      const int64_t t = t0 + r;
+      if (r < L && t >= s_begin)
+        raw[u] = *reinterpret_cast<const uint4*>(q + t * qs + ch0);
+      else if (t < s_begin && cv.st)   // history of the sequence (t - s_begin in -3 .. -1)
+        raw[u] = gather8_bf16(cv.st + (static_cast<int64_t>(n) * cv.conv_dim + ch0) * cv.state_len + cv.state_len +
+                                  (t - s_begin),
+                              cv.state_len);
+      else
+        raw[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // each input row is widened once and slides through the window; the
+    // arithmetic per output is that of conv4_silu8_bf16 (same bits)
+    TIn* dst = zq ? Qs : Ks;
+    float win[3][8];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) win[j][e] = bf16_elem(raw[j], e);
+#pragma unroll
+    for (int u = 3; u < 11; ++u) {
+      const int r = 8 * rb + u - 3;
+      float cur[8], y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cur[e] = bf16_elem(raw[u], e);
+        float acc = bs[e];
+        acc = fmaf(wt[0][e], win[0][e], acc);
+        acc = fmaf(wt[1][e], win[1][e], acc);
+        acc = fmaf(wt[2][e], win[2][e], acc);
+        acc = fmaf(wt[3][e], cur[e], acc);
+        y[e] = siluf_(acc);
+      }
+      *reinterpret_cast<uint4*>(dst + r * EP + 8 * seg) = zero_if(r >= L, pack8_bf16(y));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        win[0][e] = win[1][e];
+        win[1][e] = win[2][e];
+        win[2][e] = cur[e];
+      }
+    }
+  } else {
     const TIn* kb = k + t0 * ks + static_cast<int64_t>(hk) * D;
     const TIn* qb = q + t0 * qs + static_cast<int64_t>(hk) * D;
 #pragma unroll
@@ -664,12 +737,16 @@ __device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
 // lane l's 16 bytes in a padded LDS K block
 __device__ __forceinline__ int kl_lane(int l) { return 16 * l + 64 * (l >> 4); }
 
-template <typename TO>
+// CV: v is the conv input x at the first value channel (token stride vs); the
+// output waves apply the conv + SiLU to the value rows as they stage them,
+// wave 2 for tokens 0-31 of a chunk and wave 3 for tokens 32-63.
+template <typename TO, bool CV>
 __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
     int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
     const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
-    const int32_t* __restrict__ order, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o) {
+    const int32_t* __restrict__ order, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o,
+    ConvIn cv) {
   __shared__ f32x4 XPX[2][2][4][64];     // partial X: [parity][half][token tile][lane]
   __shared__ uint4 SBX[2][2][4][64];     // S as B operand: [parity][hi | lo][dk k-step][lane]
   __shared__ f32x4 UXF[2][4][64];        // U, accumulator layout: [parity][token tile][lane]
@@ -904,6 +981,21 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   }
   // V staging: lane l of instruction i loads token 32 i + l / 2, columns 8 (l % 2) .. +7
   const uint32_t vo0 = static_cast<uint32_t>(((lane >> 1) * vs + slice * 16 + 8 * (lane & 1)) * 2);
+  // with the conv: output wave ow stages token 32 ow + l / 2 from its window
+  // rows (that token and the three before it), the same 8 columns
+  const int ctok = 32 * ow + (lane >> 1);
+  const int cch = 2 * nk * D + h * D + slice * 16 + 8 * (lane & 1);   // first channel in conv_dim
+  float cwt[4][8], cbs[8];
+  uint4 cxr[4];                          // staging: window rows
+  float cbeta = 0.0f;                    // staging (wave 2): beta of its token
+  if constexpr (CV) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cwt[j][e] = cv.w[(cch + e) * 4 + j];
+      cbs[e] = cv.b ? cv.b[cch + e] : 0.0f;
+    }
+  }
   // T staging: block (m, s) of the strictly lower part, slot j = token
   // 32 s + perm32(lg, j) against row 16 m + lr. Blocks (2, 0) and (3, 0) lie
   // wholly below the diagonal; in the others one half is zero or full and the
@@ -1012,6 +1104,7 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   // wave 2 stages the masked T blocks, wave 3 the scalars, exp(G_C) and beta v
   auto run = [&](auto tstager) {
     constexpr bool TW = decltype(tstager)::value;
+    auto last = [&](int c) { return min(c, nchunks - 1); };
     auto load_stage = [&](int cc) {
       const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;
       if constexpr (TW) {
@@ -1025,13 +1118,35 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
       } else {
         sg[0] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
         eg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
-        // V rows past the sequence end read as zeros (resource sized to the valid rows)
+        if constexpr (!CV) {
+          // V rows past the sequence end read as zeros (resource sized to the valid rows)
+          const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+          const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+          const rsrc_t rv =
+              make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D, static_cast<uint32_t>(((L - 1) * vs + D) * 2));
+          sg[1] = bload16(rv, vo0);
+          sg[2] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
+        }
+      }
+      if constexpr (CV) {
+        // window rows ctok - 3 .. ctok of x; the resource starts 3 rows early
+        // when those rows lie in the sequence (every chunk but the first) and
+        // ends at the last valid row, so rows before the sequence (offsets that
+        // wrap below zero) and after it read as zeros
         const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
         const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-        const rsrc_t rv =
-            make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D, static_cast<uint32_t>(((L - 1) * vs + D) * 2));
-        sg[1] = bload16(rv, vo0);
-        sg[2] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
+        const int pre = cc > 0 ? 3 : 0;
+        const rsrc_t rv = make_rsrc(v + (t0 - pre) * vs + static_cast<int64_t>(h) * D,
+                                    static_cast<uint32_t>(((L - 1 + pre) * vs + D) * 2));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = ctok - 3 + j + pre;   // row from the resource start (may be < 0)
+          cxr[j] = bload16(rv, static_cast<uint32_t>((static_cast<int64_t>(r) * vs + slice * 16 + 8 * (lane & 1)) * 2));
+        }
+        if constexpr (TW)
+          cbeta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                make_rsrc(scp + ct * 4 * CH + 3 * CH, CH * 4),
+                                                static_cast<uint32_t>(ctok * 4), 0, 0));
       }
     };
     // stage chunk cs (its loads are in sg) in LDS buffer cs & 1
@@ -1054,6 +1169,28 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
       } else {
         *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = sg[0];
         if (lane == 0) EGS[buf] = bits_f(eg);
+      }
+      if constexpr (CV) {
+        const int t = ctok;
+        const float be = TW ? cbeta : SCS[buf][3 * CH + t];   // wave 3 wrote SCS above
+        uint4 win[4] = {cxr[0], cxr[1], cxr[2], cxr[3]};
+        if (cs == 0 && t < 3 && cv.st) {   // the sequence's history from the conv state
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            if (t - 3 + j < 0)
+              win[j] = gather8_bf16(cv.st + (static_cast<int64_t>(n) * cv.conv_dim + cch) * cv.state_len +
+                                        cv.state_len + (t - 3 + j),
+                                    cv.state_len);
+        }
+        float y[8];
+        conv4_silu8_bf16(win, cwt, cbs, y);
+        const int64_t t0 = s_begin + static_cast<int64_t>(last(cs)) * CH;
+        const bool pad = t0 + t >= s_end;   // rows past the sequence end stage zeros
+        float* bvs = reinterpret_cast<float*>(&BVS[buf][0][0]);
+        float* base = bvs + ((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) base[(8 * (lane & 1) + e) * 4] = pad ? 0.0f : be * y[e];
+      } else if constexpr (!TW) {
         float* bvs = reinterpret_cast<float*>(&BVS[buf][0][0]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -1070,7 +1207,6 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
         }
       }
     };
-    auto last = [&](int c) { return min(c, nchunks - 1); };
     load_q(0);
     load_p(0);
     load_stage(0);
@@ -1300,8 +1436,9 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
                           const void* ga, const void* gb, int gm, const float* A_log, const float* dt_bias,
                           const int32_t* cu, int n_seqs, int64_t T, int nk,
                           int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
-                          hipStream_t s) {
+                          const ConvIn* cvp, hipStream_t s) {
   constexpr bool BF = sizeof(TIn) == 2;
+  const ConvIn cv = cvp ? *cvp : ConvIn{nullptr, nullptr, nullptr, 0, 0};
   const WsLayout lay = ws_layout(T, n_seqs, nk, nv, BF);
   char* base = static_cast<char*>(ws);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + lay.off_chunk_off);
@@ -1320,14 +1457,18 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     if (e != hipSuccess) return e;
   }
   {
-    auto kern = gm == 1 ? chunk_prep_kernel<TIn, 1> : gm == 2 ? chunk_prep_kernel<TIn, 2> : chunk_prep_kernel<TIn, 0>;
+    auto kern = gm == 1 ? chunk_prep_kernel<TIn, 1, false>
+                : gm == 2 ? chunk_prep_kernel<TIn, 2, false> : chunk_prep_kernel<TIn, 0, false>;
+    if constexpr (BF) {
+      if (cvp) kern = gm == 1 ? chunk_prep_kernel<TIn, 1, true> : chunk_prep_kernel<TIn, 2, true>;
+    }
     const size_t lds = prep_lds_bytes<TIn>();
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
     kern<<<dim3(static_cast<unsigned>(nv), static_cast<unsigned>(nch)), 64 * PREP_WAVES, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, ga, gb, A_log, dt_bias, cu, n_seqs, T, nk, nv,
-        scale, l2, chunk_off, tp, sc, egc, kf, qf);
+        scale, l2, chunk_off, tp, sc, egc, kf, qf, cv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1336,13 +1477,17 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     const uint16_t* xf = reinterpret_cast<const uint16_t*>(tp);
     const float* scp = reinterpret_cast<const float*>(sc);
     const uint16_t* vb = static_cast<const uint16_t*>(v);
-    if (o_bf16)
-      chunk_state_bf16_kernel<uint16_t><<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
-                                                         kf, qf, order, S0, ST, static_cast<uint16_t*>(o));
-    else
-      chunk_state_bf16_kernel<float><<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc,
-                                                      kf, qf, order, S0, ST, static_cast<float*>(o));
-    return hipGetLastError();
+    auto launch = [&](auto kern, auto* optr) {
+      kern<<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order, S0, ST, optr,
+                                cv);
+      return hipGetLastError();
+    };
+    if (cvp) {
+      if (o_bf16) return launch(chunk_state_bf16_kernel<uint16_t, true>, static_cast<uint16_t*>(o));
+      return launch(chunk_state_bf16_kernel<float, true>, static_cast<float*>(o));
+    }
+    if (o_bf16) return launch(chunk_state_bf16_kernel<uint16_t, false>, static_cast<uint16_t*>(o));
+    return launch(chunk_state_bf16_kernel<float, false>, static_cast<float*>(o));
   } else {
     const size_t lds = generic_lds_bytes();
     auto launch = [&](auto kern, auto* optr) {
@@ -1371,9 +1516,21 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf1
                             hipStream_t s) {
   if (bf16)
     return chunk_dispatch<uint16_t>(q, k, v, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2,
-                                    S0, ST, o, o_bf16, ws, s);
+                                    S0, ST, o, o_bf16, ws, nullptr, s);
   return chunk_dispatch<float>(q, k, v, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2, S0,
-                               ST, o, o_bf16, ws, s);
+                               ST, o, o_bf16, ws, nullptr, s);
+}
+
+hipError_t launch_chunk_fwd_conv(const void* x, int64_t xs, const float* conv_w, const float* conv_b,
+                                 const void* conv_st, int state_len, const void* a, const void* b, int gm,
+                                 const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs, int64_t T,
+                                 int nk, int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16,
+                                 void* ws, hipStream_t s) {
+  const int conv_dim = (2 * nk + nv) * D;
+  const ConvIn cv{conv_w, conv_b, static_cast<const uint16_t*>(conv_st), state_len, conv_dim};
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  return chunk_dispatch<uint16_t>(xb, xb + nk * D, xb + 2 * nk * D, xs, xs, xs, a, b, gm, A_log, dt_bias, cu, n_seqs,
+                                  T, nk, nv, scale, l2, S0, ST, o, o_bf16, ws, &cv, s);
 }
 
 }  // namespace gdn

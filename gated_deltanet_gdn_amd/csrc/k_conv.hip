@@ -280,20 +280,23 @@ hipError_t launch_causal_conv1d(const void* x, int bf16, int64_t x_stride, const
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (st_out) {
-    const int64_t units = static_cast<int64_t>(n_seqs) * C;
-    const dim3 grid(static_cast<unsigned>((units + 255) / 256));
-    if (bf16)
-      conv_state_out_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), x_stride, cu, n_seqs,
-                                                           T, C, static_cast<const uint16_t*>(st_in),
-                                                           static_cast<uint16_t*>(st_out), state_len);
-    else
-      conv_state_out_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), x_stride, cu, n_seqs, T, C,
-                                                        static_cast<const float*>(st_in),
-                                                        static_cast<float*>(st_out), state_len);
-    return hipGetLastError();
-  }
+  if (st_out) return launch_conv_state_out(x, bf16, x_stride, cu, n_seqs, T, C, st_in, st_out, state_len, s);
   return hipSuccess;
+}
+
+hipError_t launch_conv_state_out(const void* x, int bf16, int64_t x_stride, const int32_t* cu, int n_seqs,
+                                 int64_t T, int C, const void* st_in, void* st_out, int state_len, hipStream_t s) {
+  const int64_t units = static_cast<int64_t>(n_seqs) * C;
+  const dim3 grid(static_cast<unsigned>((units + 255) / 256));
+  if (bf16)
+    conv_state_out_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), x_stride, cu, n_seqs, T,
+                                                         C, static_cast<const uint16_t*>(st_in),
+                                                         static_cast<uint16_t*>(st_out), state_len);
+  else
+    conv_state_out_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), x_stride, cu, n_seqs, T, C,
+                                                      static_cast<const float*>(st_in), static_cast<float*>(st_out),
+                                                      state_len);
+  return hipGetLastError();
 }
 
 hipError_t launch_causal_conv1d_update(const void* x, int bf16, void* state, int state_len, const float* w,

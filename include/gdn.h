@@ -131,6 +131,44 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtyp
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The prefill core of one layer with the causal conv folded into the chunk
+ * kernels ("Qwen3.5 Dense Model Architecture", Linear Attention, minimal
+ * example: the packed q|k|v projection goes through the causal conv1d and
+ * SiLU, is split into q, k, v, and feeds the chunk rule with the beta and g of
+ * the gating; "Qwen3.5 Simulation Support Design Document", 2.2 ops 1-4).
+ * The prep kernel applies the conv to the key and query rows of each chunk
+ * and the state kernel to the value rows it stages, each from a 3-token halo,
+ * so the conv output never goes to memory. The results (o, final_state,
+ * conv_state_out) are bit for bit those of gdn_causal_conv1d (silu = 1,
+ * output in the dtype of x), gdn_gating and gdn_chunk_fwd run one after the
+ * other, q, k, v being the views of the conv output at channel offsets 0,
+ * nk*dk and 2*nk*dk.
+ *   x          : [T_tot, conv_dim] bf16, channels dense, token stride
+ *                x_tok_stride (0 = conv_dim); conv_dim = 2*nk*dk + nv*dv;
+ *                16-byte aligned, stride a multiple of 8
+ *   conv_weight: [conv_dim, K] fp32;  conv_bias : [conv_dim] fp32 or NULL
+ *   conv_state_in : [n_seqs, conv_dim, state_len] bf16 or NULL (zero history):
+ *                its last K-1 entries precede each sequence's first token
+ *   conv_state_out: same shape or NULL (not written): the last state_len
+ *                inputs of each sequence; must not overlap conv_state_in
+ *   a, b, A_log, dt_bias : as gdn_chunk_fwd_gated
+ *   cu_seqlens, scale, qk_l2norm, initial_state, final_state, o, workspace:
+ *                as gdn_chunk_fwd, with the workspace size of
+ *                gdn_chunk_fwd_workspace_size(T_tot, n_seqs, nk, nv, dk, dv, GDN_BF16)
+ * Supported: dtype bf16, K = 4, dk = dv = 128, nv % nk == 0.
+ */
+int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride,
+                      const float* conv_weight, const float* conv_bias, int K,
+                      const void* conv_state_in, void* conv_state_out, int state_len,
+                      const void* a, const void* b, int ab_dtype,
+                      const float* A_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                      int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                      const float* initial_state, float* final_state,
+                      void* o, int o_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Recurrent gated delta rule, the decode path ("Qwen3.5 Simulation Support
  * Design Document", 2.2 op 5 and 2.3: decode batches, including multi-token
  * MTP decode, take the token-by-token path; "Qwen3.5 Dense Model

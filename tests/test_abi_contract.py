@@ -253,3 +253,40 @@ def _gated(L, **kw):
 def test_chunk_fwd_gated_argument_errors(L, kw, status):
     assert _gated(L, **kw) == status
     assert gdn.gdn_last_error() != ""
+
+
+def _prefill(L, **kw):
+    a = dict(x=P, dtype=1, xs=0, cw=P, cb=NULL, K=4, csi=NULL, cso=NULL, sl=3, a=P, b=P, ab_dtype=1, alog=P, dtb=P,
+             cu=NULL, n=1, T=256, nk=1, nv=2, dk=128, dv=128, scale=0.0, l2=1, s0=NULL, st=NULL, o=P, o_dtype=0,
+             ws=P2, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return L.gdn_prefill_fused(a["x"], a["dtype"], a["xs"], a["cw"], a["cb"], a["K"], a["csi"], a["cso"], a["sl"],
+                               a["a"], a["b"], a["ab_dtype"], a["alog"], a["dtb"], a["cu"], a["n"], a["T"], a["nk"],
+                               a["nv"], a["dk"], a["dv"], a["scale"], a["l2"], a["s0"], a["st"], a["o"],
+                               a["o_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), UNSUPPORTED),          # fp32 x is not built for the fused prefill
+    (dict(dtype=5), INVALID),
+    (dict(ab_dtype=4), INVALID),
+    (dict(K=3, sl=2), UNSUPPORTED),
+    (dict(sl=2), INVALID),                 # state_len < K - 1
+    (dict(xs=100), INVALID),               # stride below conv_dim = 512
+    (dict(xs=516), UNSUPPORTED),           # stride not a multiple of 8
+    (dict(x=MIS), UNSUPPORTED),
+    (dict(x=NULL), INVALID),
+    (dict(cw=NULL), INVALID),
+    (dict(a=NULL), INVALID),
+    (dict(alog=NULL), INVALID),
+    (dict(dtb=NULL), INVALID),
+    (dict(nk=3, nv=4), INVALID),
+    (dict(n=2), INVALID),                  # several sequences need cu_seqlens
+    (dict(ws=NULL), INVALID),
+    (dict(ws_bytes=16), WS_SMALL),
+    (dict(dk=64, dv=64), UNSUPPORTED),
+    (dict(csi=P, cso=ctypes.c_void_p(0x100000 + 256)), INVALID),   # overlapping conv states
+])
+def test_prefill_fused_argument_errors(L, kw, status):
+    assert _prefill(L, **kw) == status
+    assert gdn.gdn_last_error() != ""

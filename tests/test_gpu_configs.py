@@ -122,6 +122,22 @@ def long_run():
     return dict(wl=wl, x=x, y=y, cs=cs, g=g, beta=beta, o=o, st=st, out=out, T=T, C=C, kd=kd)
 
 
+def test_long_prefill_fused_equals_pipeline(long_run):
+    """The fused prefill (conv applied inside the chunk kernels) reproduces the separate conv, gating and
+    chunk launches bit for bit on the full long workload."""
+    r = long_run
+    wl, x = r["wl"], r["x"]
+    _say(wl.name, "fused prefill against the separate launches")
+    o, st, cs = gdn.gdn_prefill_fused(x["x"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"], wl.nk, wl.nv,
+                                      state_len=wl.state_len)
+    torch.cuda.synchronize()
+    for a, b, what in ((o, r["o"], "o"), (st, r["st"], "final state"), (cs, r["cs"], "conv state out")):
+        diff = (a.double() - b.double()).abs().max().item()
+        print(f"[exact] {what}: max |fused - separate| = {diff:.3e}", flush=True)
+        assert torch.equal(a, b), what
+    del o, st, cs
+
+
 def test_long_conv_windows(long_run):
     r = long_run
     T = r["T"]
