@@ -1,7 +1,7 @@
 """rocprofv3 summaries of the benchmark, written under profiles/.
 
-    python bench_profile.py run        [--out gpurun_out/profile]   # on the GPU machine
-    python bench_profile.py summarize  [--out gpurun_out/profile]   # anywhere, from run's CSVs
+    python bench_profile.py run        [--out DIR]   # on the GPU machine (default prof_out/)
+    python bench_profile.py summarize  [--out DIR]   # anywhere, from run's CSVs
 
 Runs bench.py (no CPU baseline, ending with one plain 1 GiB device copy) as a
 child process under rocprofv3, once per pass. Counters are never combined
@@ -225,7 +225,7 @@ def summarize(out):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("mode", choices=["run", "summarize"])
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "prof_out"))
     ap.add_argument("--timeout", type=int, default=240)
     args = ap.parse_args()
     if args.mode == "run":
