@@ -45,15 +45,17 @@ __device__ __forceinline__ float act_round(float v, float) { return v; }
 __device__ __forceinline__ float act_round(float v, uint16_t) { return bf16_to_f32(f32_to_bf16(v)); }
 
 // One token of the recurrence for a state held by 256 threads (thread t256:
-// columns 4 (t256 % 32) .. +3, rows t256 / 32 + 8 i). ks and qs are this
-// token's k and q of the key head (fp32 in LDS, written before a barrier that
-// precedes the call); red is LDS scratch [4 waves][a | b][128 columns]. Holds
-// one barrier of the whole workgroup. o row element offset ob (column of the
-// thread's first column); rows of the state group rg == 0 store o.
-template <typename TO>
-__device__ __forceinline__ void rec_token(float (&S)[RPT][4], const float* ks, const float* qs, const float (&vv)[4],
-                                          float gt, float bt, float* red, int t256, float scale, int l2,
-                                          TO* __restrict__ o, int64_t ob) {
+// columns 4 (t256 % 32) .. +3, rows t256 / 32 + 8 i), in two halves around a
+// barrier of the whole workgroup. ks and qs are this token's k and q of the
+// key head (fp32 in LDS, written before a barrier that precedes the first
+// half); red is LDS scratch [4 waves][a | b][128 columns]. The first half
+// forms the norms and this thread's partial sums of S^T k and S^T q and
+// writes them to red; the second half (after the barrier) adds them up,
+// stores o (row element offset ob, the thread's first column; rows of group
+// rg == 0 store) and updates S. ks must still hold the token's k then.
+struct RecNorms { float rk, rq, kq; };
+__device__ __forceinline__ RecNorms rec_pass(const float (&S)[RPT][4], const float* ks, const float* qs, float* red,
+                                             int t256, float scale, int l2) {
   const int lane = t256 & 63, wave = t256 >> 6, cg = t256 % CGN, rg = t256 / CGN;
   // norms and k.q, redundantly per wave (no extra barrier)
   const float k0 = ks[2 * lane], k1 = ks[2 * lane + 1];
@@ -64,7 +66,6 @@ __device__ __forceinline__ void rec_token(float (&S)[RPT][4], const float* ks, c
   const float rk = l2 ? 1.0f / sqrtf(skk + 1e-6f) : 1.0f;
   const float rq = (l2 ? 1.0f / sqrtf(sqq + 1e-6f) : 1.0f) * scale;
   const float kq = sqk * rk * rq;
-  const float e = expf(gt);
 
   float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -90,7 +91,15 @@ __device__ __forceinline__ void rec_token(float (&S)[RPT][4], const float* ks, c
     *reinterpret_cast<float4*>(red + (wave * 2 + 0) * D + 4 * cg) = make_float4(pa[0], pa[1], pa[2], pa[3]);
     *reinterpret_cast<float4*>(red + (wave * 2 + 1) * D + 4 * cg) = make_float4(pb[0], pb[1], pb[2], pb[3]);
   }
-  __syncthreads();
+  return {rk, rq, kq};
+}
+template <typename TO>
+__device__ __forceinline__ void rec_finish(float (&S)[RPT][4], const float* ks, const float (&vv)[4], float gt,
+                                           float bt, const float* red, int t256, RecNorms nr, TO* __restrict__ o,
+                                           int64_t ob) {
+  const int cg = t256 % CGN, rg = t256 / CGN;
+  const float rk = nr.rk, kq = nr.kq;
+  const float e = expf(gt);
   float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -114,6 +123,14 @@ __device__ __forceinline__ void rec_token(float (&S)[RPT][4], const float* ks, c
 #pragma unroll
     for (int c = 0; c < 4; ++c) S[i][c] = fmaf(e, S[i][c], kh * dl[c]);
   }
+}
+template <typename TO>
+__device__ __forceinline__ void rec_token(float (&S)[RPT][4], const float* ks, const float* qs, const float (&vv)[4],
+                                          float gt, float bt, float* red, int t256, float scale, int l2,
+                                          TO* __restrict__ o, int64_t ob) {
+  const RecNorms nr = rec_pass(S, ks, qs, red, t256, scale, l2);
+  __syncthreads();
+  rec_finish<TO>(S, ks, vv, gt, bt, red, t256, nr, o, ob);
 }
 
 // G consecutive (sequence, value head) states per workgroup, 256 threads
@@ -214,7 +231,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
   constexpr int NT = 256 * R;
   constexpr int CPT = (NCH + NT - 1) / NT;
   constexpr int KW = 4;
-  __shared__ float kqv_s[2][NCH];       // [parity][q | k | v]: this token's conv outputs
+  __shared__ float kqv_s[3][NCH];       // [token % 3][q | k | v]: conv outputs
   __shared__ float red[2][R][4][2][D];  // [parity][value head][wave][a|b][column]
 
   const int n = blockIdx.x / nk, hk = blockIdx.x % nk;
@@ -266,9 +283,9 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
     }
   }
 
-  int par = 0;
-  for (int64_t t = t0; t < t1; ++t, par ^= 1) {
-    // conv update + SiLU of this token, in the order of the separate kernel
+  // conv update + SiLU of token t into kqv_s[buf], in the order of the
+  // separate kernel; prefetches the next token's inputs
+  auto conv_token = [&](int64_t t, int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int j = tid + u * NT;
@@ -280,22 +297,35 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
 #pragma unroll
         for (int i = 0; i < KW - 1; ++i) acc = fmaf(cw[c * KW + i], hist[u][i], acc);
         acc = fmaf(cw[c * KW + KW - 1], xv, acc);
-        kqv_s[par][j] = act_round(siluf_(acc), T{});
+        kqv_s[buf][j] = act_round(siluf_(acc), T{});
 #pragma unroll
         for (int i = 0; i + 1 < KW - 1; ++i) hist[u][i] = hist[u][i + 1];
         hist[u][KW - 2] = xv;
       }
     }
+  };
+  // One barrier per token: the conv of token t + 1 is formed before the
+  // barrier that completes token t's reductions. kqv_s rotates over three
+  // buffers and red over two, so no buffer is rewritten while a thread that
+  // is one phase behind may still read it.
+  if (t0 < t1) conv_token(t0, 0);
+  __syncthreads();
+  int buf = 0, par = 0;
+  for (int64_t t = t0; t < t1; ++t) {
     // gating, as the separate gating kernel computes it
     const float av = Elem<T>::cvt(a_n), bv = Elem<T>::cvt(b_n);
     if (t + 1 < t1) { a_n = a[(t + 1) * nv + h]; b_n = b[(t + 1) * nv + h]; }
     const float gt = -exp_(alog) * softplusf_(av + dtb);
     const float bt = sigmoidf_(bv);
+    float* rd = &red[par][rho][0][0][0];
+    const RecNorms nr = rec_pass(S, &kqv_s[buf][D], &kqv_s[buf][0], rd, t256, scale, l2);
+    const int nbuf = buf == 2 ? 0 : buf + 1;
+    if (t + 1 < t1) conv_token(t + 1, nbuf);
     __syncthreads();
-    const float4 v4 = *reinterpret_cast<const float4*>(&kqv_s[par][2 * D + rho * D + col]);
+    const float4 v4 = *reinterpret_cast<const float4*>(&kqv_s[buf][2 * D + rho * D + col]);
     const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-    rec_token<TO>(S, &kqv_s[par][D], &kqv_s[par][0], vv, gt, bt, &red[par][rho][0][0][0], t256, scale, l2, o,
-                  t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
+    rec_finish<TO>(S, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
+                   t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
     if constexpr (SNAP) {   // the state after this token, for rolling back rejected draft tokens
       // (buffer stores off one per-lane offset: the row addresses are not kept live)
       const rsrc_t rs = make_rsrc(snap + (t * nv + h) * static_cast<int64_t>(D) * D, D * D * 4);
@@ -306,6 +336,8 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
                     make_uint4(__float_as_uint(S[i][0]), __float_as_uint(S[i][1]), __float_as_uint(S[i][2]),
                                __float_as_uint(S[i][3])));
     }
+    buf = nbuf;
+    par ^= 1;
   }
   {
     const int rg = t256 / CGN;
