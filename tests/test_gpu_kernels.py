@@ -248,6 +248,26 @@ def test_chunk_small(dtype, lengths, nk, nv):
     assert_close(fs, S_ref, TOL[dtype], "chunk final state")
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_chunk_random_shapes(seed):
+    """Seeded random shapes: 1-6 sequences of 0-199 tokens, 1-3 key heads with 1, 2 or 4 value heads each
+    (so the state kernel's work order takes each of its mappings), either dtype, with or without an
+    initial state; each against the oracle."""
+    rng = np.random.RandomState(1000 + seed)
+    dtype = ["f32", "bf16"][seed % 2]
+    nk = int(rng.choice([1, 2, 3]))
+    nv = nk * int(rng.choice([1, 2, 4]))
+    lengths = [int(v) for v in rng.randint(0, 200, size=int(rng.randint(1, 7)))]
+    if sum(lengths) == 0:
+        lengths[0] = 1
+    with_s0 = bool(rng.randint(0, 2))
+    _say("chunk random", seed, dtype, lengths, nk, nv, "S0" if with_s0 else "zero S0")
+    x = _inputs(dtype, lengths, nk, nv, s0_std=0.3, seed=500 + seed)
+    o, fs, o_ref, S_ref = _run_chunk(x, dtype, with_s0=with_s0)
+    assert_close(o, o_ref, TOL[dtype], "chunk o")
+    assert_close(fs, S_ref, TOL[dtype], "chunk final state")
+
+
 def test_chunk_zero_initial_state_and_alias():
     _say("chunk zero S0 / aliased state")
     x = _inputs("bf16", [190, 70], 1, 2, s0_std=0.3)

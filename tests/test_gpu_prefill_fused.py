@@ -11,6 +11,7 @@ conv bias, initial states, fp32 and bf16 gating inputs and outputs, a
 token-strided x view, and a batch with no tokens. Each test prints its case
 before touching the GPU.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -94,6 +95,27 @@ def test_prefill_fused_equals_separate_launches(ci):
     c = CASES[ci]
     _say("prefill_fused", c)
     d = _inputs(c, 70 + ci)
+    o_s, st_s, cs_s = _separate(d, c["nk"], c["nv"])
+    o_f, st_f, cs_f = _fused(d, c["nk"], c["nv"])
+    torch.cuda.synchronize()
+    _same(o_f, o_s, "o")
+    _same(st_f, st_s, "final state")
+    _same(cs_f, cs_s, "conv state out")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_fused_random_shapes(seed):
+    """Seeded random shapes (sequence count and lengths, head grouping, conv history and bias, initial state,
+    gating and output dtypes, x stride), each against the separate launches."""
+    rng = np.random.RandomState(2000 + seed)
+    nk = int(rng.choice([1, 2, 3]))
+    c = dict(name=f"random_{seed}", lengths=[int(v) for v in rng.randint(0, 180, size=int(rng.randint(1, 6)))],
+             nk=nk, nv=nk * int(rng.choice([1, 2, 4])), bias=bool(rng.randint(0, 2)),
+             conv_state=bool(rng.randint(0, 2)), s0=bool(rng.randint(0, 2)), ab=["bf16", "f32"][int(rng.randint(0, 2))],
+             o_dtype=["f32", "bf16"][int(rng.randint(0, 2))], pad=int(rng.choice([0, 8, 64])),
+             state_len=int(rng.choice([3, 4])))
+    _say("prefill_fused random", c)
+    d = _inputs(c, 300 + seed)
     o_s, st_s, cs_s = _separate(d, c["nk"], c["nv"])
     o_f, st_f, cs_f = _fused(d, c["nk"], c["nv"])
     torch.cuda.synchronize()
