@@ -65,6 +65,10 @@ int check_core(const char* fn, const void* q, const void* k, const void* v, int 
   if (vs == 0) vs = static_cast<int64_t>(nv) * dv;
   if (qs < static_cast<int64_t>(nk) * dk || ks < static_cast<int64_t>(nk) * dk || vs < static_cast<int64_t>(nv) * dv)
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: a token stride is smaller than one token's row", fn);
+  // chunk rows are addressed through 32-bit buffer offsets (64 rows of a stride)
+  constexpr int64_t kMaxStride = int64_t(1) << 24;
+  if (qs > kMaxStride || ks > kMaxStride || vs > kMaxStride)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: token strides above 2^24 elements are not supported", fn);
   if (T > 0) {
     if (!q || !k || !v || !g || !beta || !o)
       return fail(GDN_ERR_INVALID_ARGUMENT, "%s: q, k, v, g, beta and o are required", fn);

@@ -96,7 +96,8 @@ int gdn_gating(const void* a, const void* b, int ab_dtype,
  *   o      : [T_tot, nv, dv], o_dtype (fp32 recommended; bf16 rounds once)
  *   workspace : device buffer of at least gdn_chunk_fwd_workspace_size(...) bytes,
  *            256-byte aligned; its contents on entry are ignored.
- * Supported: dk = dv = 128; in_dtype f32 or bf16; nv % nk == 0.
+ * Supported: dk = dv = 128; in_dtype f32 or bf16; nv % nk == 0; token strides
+ * up to 2^24 elements.
  */
 size_t gdn_chunk_fwd_workspace_size(int64_t T_tot, int n_seqs, int nk, int nv,
                                     int dk, int dv, int in_dtype);
@@ -155,7 +156,7 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtyp
  *   cu_seqlens, scale, qk_l2norm, initial_state, final_state, o, workspace:
  *                as gdn_chunk_fwd, with the workspace size of
  *                gdn_chunk_fwd_workspace_size(T_tot, n_seqs, nk, nv, dk, dv, GDN_BF16)
- * Supported: dtype bf16, K = 4, dk = dv = 128, nv % nk == 0.
+ * Supported: dtype bf16, K = 4, dk = dv = 128, nv % nk == 0, x_tok_stride up to 2^24.
  */
 int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride,
                       const float* conv_weight, const float* conv_bias, int K,
@@ -178,7 +179,7 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride,
  *                sequence (then T_tot must equal n_seqs)
  *   state      : [n_seqs, nv, dk, dv] fp32, read and then overwritten in place
  *                with the state after each sequence's last token.
- * Supported: dk = dv = 128; in_dtype f32 or bf16.
+ * Supported: dk = dv = 128; in_dtype f32 or bf16; token strides up to 2^24 elements.
  */
 int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
                       int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,

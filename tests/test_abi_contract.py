@@ -61,6 +61,7 @@ def _chunk(L, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(nk=3, nv=4), INVALID),            # nv % nk != 0 (the pages' head-divisibility error)
     (dict(nk=0), INVALID),
+    (dict(vs=(1 << 24) + 8), UNSUPPORTED),   # chunk rows use 32-bit buffer offsets
     (dict(n=0), INVALID),
     (dict(T=-1), INVALID),
     (dict(in_dtype=7), INVALID),
