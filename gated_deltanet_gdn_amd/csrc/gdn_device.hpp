@@ -54,8 +54,19 @@ __device__ __forceinline__ void load8(const float* p, float (&out)[8]) {
 __device__ __forceinline__ float exp_(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ float exp_neg_(float x) { return exp_(-x); }
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_neg_(x)); }
+// log1p(y) for y >= 0 from the hardware log2 and reciprocal: with u = 1 + y
+// rounded, log1p(y) = ln(u) * y / (u - 1), or y when u rounds to 1. Dividing
+// by the rounded u - 1 cancels the rounding of u (Goldberg, "What Every
+// Computer Scientist Should Know About Floating-Point Arithmetic", 1991,
+// Theorem 4); with the about-1-ulp log2 and reciprocal the result stays
+// within a few ulps.
+__device__ __forceinline__ float log1p_pos_(float y) {
+  const float u = 1.0f + y;
+  const float d = u - 1.0f;
+  return d == 0.0f ? y : (__builtin_amdgcn_logf(u) * 0.6931471805599453f) * (y * __builtin_amdgcn_rcpf(d));
+}
 // log(1 + e^s) without overflow: max(s, 0) + log1p(e^{-|s|}).
-__device__ __forceinline__ float softplusf_(float s) { return fmaxf(s, 0.0f) + log1pf(exp_neg_(fabsf(s))); }
+__device__ __forceinline__ float softplusf_(float s) { return fmaxf(s, 0.0f) + log1p_pos_(exp_neg_(fabsf(s))); }
 __device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + exp_neg_(x)); }
 
 // ---------------------------------------------------------------- conv taps
