@@ -11,7 +11,7 @@
 // so the 64 KB fp32 state is read once into registers with contiguous float4
 // loads (each wave load covers 1 KB of rows) and written back once at the end. Per token both
 // Dk-reductions (S^T kh and S^T qh) share one pass over the registers:
-//   a = S^T kh, b = S^T qh (qh carries the scale; both formed on the raw k, q and scaled after)
+//   a = S^T kh, b = S^T qh (qh carries the scale)
 //   delta = beta (v - e a),  e = exp(g)
 //   o = e b + (kh . qh) delta          (= S'^T qh)
 //   S' = e S + kh delta^T
@@ -63,20 +63,19 @@ __device__ __forceinline__ RecNorms rec_pass(const float (&S)[RPT][4], const flo
   const float skk = wave_sum(k0 * k0 + k1 * k1);
   const float sqq = wave_sum(q0 * q0 + q1 * q1);
   const float sqk = wave_sum(q0 * k0 + q1 * k1);
-  const float rk = l2 ? rsqrtf(skk + 1e-6f) : 1.0f;
-  const float rq = (l2 ? rsqrtf(sqq + 1e-6f) : 1.0f) * scale;
+  const float rk = l2 ? 1.0f / sqrtf(skk + 1e-6f) : 1.0f;
+  const float rq = (l2 ? 1.0f / sqrtf(sqq + 1e-6f) : 1.0f) * scale;
   const float kq = sqk * rk * rq;
 
-  // S^T k and S^T q on the raw k and q; the norms scale the sums afterwards
   float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const float kr = ks[rg + RGN * i];
-    const float qr = qs[rg + RGN * i];
+    const float kh = ks[rg + RGN * i] * rk;
+    const float qh = qs[rg + RGN * i] * rq;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      pa[c] = fmaf(S[i][c], kr, pa[c]);
-      pb[c] = fmaf(S[i][c], qr, pb[c]);
+      pa[c] = fmaf(S[i][c], kh, pa[c]);
+      pb[c] = fmaf(S[i][c], qh, pb[c]);
     }
   }
   // the two row groups of a wave sit in lanes l and l ^ 32
@@ -99,7 +98,7 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], const float* ks, 
                                            float bt, const float* red, int t256, RecNorms nr, TO* __restrict__ o,
                                            int64_t ob) {
   const int cg = t256 % CGN, rg = t256 / CGN;
-  const float rk = nr.rk, rq = nr.rq, kq = nr.kq;
+  const float rk = nr.rk, kq = nr.kq;
   const float e = expf(gt);
   float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -109,14 +108,9 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], const float* ks, 
     a4[0] += ra.x; a4[1] += ra.y; a4[2] += ra.z; a4[3] += ra.w;
     b4[0] += rb.x; b4[1] += rb.y; b4[2] += rb.z; b4[3] += rb.w;
   }
-  float dl[4], kd[4];
+  float dl[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    a4[c] *= rk;
-    b4[c] *= rq;
-    dl[c] = bt * (vv[c] - e * a4[c]);
-    kd[c] = rk * dl[c];
-  }
+  for (int c = 0; c < 4; ++c) dl[c] = bt * (vv[c] - e * a4[c]);
   if (rg == 0) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) Elem<TO>::store(o, ob + c, fmaf(e, b4[c], kq * dl[c]));
@@ -125,9 +119,9 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], const float* ks, 
   // one more workgroup per CU)
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const float kr = ks[rg + RGN * i];
+    const float kh = ks[rg + RGN * i] * rk;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[i][c] = fmaf(e, S[i][c], kr * kd[c]);
+    for (int c = 0; c < 4; ++c) S[i][c] = fmaf(e, S[i][c], kh * dl[c]);
   }
 }
 template <typename TO>
