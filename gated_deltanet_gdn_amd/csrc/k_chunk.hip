@@ -200,8 +200,15 @@ __device__ __forceinline__ void split4_packed(float4 x, uint2& hi, uint2& lo) {
 }
 
 // lower 16x16 tiles of a 64x64 matrix, p = 0..9 -> (mi, mj), mi >= mj
-__device__ __forceinline__ int tile_mi(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
-__device__ __forceinline__ int tile_mj(int p) { const int mi = tile_mi(p); return p - mi * (mi + 1) / 2; }
+__host__ __device__ constexpr int tile_mi(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
+__host__ __device__ constexpr int tile_mj(int p) { return p - tile_mi(p) * (tile_mi(p) + 1) / 2; }
+// The tile pairs of prep wave w (slot u = 0..2, -1 = none). A wave's pairs
+// share row tiles, so each K or Q fragment it needs is read from LDS once per
+// k-step: w0 (3,0) (3,1) (3,2); w1 (3,3) (2,0) (2,1); w2 (2,2) (1,0);
+// w3 (1,1) (0,0).
+__device__ __forceinline__ int wave_pair(int w, int u) {
+  return w == 0 ? 6 + u : w == 1 ? (u == 0 ? 9 : 2 + u) : w == 2 ? (u == 0 ? 5 : u == 1 ? 1 : -1) : (u == 0 ? 2 : u == 1 ? 0 : -1);
+}
 
 // acc += A(16x16) * B(16x16), both fp32 in LDS (row pitches lda, ldb).
 template <bool BF>
@@ -299,7 +306,8 @@ __device__ __forceinline__ float exp_nonpos(double x) {
 
 // ------------------------------------------------------------------ prep
 // Four waves per (chunk, value head). The ten lower 16x16 tile pairs (mi, mj)
-// of the Grams, A and P are dealt round-robin (pair p goes to wave p % 4);
+// of the Grams, A and P are dealt out so that a wave's pairs share row tiles
+// (wave_pair);
 // wave w writes token tile w of every operand block; the off-diagonal blocks
 // of T are formed one level at a time with one wave per block.
 template <typename TIn>
@@ -311,6 +319,51 @@ constexpr size_t prep_lds_bytes() {
   return (tiles > at ? tiles : at) + CH * sizeof(double) + 4 * CH * sizeof(float);
 }
 constexpr int PREP_WAVES = 4;
+
+// k-step s of the Grams of tile pair P (K K^T and Q K^T, and Q Q^T on the
+// diagonal), from the K and Q tiles in LDS (row pitch EP)
+template <int P, typename TIn, int EP>
+__device__ __forceinline__ void gram_step(const TIn* Ks, const TIn* Qs, int lr, int lg, int s, f32x4& gkk,
+                                          f32x4& gqk, f32x4& gqq) {
+  if constexpr (P >= 0) {
+    constexpr int mi = tile_mi(P), mj = tile_mj(P);
+    constexpr bool BF = sizeof(TIn) == 2;
+    using MG = Mma<BF, true, true>;
+    constexpr int KS = MG::KS, KPL = MG::KPL;
+    if constexpr (BF) {   // raw bf16 fragments, one 16-byte LDS read each
+      const int kk = s * KS + KPL * lg;
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + (16 * mi + lr) * EP + kk);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + (16 * mi + lr) * EP + kk);
+      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Ks + (16 * mj + lr) * EP + kk);
+      gkk = mfma_bf16(ak, bk, gkk);
+      gqk = mfma_bf16(aq, bk, gqk);
+      if constexpr (mi == mj) gqq = mfma_bf16(aq, aq, gqq);
+    } else {
+      float ak[KPL], aq[KPL], bk[KPL];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int kk = s * KS + KPL * lg + j;
+        ak[j] = tof(Ks[(16 * mi + lr) * EP + kk]);
+        aq[j] = tof(Qs[(16 * mi + lr) * EP + kk]);
+        bk[j] = tof(Ks[(16 * mj + lr) * EP + kk]);
+      }
+      MG::run(gkk, ak, bk);
+      MG::run(gqk, aq, bk);
+      if constexpr (mi == mj) MG::run(gqq, aq, aq);
+    }
+  }
+}
+template <int P0, int P1, int P2, typename TIn, int EP>
+__device__ __forceinline__ void gram_pairs(const TIn* Ks, const TIn* Qs, int lr, int lg, f32x4 (&gkk)[3],
+                                           f32x4 (&gqk)[3], f32x4 (&gqq)[3]) {
+  constexpr int KS = Mma<sizeof(TIn) == 2, true, true>::KS;
+#pragma unroll
+  for (int s = 0; s < D / KS; ++s) {
+    gram_step<P0, TIn, EP>(Ks, Qs, lr, lg, s, gkk[0], gqk[0], gqq[0]);
+    gram_step<P1, TIn, EP>(Ks, Qs, lr, lg, s, gkk[1], gqk[1], gqq[1]);
+    gram_step<P2, TIn, EP>(Ks, Qs, lr, lg, s, gkk[2], gqk[2], gqq[2]);
+  }
+}
 
 // Causal conv1d (4 taps) + SiLU folded into the chunk kernels: x holds the
 // packed q | k | v channels (conv_dim = 2 nk D + nv D, bf16); the conv state
@@ -342,8 +395,6 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     uint16_t* __restrict__ qf, ConvIn cv) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int EP = prep_pitch<TIn>();
-  using MG = Mma<BF, true, true>;
-  constexpr int KS = MG::KS, KPL = MG::KPL;
   constexpr size_t tiles = 2 * CH * EP * sizeof(TIn);
   constexpr size_t at = 2 * CH * AP * sizeof(float);
   constexpr size_t head = tiles > at ? tiles : at;
@@ -465,34 +516,11 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     gkk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     gqk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     gqq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int p = wv + 4 * u;
-    if (p >= 10) break;
-    const int mi = tile_mi(p), mj = tile_mj(p);
-#pragma unroll
-    for (int s = 0; s < D / KS; ++s) {
-      if constexpr (BF) {   // raw bf16 fragments, one 16-byte LDS read each
-        const int kk = s * KS + KPL * lg;
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + (16 * mi + lr) * EP + kk);
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + (16 * mi + lr) * EP + kk);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Ks + (16 * mj + lr) * EP + kk);
-        gkk[u] = mfma_bf16(ak, bk, gkk[u]);
-        gqk[u] = mfma_bf16(aq, bk, gqk[u]);
-        if (mi == mj) gqq[u] = mfma_bf16(aq, aq, gqq[u]);
-      } else {
-        float ak[KPL], aq[KPL], bk[KPL];
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const int kk = s * KS + KPL * lg + j;
-          ak[j] = tof(Ks[(16 * mi + lr) * EP + kk]);
-          aq[j] = tof(Qs[(16 * mi + lr) * EP + kk]);
-          bk[j] = tof(Ks[(16 * mj + lr) * EP + kk]);
-        }
-        MG::run(gkk[u], ak, bk);
-        MG::run(gqk[u], aq, bk);
-        if (mi == mj) MG::run(gqq[u], aq, aq);
-      }
-    }
   }
+  if (wv == 0) gram_pairs<6, 7, 8, TIn, EP>(Ks, Qs, lr, lg, gkk, gqk, gqq);
+  else if (wv == 1) gram_pairs<9, 3, 4, TIn, EP>(Ks, Qs, lr, lg, gkk, gqk, gqq);
+  else if (wv == 2) gram_pairs<5, 1, -1, TIn, EP>(Ks, Qs, lr, lg, gkk, gqk, gqq);
+  else gram_pairs<2, 0, -1, TIn, EP>(Ks, Qs, lr, lg, gkk, gqk, gqq);
   // 3. bf16 inputs: K and Q operand blocks of the state recurrence, once
   //     per key head: K by its first value head, Q by its last; wave wv
   //     writes token tile wv
@@ -505,8 +533,8 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   // 4. |k_i|^2 and |q_i|^2 from the Gram diagonals (pairs 0, 2, 5, 9)
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
-    const int p = wv + 4 * u;
-    if (p >= 10) break;
+    const int p = wave_pair(wv, u);
+    if (p < 0) break;
     const int mi = tile_mi(p), mj = tile_mj(p);
     if (mi == mj && lr >= 4 * lg && lr < 4 * lg + 4) {
       const int row = 16 * mi + lr;
@@ -545,7 +573,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     float rkc[NP], ar[NP][4], pr[NP][4];
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-      const int p = min(wv + 4 * u, 9);
+      const int p = max(wave_pair(wv, u), 0);
       const int mi = tile_mi(p), mj = tile_mj(p);
       Gc[u] = Gs[16 * mj + lr];
       rkc[u] = rk_s[16 * mj + lr];
@@ -559,8 +587,8 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     }
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-      const int p = wv + 4 * u;
-      if (p >= 10) break;
+      const int p = wave_pair(wv, u);
+      if (p < 0) break;
       const int mi = tile_mi(p), mj = tile_mj(p);
       const int j = 16 * mj + lr;
 #pragma unroll
@@ -616,8 +644,8 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   // 8. P into the upper triangle turned by 180 degrees: X[63-i][63-j] = P[i][j], j <= i
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
-    const int p = wv + 4 * u;
-    if (p >= 10) break;
+    const int p = wave_pair(wv, u);
+    if (p < 0) break;
     const int mi = tile_mi(p), mj = tile_mj(p);
     const int j = 16 * mj + lr;
 #pragma unroll
