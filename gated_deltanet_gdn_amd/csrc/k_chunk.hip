@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   }
   __syncthreads();
 
-  // 2. Grams on this wave's lower 16x16 tile pairs p = wv + 4 u, kept in
+  // 2. Grams on this wave's lower 16x16 tile pairs (wave_pair), kept in
   //    registers; on the diagonal pairs also Q Q^T, whose diagonal is |q_i|^2
   //    (|k_i|^2 is the diagonal of K K^T)
   constexpr int NP = 3;
