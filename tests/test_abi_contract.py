@@ -291,3 +291,23 @@ def _prefill(L, **kw):
 def test_prefill_fused_argument_errors(L, kw, status):
     assert _prefill(L, **kw) == status
     assert gdn.gdn_last_error() != ""
+
+
+def _declared_arg_counts():
+    """Number of parameters of every function declared in gdn.h (comments stripped)."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, args in re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", src, flags=re.S):
+        args = args.strip()
+        out[name] = 0 if args in ("", "void") else len(args.split(","))
+    return out
+
+
+def test_binding_signatures_match_the_header(L):
+    """The ctypes binding declares the same number of arguments as the C header, for every entry point."""
+    decl = _declared_arg_counts()
+    assert len(decl) >= 10
+    for name, n in decl.items():
+        fn = getattr(L, name)
+        assert fn.argtypes is not None, f"{name}: no argtypes in the binding"
+        assert len(fn.argtypes) == n, f"{name}: header has {n} arguments, binding {len(fn.argtypes)}"
