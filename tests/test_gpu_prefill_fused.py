@@ -130,8 +130,12 @@ def test_prefill_fused_called_twice_gives_the_same_bits():
     _say("prefill_fused twice", c["name"])
     big = _inputs(dict(c, lengths=[300, 200, 129]), 90)
     small = _inputs(c, 71)
-    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(600, 8, 1, 2, DK, DK, gdn.BF16), device=dev(), dtype=torch.uint8)
-    _fused(big, 1, 2)
+    need = max(gdn.gdn_chunk_fwd_workspace_size(629, 3, 1, 2, DK, DK, gdn.BF16),
+               gdn.gdn_chunk_fwd_workspace_size(401, 8, 1, 2, DK, DK, gdn.BF16))
+    ws = torch.empty(need, device=dev(), dtype=torch.uint8)
+    gdn.gdn_prefill_fused(big["x"], big["conv_w"], big["a"], big["b"], big["A_log"], big["dt_bias"], 1, 2,
+                          conv_bias=big["bias"], cu_seqlens=big["cu"], conv_state_in=big["conv_state"],
+                          initial_state=big["s0"], o_dtype=big["o_dtype"], workspace=ws)
     r1 = gdn.gdn_prefill_fused(small["x"], small["conv_w"], small["a"], small["b"], small["A_log"],
                                small["dt_bias"], 1, 2, conv_bias=small["bias"], cu_seqlens=small["cu"],
                                conv_state_in=small["conv_state"], initial_state=small["s0"],
