@@ -3,7 +3,8 @@
 Each workload runs on the GPU exactly as the benchmark launches it (the
 binding's defaults). Checks:
   * tiny chunk fp32 (T=256, 1->2 heads) and prefill T=8192 (16->32 heads):
-    every output and final state against the oracle;
+    every output and final state against the oracle, and the benchmark's
+    gated chunk call equal to gating + chunk bit for bit;
   * varlen packed prefill (8 sequences, nonzero initial states): every head
     of every sequence;
   * decode step (256 sequences, 512 MiB state in place): stage-wise --
@@ -41,10 +42,14 @@ def _chunk_config(name):
     x = W.chunk_inputs(wl)
     d = {k: (v.to(dev()) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
     _say(name, "gpu", "T =", int(x["cu_seqlens"][-1]))
+    cu = d["cu_seqlens"] if wl.len_range else None
     g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
-    o, st = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta,
-                              cu_seqlens=d["cu_seqlens"] if wl.len_range else None, initial_state=d["S0"])
+    o, st = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, cu_seqlens=cu, initial_state=d["S0"])
+    # the benchmark's entry point (gating folded into the chunk call) gives the same bits
+    o2, st2 = gdn.gdn_chunk_fwd_gated(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                      cu_seqlens=cu, initial_state=d["S0"])
     torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(st2, st), f"{name}: gated call differs from gating + chunk"
     _say(name, "oracle")
     g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
     o_ref, s_ref = oracle.delta_rule(f64(x["q"]), f64(x["k"]), f64(x["v"]), g_ref, b_ref,
