@@ -348,6 +348,34 @@ def test_chunk_reset_and_orthonormal_keys():
     assert_close(keys[:, 0].double().numpy() @ f64(fs)[0, 0], f64(v)[:, 0], TOL["f32"], "values retrievable")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_and_recurrent_without_l2norm_custom_scale(dtype):
+    """qk_l2norm = 0 and an explicit scale, on keys and queries of about unit norm (q, k drawn N(0, 1/128)),
+    for the chunked rule and the recurrent rule against the oracle."""
+    _say("no l2norm, scale 0.3", dtype)
+    lengths, nk, nv = [150, 1, 77], 1, 2
+    x = _inputs(dtype, lengths, nk, nv, s0_std=0.3, seed=41)
+    TD = W.TORCH_DTYPE[dtype]
+    for key in ("q", "k"):   # rescale in fp32, then back to the workload dtype (the oracle reads the same values)
+        x[key] = (x[key].float() * (128 ** -0.5)).to(TD)
+    d = _to(x, dev())
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    o, fs = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, cu_seqlens=d["cu_seqlens"], initial_state=d["S0"],
+                              scale=0.3, qk_l2norm=False)
+    st = d["S0"].clone()
+    o_r = gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], g, beta, st, cu_seqlens=d["cu_seqlens"], scale=0.3,
+                                qk_l2norm=False)
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gating(f64(x["a"]), f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]))
+    o_ref, S_ref = oracle.delta_rule(f64(x["q"]), f64(x["k"]), f64(x["v"]), g_ref, b_ref,
+                                     cu_seqlens=x["cu_seqlens"].numpy(), initial_state=f64(x["S0"]), scale=0.3,
+                                     l2norm=False)
+    assert_close(o, o_ref, TOL[dtype], "chunk o (no l2norm)")
+    assert_close(fs, S_ref, TOL[dtype], "chunk state (no l2norm)")
+    assert_close(o_r, o_ref, TOL[dtype], "recurrent o (no l2norm)")
+    assert_close(st, S_ref, TOL[dtype], "recurrent state (no l2norm)")
+
+
 # ------------------------------------------------------------------ device graphs of the small kernels
 
 def test_gating_and_conv_update_in_a_device_graph():
