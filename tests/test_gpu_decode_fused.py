@@ -130,6 +130,39 @@ def test_fused_multi_token(dtype, nk, nv, lengths):
     np.testing.assert_array_equal(f64(cs), cs_ref)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_with_conv_bias_and_custom_scale(dtype):
+    """conv bias, an explicit read-out scale and a token-strided x: the fused step against the separate
+    conv (with the same bias), gating and recurrent launches, bit for bit, one token and several per sequence."""
+    nk, nv = 2, 4
+    for lengths in (None, [3, 1, 0, 4]):
+        _say("fused decode with conv bias and scale 0.2", dtype, lengths)
+        wl = W.Workload("fused_bias", 13, "decode", dtype, n_seqs=6, nk=nk, nv=nv, s0_std=0.02)
+        x = W.decode_inputs(wl) if lengths is None else W.decode_mtp_inputs(wl, lengths)
+        d = _to(x)
+        C = d["x"].shape[1]
+        wide = torch.zeros((d["x"].shape[0], C + 24), device=dev(), dtype=d["x"].dtype)
+        wide[:, :C] = d["x"]
+        xs = wide[:, :C]                                  # token stride C + 24
+        bias = W.randn((C,), 13, 99, "f32", std=0.1).to(dev())
+        cu = d["cu_seqlens"] if lengths is not None else None
+        conv_state, state = d["conv_state"].clone(), d["state"].clone()
+        o = gdn.gdn_decode_step_fused(xs, conv_state, d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], state,
+                                      nk, cu_seqlens=cu, conv_bias=bias, scale=0.2)
+        state2 = d["state"].clone()
+        if cu is None:
+            conv_state2 = d["conv_state"].clone()
+            y = gdn.gdn_causal_conv1d_update(xs.contiguous(), conv_state2, d["conv_w"], bias=bias)
+        else:
+            y, conv_state2 = gdn.gdn_causal_conv1d(xs, d["conv_w"], bias=bias, cu_seqlens=cu,
+                                                   conv_state_in=d["conv_state"])
+        q, k, v = _qkv(y, nk, nv)
+        g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"])
+        o2 = gdn.gdn_recurrent_fwd(q, k, v, g, beta, state2, cu_seqlens=cu, scale=0.2)
+        torch.cuda.synchronize()
+        _same(o, o2, "o"); _same(state, state2, "state"); _same(conv_state, conv_state2, "conv state")
+
+
 def test_fused_state_len_above_window():
     _say("fused decode, conv state of 5 entries")
     nk, nv, lengths = 2, 4, [1, 2, 7, 0]
