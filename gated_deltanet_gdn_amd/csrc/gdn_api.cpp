@@ -80,6 +80,15 @@ int check_core(const char* fn, const void* q, const void* k, const void* v, int 
   return GDN_OK;
 }
 
+// The chunk kernels launch one workgroup per (chunk slot, value head) and
+// one per (sequence, value head, 16 columns) in one-dimensional grids.
+int check_chunk_grid(const char* fn, int64_t T, int n_seqs, int nv) {
+  const int64_t slots = T / 64 + n_seqs;
+  if (slots * nv > INT32_MAX || static_cast<int64_t>(n_seqs) * nv * 8 > INT32_MAX)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many (chunk, head) units for one launch", fn);
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,6 +139,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype, int
   if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
   if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
   if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  if (const int gst = check_chunk_grid(fn, T_tot, n_seqs, nv); gst != GDN_OK) return gst;
   const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, in_dtype == GDN_BF16);
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
@@ -158,6 +168,7 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtyp
   if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
   if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
   if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  if (const int gst = check_chunk_grid(fn, T_tot, n_seqs, nv); gst != GDN_OK) return gst;
   const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, in_dtype == GDN_BF16);
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
@@ -201,6 +212,7 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const floa
   if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
   if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
   if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+  if (const int gst = check_chunk_grid(fn, T_tot, n_seqs, nv); gst != GDN_OK) return gst;
   const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, 1);
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);

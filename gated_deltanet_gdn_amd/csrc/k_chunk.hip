@@ -413,8 +413,9 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   // heads vary fastest: the value heads of one key head, and the per-token
   // g and beta of all heads (one cache line per token), are read by
   // neighbouring workgroups
-  const int h = blockIdx.x;
-  const int c = blockIdx.y;
+  // one-dimensional grid (its y dimension would cap the chunk count at 65536)
+  const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(nv));
+  const int c = static_cast<int>(blockIdx.x / static_cast<unsigned>(nv));
   const int hk = h / (nv / nk);
   const int total = cu ? chunk_off[n_seqs] : static_cast<int>((T + CH - 1) / CH);
   if (c >= total) return;
@@ -1494,7 +1495,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    kern<<<dim3(static_cast<unsigned>(nv), static_cast<unsigned>(nch)), 64 * PREP_WAVES, lds, s>>>(
+    kern<<<dim3(static_cast<unsigned>(nv * nch)), 64 * PREP_WAVES, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, ga, gb, A_log, dt_bias, cu, n_seqs, T, nk, nv,
         scale, l2, chunk_off, tp, sc, egc, kf, qf, cv);
     e = hipGetLastError();
