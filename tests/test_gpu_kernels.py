@@ -444,3 +444,28 @@ def test_batches_without_tokens():
                   (fs, "fused decode state")):
         assert torch.equal(t, S0), f"{nm} changed without tokens"
     assert torch.equal(cs, cs0), "conv state changed without tokens"
+
+
+def test_chunk_more_than_65536_chunks():
+    """A call of more than 65536 chunks (one sequence of 4.19 M tokens, 1 -> 2 heads): its last tokens and
+    final state equal, bit for bit, a second call over those tokens started from the state a first call
+    leaves at a chunk boundary (no part of the long call is dropped or repeated)."""
+    T0 = 65536 * 64 - 64
+    T = T0 + 164
+    _say("chunk call over", T, "tokens,", (T + 63) // 64, "chunks")
+    D = dev()
+    q = W.randn((T, 1, 128), 77, 1, "bf16", device=D)
+    k = W.randn((T, 1, 128), 77, 2, "bf16", device=D)
+    v = W.randn((T, 2, 128), 77, 3, "bf16", device=D)
+    a = W.randn((T, 2), 77, 4, "bf16", device=D)
+    b = W.randn((T, 2), 77, 5, "bf16", device=D)
+    A_log = W.a_log(2, 77, D)
+    dt_bias = W.randn((2,), 77, 7, "f32", std=0.1, device=D)
+    o_all, s_all = gdn.gdn_chunk_fwd_gated(q, k, v, a, b, A_log, dt_bias)
+    _, s_mid = gdn.gdn_chunk_fwd_gated(q[:T0], k[:T0], v[:T0], a[:T0], b[:T0], A_log, dt_bias)
+    o_tail, s_tail = gdn.gdn_chunk_fwd_gated(q[T0:], k[T0:], v[T0:], a[T0:].contiguous(), b[T0:].contiguous(),
+                                             A_log, dt_bias, initial_state=s_mid)
+    torch.cuda.synchronize()
+    assert torch.equal(o_tail, o_all[T0:]), "last tokens of the long call"
+    assert torch.equal(s_tail, s_all), "final state of the long call"
+    assert torch.isfinite(o_all[::4096]).all()
