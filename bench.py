@@ -276,6 +276,17 @@ def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
                 reps, warmup, stream)
     rows["gated_rmsnorm"] = _hbm_row(f"long_fused_t256k: {T * wl.nv} rows of {wl.dv}, x fp32, z bf16 -> y fp32", ms,
                                      T * wl.nv * wl.dv * (4 + 2 + 4) + wl.dv * 4, "gated_rmsnorm_kernel")
+    # the whole long pipeline: the fused prefill (conv, gating, chunk rule) then the gated RMSNorm epilogue
+    ws2 = torch.empty(gdn.gdn_chunk_fwd_workspace_size(T, 1, wl.nk, wl.nv), device=dev, dtype=torch.uint8)
+    ms = _timed(lambda: (gdn.gdn_prefill_fused(x["x"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"], wl.nk,
+                                               wl.nv, state_len=wl.state_len, final_state=st, o=o, workspace=ws2,
+                                               output_conv_state=False, stream=stream),
+                         gdn.gdn_gated_rmsnorm(o, x["z"], x["norm_w"], eps=1e-6, y=out, stream=stream)),
+                max(2, reps // 2), 1, stream)
+    rows["long_prefill_pipeline"] = dict(
+        workload=f"long_fused_t256k: conv + SiLU, gating, chunk rule (one call), then gated RMSNorm, T={T}",
+        kernel="gdn_prefill_fused + gdn_gated_rmsnorm", avg_ms=round(ms, 4), tokens_per_s=round(T / (ms * 1e-3), 1))
+    del ws2
     del x, o, out, st
     dw = W.WORKLOADS["decode_256seq"]
     dx = {kk: vv.to(dev) for kk, vv in W.decode_inputs(dw).items()}
