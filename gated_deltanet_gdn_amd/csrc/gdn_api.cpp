@@ -80,12 +80,36 @@ int check_core(const char* fn, const void* q, const void* k, const void* v, int 
   return GDN_OK;
 }
 
-// The chunk kernels launch one workgroup per (chunk slot, value head) and
-// one per (sequence, value head, 16 columns) in one-dimensional grids.
+// One dispatch holds at most 2^32 - 1 work-items and 2^31 - 1 workgroups in
+// its one-dimensional grid.
+bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks <= INT32_MAX && blocks * threads <= static_cast<int64_t>(UINT32_MAX);
+}
+
+// The chunk kernels launch 256 threads per (chunk slot, value head) and per
+// (sequence, value head, 16 columns), in one-dimensional grids.
 int check_chunk_grid(const char* fn, int64_t T, int n_seqs, int nv) {
   const int64_t slots = T / 64 + n_seqs;
-  if (slots * nv > INT32_MAX || static_cast<int64_t>(n_seqs) * nv * 8 > INT32_MAX)
+  if (!grid_fits(slots * nv, 256) || !grid_fits(static_cast<int64_t>(n_seqs) * nv * 8, 256))
     return fail(GDN_ERR_UNSUPPORTED, "%s: too many (chunk, head) units for one launch", fn);
+  return GDN_OK;
+}
+
+// Checks shared by the two entry points of the chunked rule with the gating
+// folded in; qs, ks, vs and scale come back resolved (0 = dense, <= 0 = dk^-1/2).
+int check_chunk_gated(const char* fn, const void* q, const void* k, const void* v, int in_dtype, int64_t& qs,
+                      int64_t& ks, int64_t& vs, const void* a, const void* b, int ab_dtype, const float* A_log,
+                      const float* dt_bias, const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv,
+                      int dk, int dv, float& scale, const void* o, int o_dtype) {
+  if (!valid_dtype(ab_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: ab_dtype %d is not f32/bf16", fn, ab_dtype);
+  // a and b stand where g and beta stand in the shared checks
+  const int st = check_core(fn, q, k, v, in_dtype, qs, ks, vs, static_cast<const float*>(a),
+                            static_cast<const float*>(b), n_seqs, T_tot, nk, nv, dk, dv, o, o_dtype);
+  if (st != GDN_OK) return st;
+  if (!A_log || !dt_bias) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: A_log and dt_bias are required", fn);
+  if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
+  if (const int gst = check_chunk_grid(fn, T_tot, n_seqs, nv); gst != GDN_OK) return gst;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
   return GDN_OK;
 }
 
@@ -116,6 +140,8 @@ int gdn_gating(const void* a, const void* b, int ab_dtype, const float* A_log, c
   if (T_tot > 0 && (!a || !b || !g || !beta))
     return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_gating: a, b, g and beta are required");
   if (T_tot == 0) return ok();
+  if (!grid_fits((T_tot * nv + 255) / 256, 256))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_gating: too many (token, head) elements for one launch");
   return launched(gdn::launch_gating(a, b, ab_dtype == GDN_BF16, A_log, dt_bias, T_tot, nv, g, beta,
                                      static_cast<hipStream_t>(stream)),
                   "gdn_gating");
@@ -159,20 +185,14 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtyp
                         size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_chunk_fwd_gated";
   int64_t qs = q_tok_stride, ks = k_tok_stride, vs = v_tok_stride;
-  if (!valid_dtype(ab_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: ab_dtype %d is not f32/bf16", fn, ab_dtype);
-  // a and b stand where g and beta stand in the shared checks
-  const int st = check_core(fn, q, k, v, in_dtype, qs, ks, vs, static_cast<const float*>(a),
-                            static_cast<const float*>(b), n_seqs, T_tot, nk, nv, dk, dv, o, o_dtype);
+  const int st = check_chunk_gated(fn, q, k, v, in_dtype, qs, ks, vs, a, b, ab_dtype, A_log, dt_bias, cu_seqlens,
+                                   n_seqs, T_tot, nk, nv, dk, dv, scale, o, o_dtype);
   if (st != GDN_OK) return st;
-  if (!A_log || !dt_bias) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: A_log and dt_bias are required", fn);
-  if (!cu_seqlens && n_seqs != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is required when n_seqs > 1", fn);
   if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
   if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
-  if (const int gst = check_chunk_grid(fn, T_tot, n_seqs, nv); gst != GDN_OK) return gst;
   const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, in_dtype == GDN_BF16);
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
-  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
   return launched(gdn::launch_chunk_fwd(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, a, b, ab_dtype == GDN_BF16 ? 1 : 2,
                                         A_log, dt_bias, cu_seqlens, n_seqs, T_tot, nk, nv, scale, qk_l2norm != 0,
                                         initial_state, final_state, o, o_dtype == GDN_BF16, workspace,
@@ -216,6 +236,8 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const floa
   const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, 1);
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (conv_state_out && !grid_fits((static_cast<int64_t>(n_seqs) * conv_dim + 255) / 256, 256))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many (seq, channel) units for one launch", fn);
   if (conv_state_in && conv_state_out) {
     const size_t bytes = static_cast<size_t>(n_seqs) * conv_dim * state_len * 2;
     const char* a0 = static_cast<const char*>(conv_state_in);
@@ -247,7 +269,9 @@ int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
   if (!aligned(state, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: state must be 16-byte aligned", fn);
   if (!cu_seqlens && T_tot != n_seqs)
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: without cu_seqlens T_tot must equal n_seqs (one token each)", fn);
-  if (static_cast<int64_t>(n_seqs) * nv > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: too many (seq, head) units", fn);
+  // 256 threads per (sequence, value head) state
+  if (!grid_fits(static_cast<int64_t>(n_seqs) * nv, 256))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many (seq, head) units for one launch", fn);
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(dk));
   return launched(gdn::launch_recurrent(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, g, beta, cu_seqlens, n_seqs, T_tot, nk,
                                         nv, scale, qk_l2norm != 0, state, o, o_dtype == GDN_BF16,
@@ -290,7 +314,9 @@ int gdn_decode_step_fused(const void* x, int dtype, int64_t x_tok_stride, void* 
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x token stride smaller than conv_dim (%lld)", fn,
                 static_cast<long long>(conv_dim));
   if (T_tot > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: T_tot above 2^31-1", fn);
-  if (static_cast<int64_t>(n_seqs) * nk > INT32_MAX) return fail(GDN_ERR_UNSUPPORTED, "%s: too many workgroups", fn);
+  // one workgroup of 256 threads per value head for each (sequence, key head)
+  if (!grid_fits(static_cast<int64_t>(n_seqs) * nk, 256LL * (nv / nk)))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many (seq, head) units for one launch", fn);
   if (!aligned(state, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: state must be 16-byte aligned", fn);
   if (state_indices) {
     if (n_slots <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: n_slots must be >= 1 with state_indices", fn);
@@ -328,6 +354,9 @@ int gdn_causal_conv1d(const void* x, int dtype, int64_t x_tok_stride, const floa
     if (x_tok_stride % 8) return fail(GDN_ERR_UNSUPPORTED, "%s: x token stride must be a multiple of 8", fn);
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: x and y must be 16-byte aligned", fn);
   }
+  // grid x: 64 tokens per thread, 256 threads per workgroup; the state-out pass one thread per (seq, channel)
+  if (!grid_fits((T_tot + 63) / 64, 256) || !grid_fits((static_cast<int64_t>(n_seqs) * conv_dim + 255) / 256, 256))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many tokens or (seq, channel) units for one launch", fn);
   if (conv_state_in && conv_state_out) {
     const size_t bytes = static_cast<size_t>(n_seqs) * conv_dim * state_len * dsize(dtype);
     const char* a0 = static_cast<const char*>(conv_state_in);
@@ -352,6 +381,8 @@ int gdn_causal_conv1d_update(const void* x, int dtype, void* conv_state, int sta
   if (!weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: weight is required", fn);
   if (n_seqs == 0) return ok();
   if (!x || !conv_state || !y) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, conv_state and y are required", fn);
+  if (!grid_fits((static_cast<int64_t>(n_seqs) * conv_dim + 255) / 256, 256))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many (seq, channel) units for one launch", fn);
   return launched(gdn::launch_causal_conv1d_update(x, dtype == GDN_BF16, conv_state, state_len, weight, bias, n_seqs,
                                                    conv_dim, silu != 0, y, static_cast<hipStream_t>(stream)),
                   fn);
@@ -368,7 +399,7 @@ int gdn_gated_rmsnorm(const void* x, int x_dtype, const void* z, int z_dtype, co
   if (!weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: weight is required", fn);
   if (rows == 0) return ok();
   if (!x || !z || !y) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: x, z and y are required", fn);
-  if (rows > static_cast<int64_t>(UINT32_MAX) * 8) return fail(GDN_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  if (!grid_fits((rows + 7) / 8, 256)) return fail(GDN_ERR_UNSUPPORTED, "%s: too many rows for one launch", fn);
   return launched(gdn::launch_gated_rmsnorm(x, x_dtype == GDN_BF16, z, z_dtype == GDN_BF16, weight, rows, D, eps, y,
                                             y_dtype == GDN_BF16, static_cast<hipStream_t>(stream)),
                   fn);

@@ -311,3 +311,19 @@ def test_binding_signatures_match_the_header(L):
         fn = getattr(L, name)
         assert fn.argtypes is not None, f"{name}: no argtypes in the binding"
         assert len(fn.argtypes) == n, f"{name}: header has {n} arguments, binding {len(fn.argtypes)}"
+
+
+def test_launches_beyond_2_32_work_items_are_rejected_on_the_host(L):
+    """One dispatch holds at most 2^32 - 1 work-items: every entry point rejects larger grids with
+    UNSUPPORTED before enqueuing anything (no HIP call is reached with these arguments)."""
+    n = 1 << 21   # 2^21 sequences x 8 value heads x 256 threads = 2^32 work-items
+    assert _rec(L, n=n, T=n, nk=8, nv=8) == UNSUPPORTED
+    assert _fused(L, n=n, T=n, nk=8, nv=8, n_slots=n) == UNSUPPORTED
+    # chunk state kernel: 8 column slices x 256 threads per (sequence, value head)
+    assert _chunk(L, cu=P, n=1 << 19, T=1 << 19, nk=4, nv=8) == UNSUPPORTED
+    # gated RMSNorm: 8 rows per 256-thread workgroup
+    assert L.gdn_gated_rmsnorm(P, 0, P, 1, P, 1 << 30, 128, ctypes.c_float(1e-6), P2, 0, NULL) == UNSUPPORTED
+    # gating: one thread per (token, head) in the worst case
+    assert L.gdn_gating(P, P, 1, P, P, 1 << 30, 8, P2, P2, NULL) == UNSUPPORTED
+    # conv update: one thread per (sequence, channel)
+    assert L.gdn_causal_conv1d_update(P, 1, P, 3, P, NULL, 1 << 20, 1 << 12, 4, 1, P2, NULL) == UNSUPPORTED
