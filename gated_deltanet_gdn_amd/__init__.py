@@ -20,7 +20,7 @@ __all__ = [
     "gdn_abi_version", "gdn_status_string", "gdn_last_error",
     "gdn_gating", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_recurrent_fwd",
     "gdn_causal_conv1d", "gdn_causal_conv1d_update", "gdn_gated_rmsnorm", "gdn_decode_step_fused",
-    "gdn_prefill_fused",
+    "gdn_prefill_fused", "gdn_chunk_fwd_noalloc_max_bytes", "gdn_chunk_fwd_gated_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -60,6 +60,9 @@ def lib():
         "gdn_causal_conv1d": (i32, [vp, i32, i64, vp, vp, vp, i32, i64, i32, i32, vp, vp, i32, i32, vp, vp]),
         "gdn_causal_conv1d_update": (i32, [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp]),
         "gdn_gated_rmsnorm": (i32, [vp, i32, vp, i32, vp, i64, i32, f32, vp, i32, vp]),
+        "gdn_chunk_fwd_noalloc_max_bytes": (sz, []),
+        "gdn_chunk_fwd_gated_noalloc": (i32, [vp, vp, vp, i32, i64, i64, i64, vp, vp, i32, vp, vp, vp, i32, i64, i32,
+                                              i32, i32, i32, f32, i32, vp, vp, vp, i32, vp]),
         "gdn_prefill_fused": (i32, [vp, i32, i64, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i64,
                                     i32, i32, i32, i32, f32, i32, vp, vp, vp, i32, vp, sz, vp]),
         "gdn_decode_step_fused": (i32, [vp, i32, i64, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, i32, i64, i32, i32,
@@ -211,6 +214,38 @@ def gdn_chunk_fwd_gated(q, k, v, a, b, A_log, dt_bias, cu_seqlens=None, initial_
                                    _ptr(final_state), _ptr(o), _dt(o, "o"), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _check("gdn_chunk_fwd_gated", st)
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc_max_bytes() -> int:
+    return lib().gdn_chunk_fwd_noalloc_max_bytes()
+
+
+def gdn_chunk_fwd_gated_noalloc(q, k, v, a, b, A_log, dt_bias, cu_seqlens=None, initial_state=None,
+                                output_final_state=True, final_state=None, o=None, o_dtype=torch.float32,
+                                scale=None, qk_l2norm=True, stream=None):
+    """gdn_chunk_fwd_gated with the library's per-device scratch array as its workspace (the C call
+    allocates nothing; outputs not passed in are allocated here by torch). Calls that overlap in time
+    on one GPU share that array and race. Returns (o, final_state)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, contiguous=False)
+    qs, ks, vs = _tok_view(q, "q"), _tok_view(k, "k"), _tok_view(v, "v")
+    _need(a, "a"); _need(b, "b", a.dtype)
+    _need(A_log, "A_log", torch.float32); _need(dt_bias, "dt_bias", torch.float32)
+    T, nk, dk = q.shape
+    nv, dv = v.shape[1], v.shape[2]
+    cu, n = _cu(cu_seqlens, T)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, nv, dk, dv), device=q.device, dtype=torch.float32)
+    if o is None:
+        o = torch.empty((T, nv, dv), device=q.device, dtype=o_dtype)
+    st = lib().gdn_chunk_fwd_gated_noalloc(_ptr(q), _ptr(k), _ptr(v), _dt(q, "q"), qs, ks, vs, _ptr(a), _ptr(b),
+                                           _dt(a, "a"), _ptr(A_log), _ptr(dt_bias), _ptr(cu), n, T, nk, nv, dk, dv,
+                                           float(scale or 0.0), int(bool(qk_l2norm)), _ptr(initial_state),
+                                           _ptr(final_state), _ptr(o), _dt(o, "o"), _stream(stream))
+    _check("gdn_chunk_fwd_gated_noalloc", st)
     return o, final_state
 
 

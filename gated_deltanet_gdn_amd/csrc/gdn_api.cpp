@@ -200,6 +200,32 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtyp
                   fn);
 }
 
+size_t gdn_chunk_fwd_noalloc_max_bytes(void) { return gdn::kNoallocScratchBytes; }
+
+int gdn_chunk_fwd_gated_noalloc(const void* q, const void* k, const void* v, int in_dtype, int64_t q_tok_stride,
+                                int64_t k_tok_stride, int64_t v_tok_stride, const void* a, const void* b,
+                                int ab_dtype, const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                                int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv, float scale,
+                                int qk_l2norm, const float* initial_state, float* final_state, void* o,
+                                int o_dtype, void* stream) {
+  const char* fn = "gdn_chunk_fwd_gated_noalloc";
+  int64_t qs = q_tok_stride, ks = k_tok_stride, vs = v_tok_stride;
+  const int st = check_chunk_gated(fn, q, k, v, in_dtype, qs, ks, vs, a, b, ab_dtype, A_log, dt_bias, cu_seqlens,
+                                   n_seqs, T_tot, nk, nv, dk, dv, scale, o, o_dtype);
+  if (st != GDN_OK) return st;
+  const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, in_dtype == GDN_BF16);
+  if (need > gdn::kNoallocScratchBytes)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL,
+                "%s: this call needs %zu bytes of scratch, above the %zu bytes the library holds per device; "
+                "use gdn_chunk_fwd_gated with a caller-allocated workspace",
+                fn, need, gdn::kNoallocScratchBytes);
+  return launched(gdn::launch_chunk_fwd_noalloc(q, k, v, in_dtype == GDN_BF16, qs, ks, vs, a, b,
+                                                ab_dtype == GDN_BF16 ? 1 : 2, A_log, dt_bias, cu_seqlens, n_seqs,
+                                                T_tot, nk, nv, scale, qk_l2norm != 0, initial_state, final_state, o,
+                                                o_dtype == GDN_BF16, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const float* conv_weight,
                       const float* conv_bias, int K, const void* conv_state_in, void* conv_state_out, int state_len,
                       const void* a, const void* b, int ab_dtype, const float* A_log, const float* dt_bias,

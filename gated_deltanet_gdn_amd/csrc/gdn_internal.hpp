@@ -57,6 +57,17 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf1
                             int64_t T, int nk, int nv, float scale, int l2, const float* S0, float* ST,
                             void* o, int o_bf16, void* ws, hipStream_t s);
 
+// Bytes of the device-resident scratch array that replaces the workspace in
+// the allocation-free entry point (one array per GPU, held by the library).
+constexpr size_t kNoallocScratchBytes = size_t(256) << 20;
+// launch_chunk_fwd with the library's scratch array as the workspace; the
+// caller has checked that the workspace fits it. No allocation.
+hipError_t launch_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int bf16,
+                                    int64_t qs, int64_t ks, int64_t vs, const void* ga, const void* gb, int gm,
+                                    const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs,
+                                    int64_t T, int nk, int nv, float scale, int l2, const float* S0, float* ST,
+                                    void* o, int o_bf16, hipStream_t s);
+
 // The chunked path with the causal conv1d (4 taps) + SiLU folded in, bf16 x
 // [T, (2 nk + nv) 128] with token stride xs; gating inputs as for gm = 1 / 2.
 // The conv state out is not written here (launch_conv_state_out).

@@ -42,6 +42,7 @@
 //                   two output waves one chunk behind. fp32 inputs use a
 //                   simple one-wave variant. Products with an fp32 operand
 //                   split it into bf16 hi + lo.
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -1532,6 +1533,37 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   }
 }
 
+// ------------------------------------------------------------------ allocation-free workspace
+// A file-scope device array that stands in for the caller's workspace in
+// launch_chunk_fwd_noalloc. Every GPU the library runs on holds its own copy
+// for the life of the process. In host code `scratch` names a host-side
+// stand-in, not a device address: kernels and copies use the per-device
+// address from hipGetSymbolAddress instead.
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device with that device current.
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t chunk_workspace_bytes(int64_t T, int n_seqs, int nk, int nv, int bf16) {
@@ -1548,6 +1580,19 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf1
                                     S0, ST, o, o_bf16, ws, nullptr, s);
   return chunk_dispatch<float>(q, k, v, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2, S0,
                                ST, o, o_bf16, ws, nullptr, s);
+}
+
+hipError_t launch_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int bf16, int64_t qs, int64_t ks,
+                                    int64_t vs, const void* ga, const void* gb, int gm, const float* A_log,
+                                    const float* dt_bias, const int32_t* cu, int n_seqs, int64_t T, int nk, int nv,
+                                    float scale, int l2, const float* S0, float* ST, void* o, int o_bf16,
+                                    hipStream_t s) {
+  // the caller has checked chunk_workspace_bytes(...) <= kNoallocScratchBytes
+  void* ws = nullptr;
+  const hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return e;
+  return launch_chunk_fwd(q, k, v, bf16, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2, S0,
+                          ST, o, o_bf16, ws, s);
 }
 
 hipError_t launch_chunk_fwd_conv(const void* x, int64_t xs, const float* conv_w, const float* conv_b,

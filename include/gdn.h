@@ -132,6 +132,34 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int in_dtyp
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_chunk_fwd_gated without a caller workspace, for callers that cannot
+ * allocate device memory around the call: code being captured into a device
+ * graph, tight serving loops, harnesses that forbid allocation. The library
+ * holds one scratch array of gdn_chunk_fwd_noalloc_max_bytes() bytes per GPU
+ * it runs on (a device-resident static, kept until the process ends) and
+ * uses it in place of the workspace; this entry point itself allocates and
+ * frees nothing. All arguments, results and supported shapes are those of
+ * gdn_chunk_fwd_gated (same kernels, same bits), minus the workspace.
+ * Errors: GDN_ERR_WORKSPACE_TOO_SMALL when
+ * gdn_chunk_fwd_workspace_size(T_tot, n_seqs, nk, nv, dk, dv, in_dtype)
+ * exceeds gdn_chunk_fwd_noalloc_max_bytes() (then nothing is enqueued; use
+ * gdn_chunk_fwd_gated with a workspace); otherwise as gdn_chunk_fwd_gated.
+ * Every call on one GPU shares that GPU's scratch array, and its contents on
+ * entry are ignored (nothing in it needs to start at zero): calls that overlap
+ * in time on one GPU (different streams, or different host threads without
+ * ordering) race on it and give unspecified results.
+ */
+size_t gdn_chunk_fwd_noalloc_max_bytes(void);
+int gdn_chunk_fwd_gated_noalloc(const void* q, const void* k, const void* v, int in_dtype,
+                                int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                                const void* a, const void* b, int ab_dtype,
+                                const float* A_log, const float* dt_bias,
+                                const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                                int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                                const float* initial_state, float* final_state,
+                                void* o, int o_dtype, void* stream);
+
+/*
  * The prefill core of one layer with the causal conv folded into the chunk
  * kernels ("Qwen3.5 Dense Model Architecture", Linear Attention, minimal
  * example: the packed q|k|v projection goes through the causal conv1d and

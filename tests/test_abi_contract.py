@@ -313,6 +313,41 @@ def test_binding_signatures_match_the_header(L):
         assert len(fn.argtypes) == n, f"{name}: header has {n} arguments, binding {len(fn.argtypes)}"
 
 
+def _noalloc(L, **kw):
+    a = dict(q=P, k=P, v=P, in_dtype=1, qs=0, ks=0, vs=0, a=P, b=P, ab_dtype=1, alog=P, dtb=P, cu=NULL, n=1, T=256,
+             nk=1, nv=2, dk=128, dv=128, scale=0.0, l2=1, s0=NULL, st=NULL, o=P, o_dtype=0, stream=NULL)
+    a.update(kw)
+    return L.gdn_chunk_fwd_gated_noalloc(a["q"], a["k"], a["v"], a["in_dtype"], a["qs"], a["ks"], a["vs"], a["a"],
+                                         a["b"], a["ab_dtype"], a["alog"], a["dtb"], a["cu"], a["n"], a["T"],
+                                         a["nk"], a["nv"], a["dk"], a["dv"], a["scale"], a["l2"], a["s0"], a["st"],
+                                         a["o"], a["o_dtype"], a["stream"])
+
+
+def test_noalloc_scratch_limit_is_stated(L):
+    assert gdn.gdn_chunk_fwd_noalloc_max_bytes() == 256 << 20
+    # the prefill T=8192 (16 -> 32 heads) workload fits it; T=65536 does not
+    assert gdn.gdn_chunk_fwd_workspace_size(8192, 1, 16, 32) <= gdn.gdn_chunk_fwd_noalloc_max_bytes()
+    assert gdn.gdn_chunk_fwd_workspace_size(65536, 1, 16, 32) > gdn.gdn_chunk_fwd_noalloc_max_bytes()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=65536, nk=16, nv=32), WS_SMALL),   # workspace above the scratch array: rejected before any HIP call
+    (dict(ab_dtype=4), INVALID),
+    (dict(a=NULL), INVALID),
+    (dict(alog=NULL), INVALID),
+    (dict(nk=3, nv=4), INVALID),
+    (dict(n=2), INVALID),                      # several sequences need cu_seqlens
+    (dict(dk=64), UNSUPPORTED),
+    (dict(q=MIS), UNSUPPORTED),
+])
+def test_chunk_fwd_gated_noalloc_argument_errors(L, kw, status):
+    assert _noalloc(L, **kw) == status
+    err = gdn.gdn_last_error()
+    assert err.startswith("gdn_chunk_fwd_gated_noalloc")
+    if status == WS_SMALL:
+        assert "scratch" in err and str(256 << 20) in err
+
+
 def test_launches_beyond_2_32_work_items_are_rejected_on_the_host(L):
     """One dispatch holds at most 2^32 - 1 work-items: every entry point rejects larger grids with
     UNSUPPORTED before enqueuing anything (no HIP call is reached with these arguments)."""
@@ -321,6 +356,7 @@ def test_launches_beyond_2_32_work_items_are_rejected_on_the_host(L):
     assert _fused(L, n=n, T=n, nk=8, nv=8, n_slots=n) == UNSUPPORTED
     # chunk state kernel: 8 column slices x 256 threads per (sequence, value head)
     assert _chunk(L, cu=P, n=1 << 19, T=1 << 19, nk=4, nv=8) == UNSUPPORTED
+    assert _noalloc(L, cu=P, n=1 << 19, T=1 << 19, nk=4, nv=8) in (UNSUPPORTED, WS_SMALL)
     # gated RMSNorm: 8 rows per 256-thread workgroup
     assert L.gdn_gated_rmsnorm(P, 0, P, 1, P, 1 << 30, 128, ctypes.c_float(1e-6), P2, 0, NULL) == UNSUPPORTED
     # gating: one thread per (token, head) in the worst case
