@@ -4,19 +4,25 @@
 
 One step = one pass of the prefill hot path over the T=8192 workload
 (B=1, 16 key heads repeated to 32 value heads, Dk=Dv=128, bf16 q/k/v/a/b,
-fp32 g/beta/state/output): gdn_gating then gdn_chunk_fwd (chunk table,
-per-chunk prep, per-sequence state recurrence). Inputs are resident in HBM
-before timing starts. W untimed warmup steps, then exactly K timed steps
-bracketed by torch.cuda.synchronize(); HIP events on the launch stream time
-every chunk_fwd call for the roofline figure.
+fp32 state/output): gating and the chunked rule as one gdn_chunk_fwd_gated
+call (chunk preparation with the gating folded in, then the per-sequence
+state recurrence). Inputs are resident in HBM before timing starts. About
+half a second of untimed steps lets clocks settle, then W untimed warm-up
+steps, then exactly K timed steps bracketed by torch.cuda.synchronize().
+HIP events on the launch stream then time K more calls for the roofline
+figure (warm: calls back to back), and up to 20 calls each preceded by a
+1 GiB write outside the event pair (cold: the call's inputs are no longer
+in the 256 MB memory-side cache).
 
-The decode figure runs one decode step of the 256-sequence workload (conv
-update, gating, recurrent update of the 512 MiB fp32 state in place) and
-reports the recurrent kernel's algorithmic bytes / its event-timed duration.
+The decode figures run one decode step of the 256-sequence workload (conv
+update, gating, recurrent update of the 512 MiB fp32 state in place) and the
+fused single-launch decode step, and report algorithmic bytes / event-timed
+duration.
 
-The CPU baseline times the fp64 oracle (gating + token recurrence) on the
-whole prefill workload on the host (threads stated); it is a reported
-baseline, not a target.
+The CPU baseline times the fp64 oracle on the host on every workload (the
+long prefill on its first 8192 tokens), with the CPU model, the cores this
+process may use and the threads each timing used; it is a reported baseline,
+not a target.
 
 roofline.traffic is the HBM traffic of one call, from the rocprofv3
 FETCH_SIZE / WRITE_SIZE summary committed under profiles/ (written by
@@ -301,24 +307,107 @@ def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
     return rows
 
 
-def cpu_baseline(x, threads):
+def cpu_info():
+    """CPU model, cores available to this process, and the thread cap: the cores this
+    process may run on, capped by OMP_NUM_THREADS when it is set (the machine's CPU share)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return model, avail, (min(avail, omp) if omp > 0 else avail)
+
+
+def _repeat(fn, min_s):
+    """Run fn() until at least min_s seconds of wall time have passed; returns (reps, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return reps, dt
+
+
+def cpu_baseline(W, cap, min_s=2.0):
+    """The fp64 oracle on the host cores, for every workload (a reported baseline, not the target).
+
+    Threads per workload = the thread cap (cores of this process, OMP_NUM_THREADS when set) capped at
+    the number of independent (sequence, value head) units. Each timing repeats its sample until
+    min_s seconds have passed. The long prefill is timed on its first 8192 tokens (all 64 heads, the
+    whole conv + gating + chunk + gated RMSNorm pipeline), since the whole workload would take minutes.
+    """
     import numpy as np
     import oracle
     f = lambda t: t.detach().to("cpu").double().numpy()
-    a, b, A, dt = f(x["a"]), f(x["b"]), f(x["A_log"]), f(x["dt_bias"])
-    q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
-    T = q.shape[0]
-    reps, t0 = 0, time.perf_counter()
-    while True:   # repeat the whole workload until ~10 s of wall time
+    out = {}
+
+    def chunk_rate(name, sample=None):
+        wl = W.WORKLOADS[name]
+        x = W.chunk_inputs(wl)
+        cu = x["cu_seqlens"].numpy()
+        n_units = len(x["lengths"]) * wl.nv
+        th = max(1, min(cap, n_units))
+        a, b, A, dt = f(x["a"]), f(x["b"]), f(x["A_log"]), f(x["dt_bias"])
+        q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
+        S0 = None if x["S0"] is None else f(x["S0"])
+        T = q.shape[0]
+
+        def run():
+            g, beta = oracle.gating(a, b, A, dt)
+            oracle.delta_rule(q, k, v, g, beta, cu_seqlens=cu, initial_state=S0, threads=th)
+        reps, sec = _repeat(run, min_s)
+        return dict(value=round(reps * T / sec, 1), unit="tokens/s", threads=th,
+                    sample=f"whole workload ({T} tokens, {wl.nv} value heads), gating + token recurrence, "
+                           f"{reps} runs in {sec:.2f} s")
+
+    out["tiny_chunk_f32"] = chunk_rate("tiny_chunk_f32")
+    out["prefill_chunk_t8k"] = chunk_rate("prefill_chunk_t8k")
+    out["varlen_prefill_8seq"] = chunk_rate("varlen_prefill_8seq")
+
+    wl = W.WORKLOADS["decode_256seq"]
+    x = W.decode_inputs(wl)
+    n, kd = wl.n_seqs, wl.nk * wl.dk
+    th = max(1, min(cap, n * wl.nv))
+    xx, cs, cw, a, b, A, dt, st = (f(x[kk]) for kk in ("x", "conv_state", "conv_w", "a", "b", "A_log",
+                                                       "dt_bias", "state"))
+
+    def dec():
+        y, _ = oracle.causal_conv1d_update(xx, cs, cw)
         g, beta = oracle.gating(a, b, A, dt)
-        oracle.delta_rule(q, k, v, g, beta, threads=threads)
-        reps += 1
-        dt_s = time.perf_counter() - t0
-        if dt_s >= 10.0 or reps >= 1000:
-            break
-    return dict(value=reps * T / dt_s, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"whole prefill workload (T={T}, 32 value heads), fp64 gating + token recurrence, "
-                       f"{reps} repetitions in {dt_s:.1f} s wall on {threads} threads")
+        oracle.delta_rule(y[:, :kd].reshape(n, wl.nk, wl.dk), y[:, kd:2 * kd].reshape(n, wl.nk, wl.dk),
+                          y[:, 2 * kd:].reshape(n, wl.nv, wl.dv), g, beta,
+                          cu_seqlens=np.arange(n + 1), initial_state=st, threads=th)
+    reps, sec = _repeat(dec, min_s)
+    out["decode_256seq"] = dict(value=round(reps * n * wl.nv / sec, 1), unit="state updates/s", threads=th,
+                                sample=f"whole decode step (conv update, gating, {n} x {wl.nv} state updates), "
+                                       f"{reps} runs in {sec:.2f} s")
+
+    wl = W.WORKLOADS["long_fused_t256k"]
+    Ts = 8192
+    x = W.fused_inputs(wl, T=Ts)
+    th = max(1, min(cap, wl.nv))
+    xx, cw, a, b, A, dt, z, nw = (f(x[kk]) for kk in ("x", "conv_w", "a", "b", "A_log", "dt_bias", "z",
+                                                      "norm_w"))
+    kd = wl.nk * wl.dk
+
+    def longp():
+        y, _ = oracle.causal_conv1d(xx, cw, state_len=wl.state_len)
+        g, beta = oracle.gating(a, b, A, dt)
+        o, _ = oracle.delta_rule(y[:, :kd].reshape(Ts, wl.nk, wl.dk), y[:, kd:2 * kd].reshape(Ts, wl.nk, wl.dk),
+                                 y[:, 2 * kd:].reshape(Ts, wl.nv, wl.dv), g, beta, threads=th)
+        oracle.gated_rmsnorm(o, z, nw)
+    reps, sec = _repeat(longp, min_s)
+    out["long_fused_t256k"] = dict(value=round(reps * Ts / sec, 1), unit="tokens/s", threads=th,
+                                   sample=f"first {Ts} of {wl.T} tokens, all {wl.nv} value heads, conv + SiLU, "
+                                          f"gating, token recurrence and gated RMSNorm, {reps} runs in {sec:.2f} s")
+    return out
 
 
 def main():
@@ -327,6 +416,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up steps, so that clocks settle")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-mtp", action="store_true", help="skip the 1 + 3 token fused decode measurement")
     ap.add_argument("--skip-rows", action="store_true", help="skip the per-row kernels on their own workloads")
@@ -376,7 +467,14 @@ def main():
         gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], g=g, beta=beta, stream=stream)
         gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], g, beta, final_state=st, o=o, workspace=ws, stream=stream)
 
-    # timed region: K steps between synchronisations, nothing else in the stream
+    # clocks settle under load first (untimed), then W warm-up steps, then the timed region:
+    # K steps between synchronisations, nothing else in the stream
+    settle, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        settle += 10
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -393,6 +491,17 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     chunk_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    # cold-cache figure: a 1 GiB write between calls, outside the event pair, evicts the call's inputs
+    # and workspace from the 256 MB memory-side cache (the warm figure above runs calls back to back)
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    n_cold = min(args.steps, 20)
+    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    for i in range(n_cold):
+        flush.fill_(float(i))
+        step(cevs[i])
+    torch.cuda.synchronize()
+    cold_ms = sum(a.elapsed_time(b) for a, b in cevs) / n_cold
+    del flush
 
     # the same step as two calls (gating, then the chunk rule), for reference
     for _ in range(max(10, args.warmup // 4)):
@@ -411,7 +520,9 @@ def main():
     roofline = dict(bound="mfma", kernel="gdn_chunk_fwd_gated (chunk_prep with the gating + chunk_state launches)",
                     achieved=round(achieved_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic("chunk"),
-                    avg_ms=round(chunk_ms, 4), algorithmic_flops=flops, algorithmic_bytes=cbytes,
+                    avg_ms=round(chunk_ms, 4), cold_avg_ms=round(cold_ms, 4),
+                    cold_frac=round(flops / (cold_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    algorithmic_flops=flops, algorithmic_bytes=cbytes,
                     hbm_gbps_algorithmic=round(cbytes / (chunk_ms * 1e-3) / 1e9, 1))
     # MFMA work as the hardware counted it (hi/lo precision passes included):
     # SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per call, from the same counter summary
@@ -486,9 +597,13 @@ def main():
 
     cpu = None
     if not args.skip_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(x, threads)
-        cpu["value"] = round(cpu["value"], 1)
+        model, avail, cap = cpu_info()
+        per = cpu_baseline(W, cap)
+        head = per["prefill_chunk_t8k"]
+        cpu = dict(value=head["value"], unit=head["unit"], cores=head["threads"], kind="oracle",
+                   sample=head["sample"], cpu_model=model, cores_available=avail, thread_cap=cap,
+                   thread_policy="min(cores of this process capped by OMP_NUM_THREADS, independent units)",
+                   per_config=per)
 
     out = {
         "metric": "GDN prefill tokens/s (T=8K, bf16) + decode state-update HBM GB/s",
@@ -497,6 +612,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_separate_gating": round(ms_separate, 4),
         "higher_is_better": True,
