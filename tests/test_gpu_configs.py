@@ -13,8 +13,11 @@ binding's defaults). Checks:
     from the GPU's own bf16 conv output, every unit;
   * long fused prefill (T=262144, 16->64 heads): stage-wise on samples the
     oracle can compute -- conv on three token windows of all channels, gating
-    on every 61st token, the core on two value heads over the full sequence
-    (outputs and final state), gated RMSNorm on sampled rows.
+    on every 61st token, the core on 16 value heads (one per key head, each
+    of the four positions inside a key head four times) over the full
+    sequence, for both the separate launches and the fused prefill (outputs
+    and final state), gated RMSNorm on every 257th token and on a contiguous
+    block of 4096 tokens (all heads).
 Parity bar: max-abs <= 2e-3 * RMS for bf16 inputs, 1e-5 * RMS for fp32.
 """
 import os
@@ -123,8 +126,12 @@ def long_run():
     g, beta = gdn.gdn_gating(x["a"], x["b"], x["A_log"], x["dt_bias"])
     o, st = gdn.gdn_chunk_fwd(q, k, v, g, beta)
     out = gdn.gdn_gated_rmsnorm(o, x["z"], x["norm_w"], eps=1e-6)
+    _say(wl.name, "gpu fused prefill")
+    fo, fst, fcs = gdn.gdn_prefill_fused(x["x"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"], wl.nk, wl.nv,
+                                         state_len=wl.state_len)
     torch.cuda.synchronize()
-    return dict(wl=wl, x=x, y=y, cs=cs, g=g, beta=beta, o=o, st=st, out=out, T=T, C=C, kd=kd)
+    return dict(wl=wl, x=x, y=y, cs=cs, g=g, beta=beta, o=o, st=st, out=out, T=T, C=C, kd=kd, fo=fo, fst=fst,
+                fcs=fcs)
 
 
 def test_long_prefill_fused_equals_pipeline(long_run):
@@ -133,14 +140,10 @@ def test_long_prefill_fused_equals_pipeline(long_run):
     r = long_run
     wl, x = r["wl"], r["x"]
     _say(wl.name, "fused prefill against the separate launches")
-    o, st, cs = gdn.gdn_prefill_fused(x["x"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"], wl.nk, wl.nv,
-                                      state_len=wl.state_len)
-    torch.cuda.synchronize()
-    for a, b, what in ((o, r["o"], "o"), (st, r["st"], "final state"), (cs, r["cs"], "conv state out")):
+    for a, b, what in ((r["fo"], r["o"], "o"), (r["fst"], r["st"], "final state"), (r["fcs"], r["cs"], "conv state out")):
         diff = (a.double() - b.double()).abs().max().item()
         print(f"[exact] {what}: max |fused - separate| = {diff:.3e}", flush=True)
         assert torch.equal(a, b), what
-    del o, st, cs
 
 
 def test_long_conv_windows(long_run):
@@ -166,26 +169,47 @@ def test_long_gating_sampled(long_run):
     np.testing.assert_allclose(f64(r["beta"][idx]), b_ref, rtol=4e-6)
 
 
-@pytest.mark.timeout(300)
-def test_long_core_two_heads_full_sequence(long_run):
+@pytest.fixture(scope="module")
+def long_core_ref(long_run):
+    """The oracle on 16 value heads of the long prefill over all 262,144 tokens, from the GPU's own conv
+    output (stage-wise): one value head per key head, and the position inside the key head's group of
+    four rotating, so every (key head, position) work-order case of the state kernel appears."""
     r = long_run
     wl = r["wl"]
     rr = wl.nv // wl.nk
-    heads = [0, 37]
-    khs = [h // rr for h in heads]
-    _say("long core heads", heads, "key heads", khs)
+    heads = [hk * rr + hk % rr for hk in range(wl.nk)]
+    _say("long core heads", heads)
     yg = r["y"]
     kd = r["kd"]
-    q = torch.stack([yg[:, hk * 128:(hk + 1) * 128] for hk in khs], 1)
-    k = torch.stack([yg[:, kd + hk * 128:kd + (hk + 1) * 128] for hk in khs], 1)
+    q = torch.stack([yg[:, hk * 128:(hk + 1) * 128] for hk in range(wl.nk)], 1)
+    k = torch.stack([yg[:, kd + hk * 128:kd + (hk + 1) * 128] for hk in range(wl.nk)], 1)
     v = torch.stack([yg[:, 2 * kd + h * 128:2 * kd + (h + 1) * 128] for h in heads], 1)
     hs = torch.tensor(heads, device=yg.device)
     g_ref, b_ref = oracle.gating(f64(r["x"]["a"][:, hs]), f64(r["x"]["b"][:, hs]), f64(r["x"]["A_log"][hs]),
                                  f64(r["x"]["dt_bias"][hs]))
+    # q/k of key head hk pair with value head heads[hk]: one key head per value head here
     o_ref, s_ref = oracle.delta_rule(f64(q), f64(k), f64(v), g_ref, b_ref, threads=THREADS)
+    return heads, o_ref, s_ref
+
+
+@pytest.mark.timeout(300)
+def test_long_core_sixteen_heads_full_sequence(long_run, long_core_ref):
+    r = long_run
+    heads, o_ref, s_ref = long_core_ref
     for i, h in enumerate(heads):
         assert_close(r["o"][:, h], o_ref[:, i], TOL["bf16"], f"long o head {h}")
         assert_close(r["st"][0, h], s_ref[0, i], TOL["bf16"], f"long final state head {h}")
+
+
+@pytest.mark.timeout(300)
+def test_long_fused_prefill_sixteen_heads_against_oracle(long_run, long_core_ref):
+    """The fused prefill's own outputs against the oracle on the same 16 heads (the oracle reads the
+    separate conv's bf16 output, which the fused kernels reproduce bit for bit in registers)."""
+    r = long_run
+    heads, o_ref, s_ref = long_core_ref
+    for i, h in enumerate(heads):
+        assert_close(r["fo"][:, h], o_ref[:, i], TOL["bf16"], f"fused prefill o head {h}")
+        assert_close(r["fst"][0, h], s_ref[0, i], TOL["bf16"], f"fused prefill final state head {h}")
 
 
 def test_long_rmsnorm_sampled_rows(long_run):
@@ -195,3 +219,11 @@ def test_long_rmsnorm_sampled_rows(long_run):
     z = r["x"]["z"][rows]
     ref = oracle.gated_rmsnorm(f64(x), f64(z), f64(r["x"]["norm_w"]), eps=1e-6)
     assert_close(r["out"][rows], ref, TOL["f32"], "long gated rmsnorm (fp32 x)")
+
+
+def test_long_rmsnorm_contiguous_block(long_run):
+    r = long_run
+    t0 = r["T"] // 2 + 123
+    x = r["o"][t0:t0 + 4096]      # 4096 tokens x 64 heads of rows, contiguous
+    ref = oracle.gated_rmsnorm(f64(x), f64(r["x"]["z"][t0:t0 + 4096]), f64(r["x"]["norm_w"]), eps=1e-6)
+    assert_close(r["out"][t0:t0 + 4096], ref, TOL["f32"], "long gated rmsnorm, 4096 contiguous tokens")
