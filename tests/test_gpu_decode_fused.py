@@ -300,3 +300,36 @@ def test_fused_state_snapshots():
         for n, L in enumerate(lengths):
             if L >= p:
                 _same(snap[cu[n] + p - 1], st_p[n], f"snapshot seq {n} token {p - 1}")
+
+
+def test_fused_mtp_rollback_of_rejected_draft_tokens():
+    """Speculative decode: a step over 1 + 3 draft tokens per sequence, then only a prefix is accepted.
+    The caller rolls back with what it holds: the recurrent state from the snapshot of the last accepted
+    token, and the conv state as the last state_len entries of [its copy of the conv state taken before
+    the step, the accepted x rows] (the step overwrites the conv state in place). Both must equal a step
+    run on the accepted tokens alone, bit for bit."""
+    _say("fused decode: accept a prefix of the draft tokens and roll back")
+    nk, nv = 2, 4
+    lengths = [4, 4, 4, 4]
+    accepted = [1, 2, 4, 3]
+    wl = W.Workload("fused_rollback", 17, "decode", "bf16", nk=nk, nv=nv, s0_std=0.02)
+    x = W.decode_mtp_inputs(wl, lengths)
+    d = _to(x)
+    T = sum(lengths)
+    sl = d["conv_state"].shape[2]
+    conv_copy = d["conv_state"].clone()          # the caller's copy, taken before the step
+    cs, st = d["conv_state"].clone(), d["state"].clone()
+    snap = torch.empty((T, nv, DK, DK), device=dev())
+    gdn.gdn_decode_step_fused(d["x"], cs, d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], st, nk,
+                              cu_seqlens=d["cu_seqlens"], state_snapshots=snap)
+    cu = x["cu_seqlens"].tolist()
+    st_rb = torch.stack([snap[cu[n] + accepted[n] - 1] for n in range(len(lengths))])
+    cs_rb = torch.stack([torch.cat([conv_copy[n], d["x"][cu[n]:cu[n] + accepted[n]].t()], 1)[:, -sl:]
+                         for n in range(len(lengths))])
+    rows = torch.tensor([cu[n] + j for n in range(len(lengths)) for j in range(accepted[n])], device=dev())
+    sub = dict(d, x=d["x"][rows].contiguous(), a=d["a"][rows].contiguous(), b=d["b"][rows].contiguous(),
+               cu_seqlens=torch.tensor(np.concatenate([[0], np.cumsum(accepted)]), dtype=torch.int32, device=dev()))
+    o_p, st_p, cs_p = _fused(sub, nk, sub["cu_seqlens"])
+    torch.cuda.synchronize()
+    _same(st_rb, st_p, "rolled-back recurrent state")
+    _same(cs_rb.contiguous(), cs_p, "rolled-back conv state")
