@@ -555,7 +555,7 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
 
-        for _ in range(args.warmup):
+        for _ in range(max(args.warmup, 50)):   # steady clocks, as for the fused decode legs below
             dstep()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -580,10 +580,13 @@ def main():
 
     decode_fused = decode_mtp = None
     if not args.skip_decode:
-        decode_fused = time_fused_decode(gdn, W, "decode_256seq", args.steps, args.warmup, stream, dev)
+        # (the decode steps are ~0.2 ms each: at least 50 untimed steps bring the clocks to their steady
+        # state whatever --warmup says, as the settle loop does for the chunk call)
+        dwarm = max(args.warmup, 50)
+        decode_fused = time_fused_decode(gdn, W, "decode_256seq", args.steps, dwarm, stream, dev)
         decode_fused["separate_launches_step_ms"] = decode["step_ms"]
         if not args.skip_mtp:
-            decode_mtp = time_fused_decode(gdn, W, "decode_mtp_256x4", args.steps, args.warmup, stream, dev,
+            decode_mtp = time_fused_decode(gdn, W, "decode_mtp_256x4", args.steps, dwarm, stream, dev,
                                            tokens_per_seq=W.WORKLOADS["decode_mtp_256x4"].extra["tokens_per_seq"])
 
     rows = None if args.skip_rows else time_rows(gdn, W, stream, dev)
