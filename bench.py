@@ -49,7 +49,7 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_t8k_decode
 CSRC = os.path.join(ROOT, "gated_deltanet_gdn_amd", "csrc")
 # kernel sources each measured figure depends on
 SOURCES = {"chunk": ["k_chunk.hip", "gdn_device.hpp"], "recurrent": ["k_recurrent.hip", "gdn_device.hpp"],
-           "fused": ["k_recurrent.hip", "gdn_device.hpp"]}
+           "fused": ["k_recurrent.hip", "gdn_device.hpp"], "mtp": ["k_recurrent.hip", "gdn_device.hpp"]}
 
 
 def source_hash(part):
@@ -152,7 +152,7 @@ def time_fused_decode(gdn, W, name, steps, warmup, stream, dev, tokens_per_seq=N
                 step_ms=round(step_ms, 4), tokens_per_s=round(n_tok / (step_ms * 1e-3), 1),
                 roofline=dict(bound="hbm", kernel="decode_fused_kernel", achieved=round(gbps, 1),
                               peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
-                              traffic=measured_traffic("fused") if tokens_per_seq is None else None,
+                              traffic=measured_traffic("fused" if tokens_per_seq is None else "mtp"),
                               avg_ms=round(k_ms, 4), algorithmic_bytes=nbytes))
 
 
@@ -425,6 +425,8 @@ def main():
                     help="only the per-row kernels (one JSON line with them; used for their kernel trace)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with one plain 1 GiB device copy (counter calibration runs only)")
+    ap.add_argument("--mtp-only", action="store_true",
+                    help="only the 1 + 3 token fused decode step (one JSON line; used for its counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GDN core shards by head or sequence with no "
@@ -440,6 +442,15 @@ def main():
     stream = torch.cuda.current_stream()
     if args.rows_only:
         print(json.dumps({"rows": time_rows(gdn, W, stream, dev)}), flush=True)
+        return
+    if args.mtp_only:
+        mtp = time_fused_decode(gdn, W, "decode_mtp_256x4", args.steps, max(args.warmup, 50), stream, dev,
+                                tokens_per_seq=W.WORKLOADS["decode_mtp_256x4"].extra["tokens_per_seq"])
+        if args.calibrate_copy:
+            src = torch.ones(1 << 28, device=dev, dtype=torch.float32)
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"decode_mtp_fused": mtp}), flush=True)
         return
 
     # ---------------------------------------------------------------- prefill step

@@ -11,6 +11,9 @@ with tracing:
   3. --pmc WRITE_SIZE                          HBM write KiB per dispatch
   4. --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA   MFMA work per dispatch
   5. --kernel-trace --stats of bench.py --rows-only     the per-row kernels on their workloads
+  6-8. --kernel-trace --stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE of
+       bench.py --mtp-only: the 1 + 3 token fused decode step on its own (its
+       kernel is the single-token step's, so it needs runs of its own)
 The copy gives the calibration factors: true bytes / counter reading for a
 copy of known size, applied to every kernel's reading.
 
@@ -19,6 +22,7 @@ Writes
   profiles/hbm_traffic_prefill_t8k_decode_256seq.md   (its traffic_json line is
       read by bench.py, with the hash of the kernel sources it was taken on)
   profiles/rows_long_prefill_t256k_decode_256seq_kernel_stats.md
+(the 1 + 3 token step's figures go into the traffic summary)
 This process itself never touches the GPU.
 """
 from __future__ import annotations
@@ -47,6 +51,7 @@ KERNELS = {  # what one call of each measured entry point launches (bf16 in, fp3
     "recurrent": ["recurrent_kernel<unsigned short, float"],
     "fused": ["decode_fused_kernel<unsigned short, float"],
 }
+MTP_ARGS = ["--steps", "200", "--warmup", "100", "--mtp-only", "--calibrate-copy"]
 
 
 def launched(table, names):
@@ -59,12 +64,15 @@ PASSES = [  # name, rocprofv3 arguments
     ("write", ["--pmc", "WRITE_SIZE"]),
     ("mfma", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA"]),
     ("rows", ["--kernel-trace", "--stats"]),     # bench.py --rows-only
+    ("mtp_ktrace", ["--kernel-trace", "--stats"]),   # bench.py --mtp-only
+    ("mtp_fetch", ["--pmc", "FETCH_SIZE"]),
+    ("mtp_write", ["--pmc", "WRITE_SIZE"]),
 ]
 ROWS_SUMMARY = os.path.join(ROOT, "profiles", "rows_long_prefill_t256k_decode_256seq_kernel_stats.md")
 
 
 def bench_args(name):
-    return ["--rows-only"] if name == "rows" else BENCH_ARGS
+    return ["--rows-only"] if name == "rows" else MTP_ARGS if name.startswith("mtp") else BENCH_ARGS
 
 
 def pass_command(name, prof_args):
@@ -198,9 +206,22 @@ def summarize(out):
             flops += mops * 512
             rows.append(f"| `{k}` | {f_kib:.1f} | {w_kib:.1f} | {rb / 1e6:.1f} MB | {wb / 1e6:.1f} MB | {mops:.3e} |")
         rec[part] = dict(bytes_per_call=round(total), mfma_flops_per_call=flops, source_hash=bench.source_hash(part))
+    # the 1 + 3 token step, from its own runs (calibrated by their own copy)
+    mf, mw = counters(os.path.join(out, "mtp_fetch")), counters(os.path.join(out, "mtp_write"))
+    mkf = COPY_BYTES / 1024 / max(mf[pick(mf, "copyBuffer")]["FETCH_SIZE"])
+    mkw = COPY_BYTES / 1024 / max(mw[pick(mw, "copyBuffer")]["WRITE_SIZE"])
+    k = KERNELS["fused"][0]
+    f_kib, w_kib = avg(mf[pick(mf, k)]["FETCH_SIZE"]), avg(mw[pick(mw, k)]["WRITE_SIZE"])
+    rb, wb = f_kib * 1024 * mkf, w_kib * 1024 * mkw
+    rows.append(f"| `{k}` (1 + 3 tokens) | {f_kib:.1f} | {w_kib:.1f} | {rb / 1e6:.1f} MB | {wb / 1e6:.1f} MB | 0 |")
+    rec["mtp"] = dict(bytes_per_call=round(rb + wb), mfma_flops_per_call=0.0, source_hash=bench.source_hash("mtp"))
+    mks = {r["Name"]: r for r in kernel_stats(os.path.join(out, "mtp_ktrace"))}
+    mtp_avg = float(mks[pick(mks, k)]["AverageNs"]) / 1e3
+    bm = bench_line(out, "mtp_ktrace")["decode_mtp_fused"]
+    cmd_m = [pass_command(n, a) for n, a in PASSES if n.startswith("mtp")]
     lines = ["# HBM traffic and MFMA work per call: prefill T=8192 (bf16, 16->32 heads) and decode 256 seqs", "",
              "Commands (from /tmp, TMPDIR=/tmp), one counter set per run:", "",
-             "    " + cmd2, "    " + cmd3, "    " + cmd4, "",
+             "    " + cmd2, "    " + cmd3, "    " + cmd4, *["    " + c for c in cmd_m[1:]], "",
              "Calibration on the plain 1 GiB device copy (`copyBuffer`) in the same runs:", "",
              f"- FETCH_SIZE read {copy_f:.1f} KiB for {COPY_BYTES // 1024} KiB: read bytes = {kf:.4f} x 1024 x FETCH_SIZE",
              f"- WRITE_SIZE read {copy_w:.1f} KiB for {COPY_BYTES // 1024} KiB: write bytes = {kw:.4f} x 1024 x WRITE_SIZE",
@@ -212,7 +233,11 @@ def summarize(out):
              f"- recurrent_kernel: {rec['recurrent']['bytes_per_call'] / 1e6:.1f} MB per call "
              f"(algorithmic {bench.recurrent_bytes(256, 16, 32) / 1e6:.1f} MB)",
              f"- decode_fused_kernel: {rec['fused']['bytes_per_call'] / 1e6:.1f} MB per call "
-             f"(algorithmic {bench.fused_decode_bytes(256, 256, 16, 32) / 1e6:.1f} MB)", "",
+             f"(algorithmic {bench.fused_decode_bytes(256, 256, 16, 32) / 1e6:.1f} MB)",
+             f"- decode_fused_kernel, 1 + 3 tokens per sequence: {rec['mtp']['bytes_per_call'] / 1e6:.1f} MB per call "
+             f"(algorithmic {bench.fused_decode_bytes(1024, 256, 16, 32) / 1e6:.1f} MB); kernel trace average "
+             f"{mtp_avg:.1f} us ({cmd_m[0]}), events {bm['roofline']['avg_ms'] * 1e3:.1f} us, "
+             f"{100 * bm['roofline']['frac']:.1f} % of HBM peak", "",
              "Source hashes are of the kernel sources the counters were taken on; bench.py reports traffic",
              "only while they match.", "",
              "traffic_json: " + json.dumps(rec), ""]
