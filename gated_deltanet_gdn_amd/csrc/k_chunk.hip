@@ -42,6 +42,8 @@
 //                   two output waves one chunk behind. fp32 inputs use a
 //                   simple one-wave variant. Products with an fp32 operand
 //                   split it into bf16 hi + lo.
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <type_traits>
 
@@ -1282,6 +1284,526 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   else
     run(std::false_type{});
 }
+// ------------------------------------------------------------------ state: bf16 inputs, two 16-column slices per workgroup
+// The wide form, for launches with at least twice as many 16-column slices
+// as CUs (several sequences, or many heads), where a CU's throughput matters
+// more than one slice's latency. One workgroup per (sequence, value head, 32
+// value columns), four waves:
+//   Waves 0 and 1 (recurrence): wave j owns all 128 rows of S for the
+//     columns of slice 2 p + j (eight MFMA accumulators) and runs the chunk
+//     step of the four-wave form on them alone, with no partial products to
+//     swap. X is still formed as (K S over dk rows 0-63) + (K S over rows
+//     64-127), the sum the four-wave form's two halves exchange, so every
+//     result equals that form's bit for bit.
+//   Waves 2 and 3 (output, one chunk behind): the four-wave form's output
+//     work for both slices (wave 2 token tiles 0 and 3, wave 3 tiles 1 and
+//     2); the Q and P blocks of a tile serve both slices.
+// Staging: wave 2 the masked T blocks, wave 3 the per-token scalars and
+// exp(G_C), both one chunk ahead; wave 2 stages beta v for slice 2 p, wave 3
+// for slice 2 p + 1, each for all 64 tokens of a chunk (beta from memory).
+// One barrier per chunk; every LDS buffer shared between waves is
+// double-buffered by chunk parity as in the four-wave form.
+__device__ __forceinline__ void wide_unit_pair(int b, int n_units, int r, int& unit_slot, int& pair) {
+  const int j = b >> 3;          // this workgroup's position on its XCD
+  if (n_units % (8 * r) == 0) {
+    pair = j & 3;
+    const int k = j >> 2;        // unit position on the XCD
+    unit_slot = ((k / r) * 8 + (b & 7)) * r + k % r;
+  } else if (n_units % 8 == 0) {
+    pair = j & 3;
+    unit_slot = ((j >> 2) << 3) + (b & 7);
+  } else {
+    const int bid = xcd_swizzle(b, n_units * 4);
+    pair = bid & 3;
+    unit_slot = bid >> 2;
+  }
+}
+
+template <typename TO, bool CV>
+__global__ void __launch_bounds__(256) chunk_state_wide_kernel(
+    const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
+    int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
+    const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
+    const int32_t* __restrict__ order, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o,
+    ConvIn cv) {
+  __shared__ uint4 SBX[2][2][2][4][64];  // S as B operand: [slice][parity][hi | lo][dk k-step][lane]
+  __shared__ f32x4 UXF[2][2][4][64];     // U: [slice][parity][token tile][lane]
+  __shared__ f32x4 BVS[2][2][4][64];     // beta * v: [slice][parity][token tile][lane]
+  __shared__ uint4 TSX[2][12][64];       // masked T blocks: [parity][hi (6) | lo (6)][lane]
+  // each recurrence wave's 16 K blocks of the current chunk, read back
+  // transposed (lane l at byte 16 l + 64 (l / 16) of its block)
+  __shared__ __attribute__((aligned(16))) unsigned char KLX[2][16][KL_BLK];
+  __shared__ __attribute__((aligned(16))) float SCS[2][4 * CH];   // planes a | b | c | beta
+  __shared__ float EGS[2];               // exp(G_C)
+
+  int slot, pair;
+  wide_unit_pair(blockIdx.x, gridDim.x / 4, nv / nk, slot, pair);
+  const int n = cu ? order[slot / nv] : 0, h = slot % nv;
+  const int unit = n * nv + h;
+  const int hk = h / (nv / nk);
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const uint32_t lo16 = static_cast<uint32_t>(lane * 16);
+
+  int64_t s_begin, s_end;
+  seq_bounds(cu, n, T, s_begin, s_end);
+  int cbase, nchunks;
+  chunk_span(chunk_off, cu, T, n, cbase, nchunks);
+
+  if (w < 2) {
+    // ================================================================ recurrence waves
+    const int col = (2 * pair + w) * 16 + lr;
+    f32x4 S[8];                            // rows 16 tt + 4 lg + i, column col
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[tt][i] = S0 ? S0[(static_cast<int64_t>(unit) * D + 16 * tt + 4 * lg + i) * D + col] : 0.0f;
+
+    if (nchunks > 0) {
+      unsigned char (*kl)[KL_BLK] = KLX[w];
+      uint4 kb[4][4];                      // K (token tile m, dk k-step ks)
+      auto load_k = [&](int cc) {
+        const size_t kt = static_cast<size_t>(cbase + cc) * nk + hk;
+        const rsrc_t r = make_rsrc(kf + kt * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) kb[m][ks] = bload16(r, (4 * m + ks) * BLK_BYTES + lo16);
+      };
+      f32x4 X0[4], X1[4];                  // K S over dk rows 0-63 and 64-127
+      // S_c as B operand (published for the output waves) and X_c
+      auto first_half = [&](int c) {
+        const int buf = c & 1;
+        uint4 sh[4], sl[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          uint2 h0, l0, h1, l1;
+          split4_packed(make_float4(S[2 * ks][0], S[2 * ks][1], S[2 * ks][2], S[2 * ks][3]), h0, l0);
+          split4_packed(make_float4(S[2 * ks + 1][0], S[2 * ks + 1][1], S[2 * ks + 1][2], S[2 * ks + 1][3]), h1, l1);
+          sh[ks] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+          sl[ks] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+          SBX[w][buf][0][ks][lane] = sh[ks];
+          SBX[w][buf][1][ks][lane] = sl[ks];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            x0 = mfma_bf16(as_bf16x8(kb[m][kk]), as_bf16x8(sl[kk]), x0);
+            x0 = mfma_bf16(as_bf16x8(kb[m][kk]), as_bf16x8(sh[kk]), x0);
+          }
+#pragma unroll
+          for (int kk = 2; kk < 4; ++kk) {
+            x1 = mfma_bf16(as_bf16x8(kb[m][kk]), as_bf16x8(sl[kk]), x1);
+            x1 = mfma_bf16(as_bf16x8(kb[m][kk]), as_bf16x8(sh[kk]), x1);
+          }
+          X0[m] = x0;
+          X1[m] = x1;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            *reinterpret_cast<uint4*>(&kl[4 * m + ks][kl_lane(lane)]) = kb[m][ks];
+        }
+        load_k(min(c + 1, nchunks - 1));
+      };
+      // the rest of chunk c: R, U, c U, and the update of S
+      auto second_half = [&](int c) {
+        const int buf = c & 1;
+        // K^T blocks (dk tile tt, token k-step s), read transposed as in the
+        // four-wave form: block (token tile 2 s + h, dk k-step tt / 2)
+        uint4 kta[8][2];
+        {
+          const int kll = kl_lane(16 * (lr & 3) + 4 * lg + (lr >> 2));
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const uint2 y0 = lds_tr16(&kl[4 * (2 * s) + tt / 2][kll + 8 * (tt & 1)]);
+              const uint2 y1 = lds_tr16(&kl[4 * (2 * s + 1) + tt / 2][kll + 8 * (tt & 1)]);
+              kta[tt][s] = make_uint4(y0.x, y0.y, y1.x, y1.y);
+            }
+        }
+        f32x4 R[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 bv = BVS[w][buf][m][lane];
+          const float4 bb = *reinterpret_cast<const float4*>(&SCS[buf][CH + 16 * m + 4 * lg]);
+          const float bbv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) R[m][i] = bv[i] - bbv[i] * (X0[m][i] + X1[m][i]);
+        }
+        uint4 rh[2], rl[2];                // R as B operand, token k-steps 0, 1
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          uint2 h0, l0, h1, l1;
+          split4_packed(make_float4(R[2 * s][0], R[2 * s][1], R[2 * s][2], R[2 * s][3]), h0, l0);
+          split4_packed(make_float4(R[2 * s + 1][0], R[2 * s + 1][1], R[2 * s + 1][2], R[2 * s + 1][3]), h1, l1);
+          rh[s] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+          rl[s] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+        }
+        // T blocks (m, s): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), masked, hi | lo
+        uint4 mh[6], ml[6];
+#pragma unroll
+        for (int b = 0; b < 6; ++b) {
+          mh[b] = TSX[buf][b][lane];
+          ml[b] = TSX[buf][6 + b][lane];
+        }
+        // U = R + T_strict R
+        f32x4 U[4];
+        auto tr = [&](f32x4& acc, int b, int s) {
+          acc = mfma_bf16(as_bf16x8(ml[b]), as_bf16x8(rh[s]), acc);
+          acc = mfma_bf16(as_bf16x8(mh[b]), as_bf16x8(rl[s]), acc);
+          acc = mfma_bf16(as_bf16x8(mh[b]), as_bf16x8(rh[s]), acc);
+        };
+#pragma unroll
+        for (int m = 0; m < 4; ++m) U[m] = R[m];
+        tr(U[0], 0, 0);
+        tr(U[1], 1, 0);
+        tr(U[2], 2, 0);
+        tr(U[3], 4, 0);
+        tr(U[2], 3, 1);
+        tr(U[3], 5, 1);
+        // U for the output waves; c U as B operand
+#pragma unroll
+        for (int m = 0; m < 4; ++m) UXF[w][buf][m][lane] = U[m];
+        f32x4 cU[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 c4 = *reinterpret_cast<const float4*>(&SCS[buf][2 * CH + 16 * m + 4 * lg]);
+          cU[m][0] = c4.x * U[m][0];
+          cU[m][1] = c4.y * U[m][1];
+          cU[m][2] = c4.z * U[m][2];
+          cU[m][3] = c4.w * U[m][3];
+        }
+        uint4 ch[2], cl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          uint2 h0, l0, h1, l1;
+          split4_packed(make_float4(cU[2 * s][0], cU[2 * s][1], cU[2 * s][2], cU[2 * s][3]), h0, l0);
+          split4_packed(make_float4(cU[2 * s + 1][0], cU[2 * s + 1][1], cU[2 * s + 1][2], cU[2 * s + 1][3]), h1, l1);
+          ch[s] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+          cl[s] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+        }
+        const float eg = EGS[buf];
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const uint4* ktb = kta[tt];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[tt][i] *= eg;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            S[tt] = mfma_bf16(as_bf16x8(ktb[s]), as_bf16x8(cl[s]), S[tt]);
+            S[tt] = mfma_bf16(as_bf16x8(ktb[s]), as_bf16x8(ch[s]), S[tt]);
+          }
+        }
+      };
+
+      load_k(0);
+      first_half(0);
+      // the last pass also runs first_half for a chunk n that does not exist:
+      // it writes buffers of parity n that nobody reads afterwards
+      for (int c = 0; c < nchunks; ++c) {
+        __syncthreads();                   // B(c)
+        second_half(c);
+        first_half(c + 1);
+      }
+      __syncthreads();                     // B(n): the last U is in LDS
+    }
+    if (ST) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ST[(static_cast<int64_t>(unit) * D + 16 * tt + 4 * lg + i) * D + col] = S[tt][i];
+    }
+    return;
+  }
+
+  // ================================================================ output waves
+  if (nchunks == 0) return;
+  const int ow = w - 2;
+  const int mt[2] = {ow, 3 - ow};        // token tiles: one with one P k-step, one with two
+  // P blocks and their masks as in the four-wave form
+  uint4 pm[3];
+  uint32_t po[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    const int m = b == 0 ? mt[0] : mt[1], s = b == 2 ? 1 : 0;
+    const int row = 16 * m + lr;
+    uint32_t mm[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bool lo = 32 * s + perm32(lg, 7 - 2 * d) <= row;
+      const bool hi = 32 * s + perm32(lg, 6 - 2 * d) <= row;
+      mm[d] = (lo ? 0x0000ffffu : 0u) | (hi ? 0xffff0000u : 0u);
+    }
+    pm[b] = make_uint4(mm[0], mm[1], mm[2], mm[3]);
+    po[b] = static_cast<uint32_t>((2 * (3 - m) + 1 - s) * BLK_BYTES + (63 - lane) * 16);
+  }
+  // beta v staging for slice 2 p + ow: lane l takes tokens l / 2 and 32 + l / 2,
+  // columns 8 (l % 2) .. +7 of the head (offsets from the head's first value column)
+  const int vcol = (2 * pair + ow) * 16 + 8 * (lane & 1);
+  const uint32_t vo0 = static_cast<uint32_t>(((lane >> 1) * vs + vcol) * 2);
+  const int cch = 2 * nk * D + h * D + vcol;   // first conv channel of those columns
+  float cwt[4][8], cbs[8];
+  uint4 cxr[2][4];                       // staging: window rows of both tokens
+  uint4 svr[2];                          // staging: value rows of both tokens
+  float sbeta[2];                        // staging: beta of both tokens
+  if constexpr (CV) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cwt[j][e] = cv.w[(cch + e) * 4 + j];
+      cbs[e] = cv.b ? cv.b[cch + e] : 0.0f;
+    }
+  }
+  uint2 dm;                              // T staging masks as in the four-wave form
+  {
+    uint32_t mm[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+      mm[d] = (4 * lg + 2 * d < lr ? 0x0000ffffu : 0u) | (4 * lg + 2 * d + 1 < lr ? 0xffff0000u : 0u);
+    dm = make_uint2(mm[0], mm[1]);
+  }
+
+  uint4 qb[2][4];                        // Q (tile mt[u], dk k-step)
+  uint4 ph[3], pl[3];                    // P blocks, hi | lo
+  uint4 sg[12];                          // staging: T blocks (wave 2), or scalars (wave 3)
+  uint32_t eg = 0;                       // staging: exp(G_C)
+  auto load_q = [&](int cc) {
+    const size_t kt = static_cast<size_t>(cbase + cc) * nk + hk;
+    const rsrc_t r = make_rsrc(qf + kt * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qb[u][s] = bload16(r, static_cast<uint32_t>((4 * mt[u] + s) * BLK_BYTES) + lo16);
+  };
+  auto load_p = [&](int cc) {
+    const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;
+    const rsrc_t r = make_rsrc(xf + ct * TILE_ELEMS, TILE_ELEMS * 2);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      ph[b] = bload16(r, po[b]);
+      pl[b] = bload16(r, po[b] + 8 * BLK_BYTES);
+    }
+  };
+  // Y^T = S^T Q^T of chunk c for both tiles of both slices, and a of chunk c
+  auto out_y = [&](int c, f32x4 (&Y)[2][2], float (&a)[2]) {
+    const int buf = c & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 sh[4], sl[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sh[s] = SBX[j][buf][0][s][lane];
+        sl[s] = SBX[j][buf][1][s][lane];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          y = mfma_bf16(as_bf16x8(sl[s]), as_bf16x8(qb[u][s]), y);
+          y = mfma_bf16(as_bf16x8(sh[s]), as_bf16x8(qb[u][s]), y);
+        }
+        Y[j][u] = y;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) a[u] = SCS[buf][16 * mt[u] + lr];
+  };
+  // O^T = a Y^T + U^T P^T of chunk c for both slices, stored non-temporally
+  auto out_o = [&](int c, const f32x4 (&Y)[2][2], const float (&a)[2]) {
+    const int buf = c & 1;
+    const int64_t t0 = s_begin + static_cast<int64_t>(c) * CH;
+    const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+    const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
+                                static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // U^T as A operand (token k-steps 0, 1), slots reversed to match the turned P blocks
+      uint4 uh[2], ul[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 u0 = UXF[j][buf][2 * s][lane], u1 = UXF[j][buf][2 * s + 1][lane];
+        uint2 h0, l0, h1, l1;
+        split4_packed(make_float4(u0[0], u0[1], u0[2], u0[3]), h0, l0);
+        split4_packed(make_float4(u1[0], u1[1], u1[2], u1[3]), h1, l1);
+        uh[s] = rev8(make_uint4(h0.x, h0.y, h1.x, h1.y));
+        ul[s] = rev8(make_uint4(l0.x, l0.y, l1.x, l1.y));
+      }
+      f32x4 O[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[u][i] = a[u] * Y[j][u][i];
+      auto up = [&](f32x4& acc, int b, int s) {
+        const bf16x8 bh = as_bf16x8(and4(ph[b], pm[b])), bl = as_bf16x8(and4(pl[b], pm[b]));
+        acc = mfma_bf16(as_bf16x8(uh[s]), bl, acc);
+        acc = mfma_bf16(as_bf16x8(ul[s]), bh, acc);
+        acc = mfma_bf16(as_bf16x8(uh[s]), bh, acc);
+      };
+      up(O[0], 0, 0);
+      up(O[1], 1, 0);
+      up(O[1], 2, 1);
+      const int ocol = (2 * pair + j) * 16 + 4 * lg;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t oo = static_cast<uint32_t>(((16 * mt[u] + lr) * nv * D + ocol) * sizeof(TO));
+        if constexpr (sizeof(TO) == 4) {
+          bstore16_nt(ro, oo, make_uint4(__float_as_uint(O[u][0]), __float_as_uint(O[u][1]),
+                                         __float_as_uint(O[u][2]), __float_as_uint(O[u][3])));
+        } else {
+          bstore8_nt(ro, oo,
+                     make_uint2(f32_to_bf16(O[u][0]) | (static_cast<uint32_t>(f32_to_bf16(O[u][1])) << 16),
+                                f32_to_bf16(O[u][2]) | (static_cast<uint32_t>(f32_to_bf16(O[u][3])) << 16)));
+        }
+      }
+    }
+  };
+
+  // wave 2 stages the masked T blocks, wave 3 the scalars and exp(G_C); each
+  // stages beta v for its slice
+  auto run = [&](auto tstager) {
+    constexpr bool TW = decltype(tstager)::value;
+    auto last = [&](int c) { return min(c, nchunks - 1); };
+    auto load_stage = [&](int cc) {
+      const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;
+      if constexpr (TW) {
+        const rsrc_t r = make_rsrc(xf + ct * TILE_ELEMS, TILE_ELEMS * 2);
+        constexpr int blk[6] = {0, 2, 4, 5, 6, 7};   // 2 m + s
+#pragma unroll
+        for (int b = 0; b < 6; ++b) {
+          sg[b] = bload16(r, blk[b] * BLK_BYTES + lo16);
+          sg[6 + b] = bload16(r, (8 + blk[b]) * BLK_BYTES + lo16);
+        }
+      } else {
+        sg[0] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
+        eg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
+      }
+      const rsrc_t rb = make_rsrc(scp + ct * 4 * CH + 3 * CH, CH * 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        sbeta[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rb, static_cast<uint32_t>((32 * i + (lane >> 1)) * 4), 0, 0));
+      const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+      const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+      if constexpr (!CV) {
+        // V rows past the sequence end read as zeros (resource sized to the valid rows)
+        const rsrc_t rv =
+            make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D, static_cast<uint32_t>(((L - 1) * vs + D) * 2));
+        svr[0] = bload16(rv, vo0);
+        svr[1] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
+      } else {
+        // window rows t - 3 .. t of x for both tokens; the resource starts 3
+        // rows early when those rows lie in the sequence (every chunk but the
+        // first) and ends at the last valid row, so rows before the sequence
+        // (offsets that wrap below zero) and after it read as zeros
+        const int pre = cc > 0 ? 3 : 0;
+        const rsrc_t rv = make_rsrc(v + (t0 - pre) * vs + static_cast<int64_t>(h) * D,
+                                    static_cast<uint32_t>(((L - 1 + pre) * vs + D) * 2));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 32 * i + (lane >> 1) - 3 + j + pre;   // row from the resource start (may be < 0)
+            cxr[i][j] = bload16(rv, static_cast<uint32_t>((static_cast<int64_t>(r) * vs + vcol) * 2));
+          }
+      }
+    };
+    // stage chunk cs (its loads are in sg, svr / cxr, sbeta) in LDS buffer cs & 1
+    auto stage = [&](int cs) {
+      const int buf = cs & 1;
+      if constexpr (TW) {
+        auto lowmask = [&](const uint4& x) { return make_uint4(x.x & dm.x, x.y & dm.y, 0u, 0u); };
+        auto highmask = [&](const uint4& x) { return make_uint4(x.x, x.y, x.z & dm.x, x.w & dm.y); };
+#pragma unroll
+        for (int pl2 = 0; pl2 < 2; ++pl2) {
+          const uint4* t = sg + 6 * pl2;
+          uint4* d = &TSX[buf][6 * pl2][0];
+          d[0 * 64 + lane] = lowmask(t[0]);    // (0, 0)
+          d[1 * 64 + lane] = highmask(t[1]);   // (1, 0)
+          d[2 * 64 + lane] = t[2];             // (2, 0)
+          d[3 * 64 + lane] = lowmask(t[3]);    // (2, 1)
+          d[4 * 64 + lane] = t[4];             // (3, 0)
+          d[5 * 64 + lane] = highmask(t[5]);   // (3, 1)
+        }
+      } else {
+        *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = sg[0];
+        if (lane == 0) EGS[buf] = bits_f(eg);
+      }
+      float* bvs = reinterpret_cast<float*>(&BVS[ow][buf][0][0]);
+      const int64_t t0 = s_begin + static_cast<int64_t>(last(cs)) * CH;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = 32 * i + (lane >> 1);
+        // slot of (t, column c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
+        float* base = bvs + ((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
+        if constexpr (CV) {
+          uint4 win[4] = {cxr[i][0], cxr[i][1], cxr[i][2], cxr[i][3]};
+          if (i == 0 && cs == 0 && t < 3 && cv.st) {   // the sequence's history from the conv state
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+              if (t - 3 + j < 0)
+                win[j] = gather8_bf16(cv.st + (static_cast<int64_t>(n) * cv.conv_dim + cch) * cv.state_len +
+                                          cv.state_len + (t - 3 + j),
+                                      cv.state_len);
+          }
+          float y[8];
+          conv4_silu8_bf16(win, cwt, cbs, y);
+          const bool pad = t0 + t >= s_end;   // rows past the sequence end stage zeros
+#pragma unroll
+          for (int e = 0; e < 8; ++e) base[(8 * (lane & 1) + e) * 4] = pad ? 0.0f : sbeta[i] * y[e];
+        } else {
+          const uint32_t d[4] = {svr[i].x, svr[i].y, svr[i].z, svr[i].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t bits = (e & 1) ? (d[e >> 1] & 0xffff0000u) : (d[e >> 1] << 16);
+            base[(8 * (lane & 1) + e) * 4] = sbeta[i] * __uint_as_float(bits);
+          }
+        }
+      }
+    };
+    load_q(0);
+    load_p(0);
+    load_stage(0);
+    stage(0);
+    load_stage(last(1));
+    __syncthreads();                     // B(0)
+    f32x4 Y[2][2];
+    float a[2];
+    out_y(0, Y, a);
+    load_q(last(1));
+    stage(1);
+    load_stage(last(2));
+    // the pass with c = nchunks (after B(n)) only stores the last chunk's
+    // output; its other work re-reads chunk n-1 data or stale buffers that
+    // nobody reads afterwards
+    for (int c = 1; c <= nchunks; ++c) {
+      __syncthreads();                   // B(c)
+      f32x4 Yn[2][2];
+      float an[2];
+      out_y(last(c), Yn, an);
+      load_q(last(c + 1));
+      out_o(c - 1, Y, a);
+      load_p(last(c));
+      stage(c + 1);
+      load_stage(last(c + 2));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) Y[j][u] = Yn[j][u];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) a[u] = an[u];
+    }
+  };
+  if (w == 2)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+}
+
 // ------------------------------------------------------------------ state: generic (fp32 inputs), one wave per 16 columns
 constexpr int KP = 132;    // LDS pitch (floats) of 64 x 128 K/Q tiles
 constexpr int RP = 18;     // LDS pitch of the 64 x 16 R / U tiles
@@ -1469,6 +1991,34 @@ constexpr size_t generic_lds_bytes() {
   return (2 * CH * KP + CH * AP + CH * 16) * sizeof(float) + CH * sizeof(float4) + CH * RP * sizeof(float);
 }
 
+// Compute units of the current device, asked once per device.
+int device_cus() {
+  constexpr int kDevs = 64;
+  static std::mutex mu;
+  static int cus[kDevs] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cus[dev]) {
+    int nc = 0;
+    if (hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || nc <= 0) nc = 256;
+    cus[dev] = nc;
+  }
+  return cus[dev];
+}
+
+// Which bf16 state kernel runs: the wide form (two slices per workgroup) when
+// a launch has at least twice as many 16-column slices as the device has CUs,
+// else the four-wave form. GDN_STATE_FORM=narrow or =wide in the environment
+// forces one; both give the same bits.
+bool use_wide_state(int64_t slices) {
+  if (const char* f = std::getenv("GDN_STATE_FORM")) {
+    if (std::strcmp(f, "wide") == 0) return true;
+    if (std::strcmp(f, "narrow") == 0) return false;
+  }
+  return slices >= 2 * static_cast<int64_t>(device_cus());
+}
+
 template <typename TIn>
 hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
                           const void* ga, const void* gb, int gm, const float* A_log, const float* dt_bias,
@@ -1520,6 +2070,20 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
                                 cv);
       return hipGetLastError();
     };
+    if (use_wide_state(static_cast<int64_t>(grid))) {
+      const unsigned wgrid = grid / 2;   // two slices per workgroup
+      auto launch_wide = [&](auto kern, auto* optr) {
+        kern<<<wgrid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order, S0, ST,
+                                   optr, cv);
+        return hipGetLastError();
+      };
+      if (cvp) {
+        if (o_bf16) return launch_wide(chunk_state_wide_kernel<uint16_t, true>, static_cast<uint16_t*>(o));
+        return launch_wide(chunk_state_wide_kernel<float, true>, static_cast<float*>(o));
+      }
+      if (o_bf16) return launch_wide(chunk_state_wide_kernel<uint16_t, false>, static_cast<uint16_t*>(o));
+      return launch_wide(chunk_state_wide_kernel<float, false>, static_cast<float*>(o));
+    }
     // Several sequences (cu_seqlens): two workgroups per CU, so that a CU can
     // take another (sequence, head, slice) while one runs a long sequence;
     // measured on 8 packed sequences of 512-16384 tokens, 11 % less time. One
