@@ -98,6 +98,12 @@ int gdn_gating(const void* a, const void* b, int ab_dtype,
  *            256-byte aligned; its contents on entry are ignored.
  * Supported: dk = dv = 128; in_dtype f32 or bf16; nv % nk == 0; token strides
  * up to 2^24 elements.
+ * For bf16 inputs the library picks one of two forms of its state kernel from
+ * the launch shape (one 16-column slice per workgroup, or two when there are
+ * at least twice as many slices as the device has CUs); both give the same
+ * bits. The environment variable GDN_STATE_FORM=narrow or =wide, read at each
+ * call, forces one (for tests and measurement). This applies to every chunk
+ * entry point below.
  */
 size_t gdn_chunk_fwd_workspace_size(int64_t T_tot, int n_seqs, int nk, int nv,
                                     int dk, int dv, int in_dtype);
