@@ -1285,9 +1285,9 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     run(std::false_type{});
 }
 // ------------------------------------------------------------------ state: bf16 inputs, two 16-column slices per workgroup
-// The wide form, for launches with at least twice as many 16-column slices
-// as CUs (several sequences, or many heads), where a CU's throughput matters
-// more than one slice's latency. One workgroup per (sequence, value head, 32
+// The wide form, for launches with more 16-column slices than CUs (several
+// sequences, or many heads), where a CU's throughput matters more than one
+// slice's latency. One workgroup per (sequence, value head, 32
 // value columns), four waves:
 //   Waves 0 and 1 (recurrence): wave j owns all 128 rows of S for the
 //     columns of slice 2 p + j (eight MFMA accumulators) and runs the chunk
@@ -2007,16 +2007,18 @@ int device_cus() {
   return cus[dev];
 }
 
-// Which bf16 state kernel runs: the wide form (two slices per workgroup) when
-// a launch has at least twice as many 16-column slices as the device has CUs,
-// else the four-wave form. GDN_STATE_FORM=narrow or =wide in the environment
-// forces one; both give the same bits.
+// Which bf16 state kernel runs: the four-wave form (one slice per workgroup,
+// the shorter chain) while every slice gets a CU of its own, else the wide
+// form (two slices per workgroup): once the four-wave form would need a
+// second round of workgroups, one wide round (about 5,000 cycles per chunk)
+// beats two four-wave rounds (about 2 x 2,700). GDN_STATE_FORM=narrow or
+// =wide in the environment forces one; both give the same bits.
 bool use_wide_state(int64_t slices) {
   if (const char* f = std::getenv("GDN_STATE_FORM")) {
     if (std::strcmp(f, "wide") == 0) return true;
     if (std::strcmp(f, "narrow") == 0) return false;
   }
-  return slices >= 2 * static_cast<int64_t>(device_cus());
+  return slices > static_cast<int64_t>(device_cus());
 }
 
 template <typename TIn>

@@ -100,7 +100,7 @@ int gdn_gating(const void* a, const void* b, int ab_dtype,
  * up to 2^24 elements.
  * For bf16 inputs the library picks one of two forms of its state kernel from
  * the launch shape (one 16-column slice per workgroup, or two when there are
- * at least twice as many slices as the device has CUs); both give the same
+ * more slices than the device has CUs); both give the same
  * bits. The environment variable GDN_STATE_FORM=narrow or =wide, read at each
  * call, forces one (for tests and measurement). This applies to every chunk
  * entry point below.

@@ -1,9 +1,9 @@
 """GPU tests of the two forms of the bf16 chunk state kernel.
 
-The library runs the four-wave form (one workgroup per 16-column slice) when a
-launch has few slices, and the wide form (two slices per workgroup, one
-recurrence wave per slice holding all 128 rows of S) when it has at least
-twice as many slices as the device has CUs; the environment variable
+The library runs the four-wave form (one workgroup per 16-column slice) while
+every slice gets a CU of its own, and the wide form (two slices per
+workgroup, one recurrence wave per slice holding all 128 rows of S) when a
+launch has more slices than the device has CUs; the environment variable
 GDN_STATE_FORM=narrow|wide forces either. The wide form sums K S in the same
 two halves as the four-wave form, so both give the same bits. These tests run
 each form on the same inputs and require equal o, final state and (for the
