@@ -277,6 +277,36 @@ def time_rows(gdn, W, stream, dev, reps=5, warmup=3):
         frac=round(tf / PEAK_BF16_TFLOPS, 4), algorithmic_bytes=vb, hbm_gbps_algorithmic=round(vb / (ms * 1e-3) / 1e9, 1),
         tokens_per_s=round(Tv / (ms * 1e-3), 1))
     del vx, vo, vst, vws
+    # one sequence with few heads (one GPU's share of the prefill workload under an 8-way head split): the
+    # segment-parallel prefill (the library's choice for this shape) against the unsplit call
+    sw = W.WORKLOADS["prefill_head_share_t8k"]
+    sx = W.chunk_inputs(sw, device=dev)
+    so = torch.empty((sw.T, sw.nv, sw.dv), device=dev)
+    sst = torch.empty((1, sw.nv, sw.dk, sw.dv), device=dev)
+    sws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(sw.T, 1, sw.nk, sw.nv), device=dev, dtype=torch.uint8)
+    seg_call = lambda: gdn.gdn_chunk_fwd_gated(sx["q"], sx["k"], sx["v"], sx["a"], sx["b"], sx["A_log"],
+                                               sx["dt_bias"], final_state=sst, o=so, workspace=sws, stream=stream)
+    ms = _timed(seg_call, 4 * reps, 4 * warmup, stream)
+    old_seg = os.environ.get("GDN_SEGMENTS")
+    os.environ["GDN_SEGMENTS"] = "1"
+    try:
+        ms_u = _timed(seg_call, 4 * reps, 4 * warmup, stream)
+    finally:
+        if old_seg is None:
+            del os.environ["GDN_SEGMENTS"]
+        else:
+            os.environ["GDN_SEGMENTS"] = old_seg
+    sflops = chunk_flops_per_token_head(r=sw.nv // sw.nk) * sw.T * sw.nv
+    tf = sflops / (ms * 1e-3) / 1e12
+    rows["chunk_fwd_segments"] = dict(
+        workload=f"prefill_head_share_t8k: T={sw.T}, {sw.nk}->{sw.nv} heads, zero initial state, gating folded in "
+                 f"(one GPU's share of prefill_chunk_t8k under an 8-way head split)",
+        kernel="segment_table + chunk_prep + chunk_state (8 segments: local states and transitions) + "
+               "segment_combine + chunk_state (rerun from the incoming states)", bound="mfma",
+        avg_ms=round(ms, 4), avg_ms_unsplit=round(ms_u, 4), speedup_vs_unsplit=round(ms_u / ms, 3),
+        algorithmic_flops=sflops, achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+        frac=round(tf / PEAK_BF16_TFLOPS, 4), tokens_per_s=round(sw.T / (ms * 1e-3), 1))
+    del sx, so, sst, sws
     out = torch.empty((T, wl.nv, wl.dv), device=dev)
     ms = _timed(lambda: gdn.gdn_gated_rmsnorm(o, x["z"], x["norm_w"], eps=1e-6, y=out, stream=stream),
                 reps, warmup, stream)

@@ -63,16 +63,26 @@ constexpr int TILE_ELEMS = CH * D;   // bf16 elements of one 16 KB operand tile
 // Workspace: chunk table | sequence order | per (chunk, value head): 16 KB tile, 1 KB of
 // per-token scalars, exp(G_C) | bf16 inputs only, per (chunk, key head): K and
 // Q operand tiles of 16 KB each.
+// Segment-parallel prefill (one sequence, bf16 inputs, at most four value
+// heads, i.e. at most 32 column slices): the sequence is split into up to
+// kMaxSeg segments of whole chunks, which the chunk table then treats as
+// sequences. The workspace reserves room for it whenever the shape allows it.
+constexpr int kMaxSeg = 16;
+inline bool seg_eligible(int n_seqs, int nv, bool bf16) { return bf16 && n_seqs == 1 && nv <= 4; }
+
 struct WsLayout {
-  size_t off_chunk_off, off_order, off_tp, off_sc, off_egc, off_kf, off_qf, total;
+  size_t off_chunk_off, off_order, off_tp, off_sc, off_egc, off_kf, off_qf, off_segcu, off_sega, off_segs, total;
 };
 inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
-  const int64_t nch = T / CH + n_seqs;   // >= sum_n ceil(len_n / 64)
+  const int64_t nch = T / CH + n_seqs;   // >= sum_n ceil(len_n / 64), also for segments of whole chunks
+  const bool seg = seg_eligible(n_seqs, nv, bf16);
+  const size_t ntab = seg ? kMaxSeg : static_cast<size_t>(n_seqs);   // chunk table entries
   const size_t tile_bytes = static_cast<size_t>(TILE_ELEMS) * 2;
+  const size_t state_bytes = static_cast<size_t>(nv) * D * D * sizeof(float);
   WsLayout w{};
   size_t o = 0;
-  w.off_chunk_off = o; o += (static_cast<size_t>(n_seqs) + 1) * sizeof(int32_t); o = (o + 255) & ~size_t(255);
-  w.off_order = o;     o += static_cast<size_t>(n_seqs) * sizeof(int32_t); o = (o + 255) & ~size_t(255);
+  w.off_chunk_off = o; o += (ntab + 1) * sizeof(int32_t); o = (o + 255) & ~size_t(255);
+  w.off_order = o;     o += ntab * sizeof(int32_t); o = (o + 255) & ~size_t(255);
   w.off_tp = o;        o += static_cast<size_t>(nch) * nv * tile_bytes;
   w.off_sc = o;        o += static_cast<size_t>(nch) * nv * CH * sizeof(float4);
   w.off_egc = o;       o += static_cast<size_t>(nch) * nv * sizeof(float); o = (o + 255) & ~size_t(255);
@@ -80,6 +90,12 @@ inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
   if (bf16) {
     w.off_kf = o;  o += static_cast<size_t>(nch) * nk * tile_bytes;
     w.off_qf = o;  o += static_cast<size_t>(nch) * nk * tile_bytes;
+  }
+  w.off_segcu = w.off_sega = w.off_segs = o;
+  if (seg) {   // segment bounds | final states of the first pass (D, then M) | incoming states
+    w.off_segcu = o; o += (kMaxSeg + 1) * sizeof(int32_t); o = (o + 255) & ~size_t(255);
+    w.off_sega = o;  o += 2 * kMaxSeg * state_bytes;
+    w.off_segs = o;  o += kMaxSeg * state_bytes;
   }
   w.total = o;
   return w;
@@ -137,6 +153,28 @@ __global__ void __launch_bounds__(256) chunk_offsets_kernel(const int32_t* __res
   } else {
     for (int n = tid; n < n_seqs; n += 256) order[n] = n;
   }
+}
+
+// Segment table of the segment-parallel prefill: segment p covers tokens
+// [b + p L, min(b + (p + 1) L, e)) of the one sequence [b, e) (b = 0, e = T
+// without cu_seqlens), L = 64 seg_chunks; segments past e are empty. Written
+// as the chunk table of P sequences: bounds, first chunk slots (every
+// segment but the last non-empty one holds seg_chunks whole chunks) and the
+// identity order.
+__global__ void __launch_bounds__(64) segment_table_kernel(const int32_t* __restrict__ cu, int64_t T,
+                                                           int seg_chunks, int P, int32_t* __restrict__ seg_cu,
+                                                           int32_t* __restrict__ off, int32_t* __restrict__ order) {
+  const int p = threadIdx.x;
+  if (p > P) return;
+  int64_t b = 0, e = T;
+  if (cu) {
+    b = min(max(static_cast<int64_t>(cu[0]), int64_t(0)), T);
+    e = min(max(static_cast<int64_t>(cu[1]), b), T);
+  }
+  const int64_t nc = (e - b + CH - 1) / CH;
+  seg_cu[p] = static_cast<int32_t>(p == P ? e : min(b + static_cast<int64_t>(p) * seg_chunks * CH, e));
+  off[p] = static_cast<int32_t>(min(static_cast<int64_t>(p) * seg_chunks, nc));
+  if (p < P) order[p] = p;
 }
 
 __device__ __forceinline__ int find_le(const int32_t* a, int n, int64_t x) {
@@ -769,6 +807,19 @@ __device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
 // lane l's 16 bytes in a padded LDS K block
 __device__ __forceinline__ int kl_lane(int l) { return 16 * l + 64 * (l >> 4); }
 
+// A pass of the segment-parallel prefill (one sequence split into P segments
+// of whole chunks, each a sequence of the chunk table). P = 0: an ordinary
+// launch. P > 0: launch sequence nn < P runs segment nn from a zero state
+// (its local final state D), and nn >= P runs segment nn - P from the
+// identity with v = 0 (its transition M); final states go to ST[nn].
+// no_out: no output stores. st_only >= 0: only that sequence writes its final
+// state, to ST[0].
+struct SegRun {
+  int P;
+  int no_out;
+  int st_only;
+};
+
 // CV: v is the conv input x at the first value channel (token stride vs); the
 // output waves apply the conv + SiLU to the value rows as they stage them,
 // wave 2 for tokens 0-31 of a chunk and wave 3 for tokens 32-63.
@@ -781,7 +832,7 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
     const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
     const int32_t* __restrict__ order, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o,
-    ConvIn cv) {
+    ConvIn cv, SegRun seg) {
   __shared__ f32x4 XPX[DUAL ? 1 : 2][2][4][64];   // partial X: [parity][half][token tile][lane]
   __shared__ uint4 SBX[DUAL ? 1 : 2][2][4][64];   // S as B operand: [parity][hi | lo][dk k-step][lane]
   constexpr int PB = DUAL ? 0 : 1;       // parity mask of XPX and SBX
@@ -798,8 +849,10 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   int slot, slice;
   state_unit_slice(blockIdx.x, gridDim.x / 8, nv / nk, slot, slice);
   // sequences in the chunk table's order (longest first), value heads fastest
-  const int n = cu ? order[slot / nv] : 0, h = slot % nv;
-  const int unit = n * nv + h;
+  const int nn = seg.P ? slot / nv : (cu ? order[slot / nv] : 0);
+  const bool trans = seg.P && nn >= seg.P;   // transition run: S0 = I, v = 0
+  const int n = trans ? nn - seg.P : nn, h = slot % nv;
+  const int unit = nn * nv + h;
   const int hk = h / (nv / nk);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -824,7 +877,8 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S[tt][i] = S0 ? S0[(static_cast<int64_t>(unit) * D + 64 * hf + 16 * tt + 4 * lg + i) * D + col] : 0.0f;
+          S[tt][i] = S0 ? S0[(static_cast<int64_t>(unit) * D + 64 * hf + 16 * tt + 4 * lg + i) * D + col]
+                        : (trans && 64 * hf + 16 * tt + 4 * lg + i == col ? 1.0f : 0.0f);
 
       if (nchunks > 0) {
         // operand blocks of one chunk, one register set: each group is reloaded
@@ -978,12 +1032,13 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
         }
         __syncthreads();                   // B(n): the last U is in LDS
       }
-      if (ST) {
+      if (ST && (seg.st_only < 0 || n == seg.st_only)) {
+        const int64_t su = seg.st_only < 0 ? unit : h;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            ST[(static_cast<int64_t>(unit) * D + 64 * hf + 16 * tt + 4 * lg + i) * D + col] = S[tt][i];
+            ST[(su * D + 64 * hf + 16 * tt + 4 * lg + i) * D + col] = S[tt][i];
       }
     };
     if (w == 0)
@@ -1123,8 +1178,9 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
     up(O[1], 2, 1);
     const int64_t t0 = s_begin + static_cast<int64_t>(c) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+    // (sized to nothing when the pass stores no output: stores past it are dropped)
     const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
-                                static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
+                                seg.no_out ? 0u : static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if constexpr (sizeof(TO) == 4) {
@@ -1156,11 +1212,12 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
         sg[0] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
         eg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
         if constexpr (!CV) {
-          // V rows past the sequence end read as zeros (resource sized to the valid rows)
+          // V rows past the sequence end read as zeros (resource sized to the
+          // valid rows; to nothing in a transition run, whose v is zero)
           const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
           const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-          const rsrc_t rv =
-              make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D, static_cast<uint32_t>(((L - 1) * vs + D) * 2));
+          const rsrc_t rv = make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D,
+                                      trans ? 0u : static_cast<uint32_t>(((L - 1) * vs + D) * 2));
           sg[1] = bload16(rv, vo0);
           sg[2] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
         }
@@ -1804,6 +1861,90 @@ __global__ void __launch_bounds__(256) chunk_state_wide_kernel(
     run(std::false_type{});
 }
 
+// ------------------------------------------------------------------ segment-parallel prefill: incoming states
+// A segment's final state is affine in its incoming state, S_out = M S_in + D,
+// with D the final state from a zero start and M the one from the identity
+// with v = 0 (both from the first pass, D_p = seg_a[p], M_p = seg_a[P + p]).
+// One workgroup per (value head, 16 columns) chains them in segment order:
+// S_in[0] = S0 (zero if none), S_in[p + 1] = M_p S_in[p] + D_p. The products
+// run on MFMA with both fp32 operands split into bf16 hi + lo (three
+// passes); wave w forms rows 16 w .. 16 w + 15. M and D do not depend on the
+// chain, so their loads run three steps ahead (a ring of three register
+// sets; the loop is unrolled by three so that every set index is a constant).
+constexpr int SCP = 132;   // LDS pitch (floats) of the transposed 16 x 128 slice
+__global__ void __launch_bounds__(512) segment_combine_kernel(const float* __restrict__ seg_a,
+                                                              const float* __restrict__ S0, int P, int nv,
+                                                              float* __restrict__ seg_s) {
+  __shared__ __attribute__((aligned(16))) float St[2][16][SCP];   // S_in[p] of this slice: [column][row]
+  const int h = blockIdx.x / 8, slice = blockIdx.x % 8;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int col = slice * 16 + lr;
+  const size_t st = static_cast<size_t>(D) * D;
+  for (int e = tid; e < D * 16; e += 512) {
+    const int row = e >> 4, cc = e & 15;
+    const size_t idx = static_cast<size_t>(h) * st + static_cast<size_t>(row) * D + slice * 16 + cc;
+    const float x = S0 ? S0[idx] : 0.0f;
+    St[0][cc][row] = x;
+    seg_s[idx] = x;
+  }
+  // per set: row 16 w + lr of M_p at k-slots 32 s + 8 lg .. +7, and D_p at
+  // this lane's rows 16 w + 4 lg + i, column col
+  float4 am[3][4][2];
+  float dv[3][4];
+  auto load = [&](auto setc, int p) {
+    constexpr int r3 = decltype(setc)::value;
+    if (p + 1 >= P) return;
+    const float* r = seg_a + (static_cast<size_t>(P + p) * nv + h) * st + static_cast<size_t>(16 * w + lr) * D + 8 * lg;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      am[r3][s4][0] = *reinterpret_cast<const float4*>(r + 32 * s4);
+      am[r3][s4][1] = *reinterpret_cast<const float4*>(r + 32 * s4 + 4);
+    }
+    const float* Dp = seg_a + (static_cast<size_t>(p) * nv + h) * st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dv[r3][i] = Dp[static_cast<size_t>(16 * w + 4 * lg + i) * D + col];
+  };
+  auto step = [&](auto setc, int p) {
+    constexpr int r3 = decltype(setc)::value;
+    if (p + 1 >= P) return;
+    const int buf = p & 1;
+    float* out = seg_s + (static_cast<size_t>(p + 1) * nv + h) * st;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float4 a0 = am[r3][s4][0], a1 = am[r3][s4][1];
+      const float4 b0 = *reinterpret_cast<const float4*>(&St[buf][lr][32 * s4 + 8 * lg]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&St[buf][lr][32 * s4 + 8 * lg + 4]);
+      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      Mma<true, false, false>::run(acc, a, b);
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = acc[i] + dv[r3][i];
+    load(setc, p + 3);   // this set is free again
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * w + 4 * lg + i;
+      out[static_cast<size_t>(row) * D + col] = x[i];
+      St[buf ^ 1][lr][row] = x[i];
+    }
+    __syncthreads();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  load(C0{}, 0);
+  load(C1{}, 1);
+  load(C2{}, 2);
+  __syncthreads();
+  for (int p = 0; p + 1 < P; p += 3) {
+    step(C0{}, p);
+    step(C1{}, p + 1);
+    step(C2{}, p + 2);
+  }
+}
+
 // ------------------------------------------------------------------ state: generic (fp32 inputs), one wave per 16 columns
 constexpr int KP = 132;    // LDS pitch (floats) of 64 x 128 K/Q tiles
 constexpr int RP = 18;     // LDS pitch of the 64 x 16 R / U tiles
@@ -2021,6 +2162,25 @@ bool use_wide_state(int64_t slices) {
   return slices > static_cast<int64_t>(device_cus());
 }
 
+// Segments of the segment-parallel prefill for this call (1 = not split):
+// eight, of at least four chunks each. Pass 1 runs 2 P nv 8 workgroups (a
+// local state and a transition per segment and 16-column slice), 512 at four
+// value heads, two rounds on 256 CUs; measured at 8192 tokens, eight segments
+// beat four at 1, 2 and 4 value heads and sixteen at 1. The count depends on
+// the shape only, not on the device, so results do not either.
+// GDN_SEGMENTS=<P> in the environment forces a count (1 = unsplit).
+int segment_count(int64_t T, int n_seqs, int nv, bool bf16, int& seg_chunks) {
+  seg_chunks = 0;
+  if (!seg_eligible(n_seqs, nv, bf16)) return 1;
+  const int64_t nc = (T + CH - 1) / CH;
+  int64_t P = std::min<int64_t>(8, nc / 4);
+  if (const char* f = std::getenv("GDN_SEGMENTS")) P = std::min<int64_t>(std::atoi(f), nc);
+  P = std::min<int64_t>(P, kMaxSeg);
+  if (P < 2) return 1;
+  seg_chunks = static_cast<int>((nc + P - 1) / P);
+  return static_cast<int>((nc + seg_chunks - 1) / seg_chunks);
+}
+
 template <typename TIn>
 hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
                           const void* ga, const void* gb, int gm, const float* A_log, const float* dt_bias,
@@ -2041,7 +2201,17 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
 
   const int64_t nch = T / CH + n_seqs;
   hipError_t e = hipSuccess;
-  if (cu) {   // varlen chunk table (one sequence needs none)
+  // segment-parallel prefill: the segments become the sequences of the chunk table
+  int seg_chunks = 0;
+  const int P = cvp ? 1 : segment_count(T, n_seqs, nv, BF, seg_chunks);
+  if (P > 1) {
+    int32_t* seg_cu = reinterpret_cast<int32_t*>(base + lay.off_segcu);
+    segment_table_kernel<<<1, 64, 0, s>>>(cu, T, seg_chunks, P, seg_cu, chunk_off, order);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    cu = seg_cu;
+    n_seqs = P;
+  } else if (cu) {   // varlen chunk table (one sequence needs none)
     chunk_offsets_kernel<<<1, 256, 0, s>>>(cu, n_seqs, T, static_cast<int32_t>(nch), chunk_off, order);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -2069,9 +2239,30 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     const uint16_t* vb = static_cast<const uint16_t*>(v);
     auto launch = [&](auto kern, auto* optr) {
       kern<<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order, S0, ST, optr,
-                                cv);
+                                cv, SegRun{0, 0, -1});
       return hipGetLastError();
     };
+    if (P > 1) {
+      // pass 1: every segment from zero (D) and from the identity with v = 0
+      // (M), no outputs; then the incoming states; pass 2: every segment from
+      // its incoming state, outputs, and the last one's final state
+      float* seg_a = reinterpret_cast<float*>(base + lay.off_sega);
+      float* seg_s = reinterpret_cast<float*>(base + lay.off_segs);
+      auto passes = [&](auto kern, auto* optr) {
+        kern<<<2 * grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order,
+                                      nullptr, seg_a, optr, cv, SegRun{P, 1, -1});
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        segment_combine_kernel<<<nv * (D / 16), 512, 0, s>>>(seg_a, S0, P, nv, seg_s);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        kern<<<grid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order, seg_s, ST,
+                                  optr, cv, SegRun{0, 0, P - 1});
+        return hipGetLastError();
+      };
+      if (o_bf16) return passes(chunk_state_bf16_kernel<uint16_t, false, false>, static_cast<uint16_t*>(o));
+      return passes(chunk_state_bf16_kernel<float, false, false>, static_cast<float*>(o));
+    }
     if (use_wide_state(static_cast<int64_t>(grid))) {
       const unsigned wgrid = grid / 2;   // two slices per workgroup
       auto launch_wide = [&](auto kern, auto* optr) {

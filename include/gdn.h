@@ -104,6 +104,19 @@ int gdn_gating(const void* a, const void* b, int ab_dtype,
  * bits. The environment variable GDN_STATE_FORM=narrow or =wide, read at each
  * call, forces one (for tests and measurement). This applies to every chunk
  * entry point below.
+ * Segment-parallel prefill: one sequence (n_seqs == 1) with bf16 inputs and
+ * at most four value heads has few independent recurrences (8 per value head),
+ * so gdn_chunk_fwd and gdn_chunk_fwd_gated split it into up to eight segments
+ * of at least four chunks. Each segment's final state is affine in its
+ * incoming state, S_out = M S_in + D: a first pass forms every segment's D
+ * (from a zero state) and M (from the identity with v = 0), a small kernel
+ * chains the incoming states in segment order, and a second pass reruns every
+ * segment from its incoming state, writing o and the final state. The split
+ * depends on the shape only, so results do not depend on the device; they
+ * differ from the unsplit call by rounding only. GDN_SEGMENTS=<P> in the
+ * environment (read at each call) forces P segments, 1 = unsplit. The
+ * workspace size includes room for up to 16 segments whenever the shape
+ * allows the split.
  */
 size_t gdn_chunk_fwd_workspace_size(int64_t T_tot, int n_seqs, int nk, int nv,
                                     int dk, int dv, int in_dtype);

@@ -96,6 +96,21 @@ def test_workspace_size_is_monotone_and_positive(L):
     assert gdn.gdn_chunk_fwd_workspace_size(-1, 1, 16, 32) == 0
 
 
+def test_workspace_reserves_segment_states_for_one_sequence_with_few_heads(L):
+    """One sequence with bf16 inputs and at most four value heads may run as up to 16 segments: the workspace
+    then also holds 3 x 16 fp32 states per value head (local states, transitions, incoming states)."""
+    state = 128 * 128 * 4
+    for nk, nv in [(1, 1), (1, 2), (2, 4)]:
+        one = gdn.gdn_chunk_fwd_workspace_size(8192, 1, nk, nv)
+        two = gdn.gdn_chunk_fwd_workspace_size(8192, 2, nk, nv)
+        assert one >= two + 3 * 16 * nv * state - 256 * 1024   # two sequences hold one more chunk slot
+    # not for fp32 inputs, several sequences or more heads
+    wide = gdn.gdn_chunk_fwd_workspace_size(8192, 1, 4, 8)
+    assert wide < gdn.gdn_chunk_fwd_workspace_size(8192, 2, 4, 8) + 3 * 16 * 8 * state
+    f32 = gdn.gdn_chunk_fwd_workspace_size(8192, 1, 1, 2, in_dtype=gdn.F32)
+    assert f32 < gdn.gdn_chunk_fwd_workspace_size(8192, 2, 1, 2, in_dtype=gdn.F32) + 3 * 16 * 2 * state
+
+
 def _rec(L, **kw):
     a = dict(q=P, k=P, v=P, in_dtype=1, qs=0, ks=0, vs=0, g=P, beta=P, cu=NULL, n=4, T=4, nk=2, nv=4, dk=128,
              dv=128, scale=0.0, l2=1, state=P2, o=P, o_dtype=0, stream=NULL)

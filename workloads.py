@@ -62,6 +62,9 @@ WORKLOADS = {
     "decode_256seq": Workload("decode_256seq", 4, "decode", "bf16", n_seqs=256, nk=16, nv=32,
                               s0_std=0.02),
     "long_fused_t256k": Workload("long_fused_t256k", 5, "fused", "bf16", T=262144, nk=16, nv=64),
+    # one GPU's share of prefill_chunk_t8k when its 16 key heads are split over 8 GPUs: few column
+    # slices, the shape the segment-parallel prefill is for
+    "prefill_head_share_t8k": Workload("prefill_head_share_t8k", 7, "chunk", "bf16", T=8192, nk=2, nv=4),
     # decode with multi-token prediction: each sequence carries 1 + 3 draft tokens
     "decode_mtp_256x4": Workload("decode_mtp_256x4", 6, "decode", "bf16", n_seqs=256, nk=16, nv=32,
                                  s0_std=0.02, extra=dict(tokens_per_seq=4)),
