@@ -2,11 +2,13 @@
 
 gdn_chunk_fwd_gated_noalloc runs the same kernels as gdn_chunk_fwd_gated with
 the library's per-device scratch array in place of the workspace, so its
-outputs must equal that entry point's bit for bit. Three calls in a row go
+outputs must equal that entry point's bit for bit. Four calls in a row go
 through the C ABI on the same GPU, each smaller than the one before (the
-prefill T=8192 workload, then a varlen batch with initial states, then a
-small fp32 call), so each call reuses the scratch the previous one left
-behind; each is compared with a fresh gdn_chunk_fwd_gated call.
+prefill T=8192 workload, then one GPU's share of it under an 8-way head
+split, which runs segment-parallel, then a varlen batch with initial
+states, then a small fp32 call), so each call reuses the scratch the
+previous one left behind; each is compared with a fresh
+gdn_chunk_fwd_gated call.
 """
 import pytest
 import torch
@@ -60,6 +62,14 @@ def test_noalloc_equals_workspace_entry_point_on_calls_of_shrinking_size():
     o, st, o_ref, st_ref = _both(d)
     assert torch.isfinite(o).all()
     assert torch.equal(o, o_ref) and torch.equal(st, st_ref), "T=8192: no-alloc call differs"
+    del d, o, st, o_ref, st_ref
+
+    print("[case] noalloc: prefill_head_share_t8k (segment-parallel), with an initial state", flush=True)
+    wl, d = _inputs("prefill_head_share_t8k")
+    S0 = 0.05 * torch.randn(1, wl.nv, 128, 128, device=dev(), generator=torch.Generator(dev()).manual_seed(9))
+    o, st, o_ref, st_ref = _both(d, None, S0)
+    assert torch.isfinite(o).all()
+    assert torch.equal(o, o_ref) and torch.equal(st, st_ref), "segment-parallel call: no-alloc call differs"
     del d, o, st, o_ref, st_ref
 
     print("[case] noalloc: varlen 4 sequences, bf16, initial states", flush=True)
