@@ -63,12 +63,12 @@ constexpr int TILE_ELEMS = CH * D;   // bf16 elements of one 16 KB operand tile
 // Workspace: chunk table | sequence order | per (chunk, value head): 16 KB tile, 1 KB of
 // per-token scalars, exp(G_C) | bf16 inputs only, per (chunk, key head): K and
 // Q operand tiles of 16 KB each.
-// Segment-parallel prefill (one sequence, bf16 inputs, at most four value
-// heads, i.e. at most 32 column slices): the sequence is split into up to
+// Segment-parallel prefill (one sequence, bf16 inputs, at most eight value
+// heads, i.e. at most 64 column slices): the sequence is split into up to
 // kMaxSeg segments of whole chunks, which the chunk table then treats as
 // sequences. The workspace reserves room for it whenever the shape allows it.
 constexpr int kMaxSeg = 16;
-inline bool seg_eligible(int n_seqs, int nv, bool bf16) { return bf16 && n_seqs == 1 && nv <= 4; }
+inline bool seg_eligible(int n_seqs, int nv, bool bf16) { return bf16 && n_seqs == 1 && nv <= 8; }
 
 struct WsLayout {
   size_t off_chunk_off, off_order, off_tp, off_sc, off_egc, off_kf, off_qf, off_segcu, off_sega, off_segs, total;
@@ -2162,18 +2162,21 @@ bool use_wide_state(int64_t slices) {
   return slices > static_cast<int64_t>(device_cus());
 }
 
-// Segments of the segment-parallel prefill for this call (1 = not split):
-// eight, of at least four chunks each. Pass 1 runs 2 P nv 8 workgroups (a
-// local state and a transition per segment and 16-column slice), 512 at four
-// value heads, two rounds on 256 CUs; measured at 8192 tokens, eight segments
-// beat four at 1, 2 and 4 value heads and sixteen at 1. The count depends on
-// the shape only, not on the device, so results do not either.
-// GDN_SEGMENTS=<P> in the environment forces a count (1 = unsplit).
+// Segments of the segment-parallel prefill for this call (1 = not split).
+// The split triples the recurrence work (pass 1 forms a local state and a
+// transition per segment and 16-column slice, pass 2 reruns the segment), so
+// it pays where 3 x (value heads x 8) slices still fit the 256 CUs of an
+// MI355X: eight segments (of at least four chunks) up to four value heads;
+// four from five to eight heads, for sequences of at least 256 chunks, where
+// the gain (measured 1.12x at 16384 tokens, 1.29x at 262144) outweighs the
+// fixed cost of the extra launches. The count depends on the shape only, not
+// on the device, so results do not either. GDN_SEGMENTS=<P> in the
+// environment forces a count (1 = unsplit).
 int segment_count(int64_t T, int n_seqs, int nv, bool bf16, int& seg_chunks) {
   seg_chunks = 0;
   if (!seg_eligible(n_seqs, nv, bf16)) return 1;
   const int64_t nc = (T + CH - 1) / CH;
-  int64_t P = std::min<int64_t>(8, nc / 4);
+  int64_t P = nv <= 4 ? std::min<int64_t>(8, nc / 4) : (nc >= 256 ? 4 : 1);
   if (const char* f = std::getenv("GDN_SEGMENTS")) P = std::min<int64_t>(std::atoi(f), nc);
   P = std::min<int64_t>(P, kMaxSeg);
   if (P < 2) return 1;

@@ -105,9 +105,10 @@ int gdn_gating(const void* a, const void* b, int ab_dtype,
  * call, forces one (for tests and measurement). This applies to every chunk
  * entry point below.
  * Segment-parallel prefill: one sequence (n_seqs == 1) with bf16 inputs and
- * at most four value heads has few independent recurrences (8 per value head),
- * so gdn_chunk_fwd and gdn_chunk_fwd_gated split it into up to eight segments
- * of at least four chunks. Each segment's final state is affine in its
+ * at most eight value heads has few independent recurrences (8 per value
+ * head), so gdn_chunk_fwd and gdn_chunk_fwd_gated split it into segments of
+ * whole chunks: eight (of at least four chunks) up to four value heads, four
+ * from five to eight heads when the sequence has at least 256 chunks. Each segment's final state is affine in its
  * incoming state, S_out = M S_in + D: a first pass forms every segment's D
  * (from a zero state) and M (from the identity with v = 0), a small kernel
  * chains the incoming states in segment order, and a second pass reruns every

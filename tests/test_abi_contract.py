@@ -97,16 +97,16 @@ def test_workspace_size_is_monotone_and_positive(L):
 
 
 def test_workspace_reserves_segment_states_for_one_sequence_with_few_heads(L):
-    """One sequence with bf16 inputs and at most four value heads may run as up to 16 segments: the workspace
+    """One sequence with bf16 inputs and at most eight value heads may run as up to 16 segments: the workspace
     then also holds 3 x 16 fp32 states per value head (local states, transitions, incoming states)."""
     state = 128 * 128 * 4
-    for nk, nv in [(1, 1), (1, 2), (2, 4)]:
+    for nk, nv in [(1, 1), (1, 2), (2, 4), (2, 8)]:
         one = gdn.gdn_chunk_fwd_workspace_size(8192, 1, nk, nv)
         two = gdn.gdn_chunk_fwd_workspace_size(8192, 2, nk, nv)
-        assert one >= two + 3 * 16 * nv * state - 256 * 1024   # two sequences hold one more chunk slot
+        assert one >= two + 3 * 16 * nv * state - 512 * 1024   # two sequences hold one more chunk slot
     # not for fp32 inputs, several sequences or more heads
-    wide = gdn.gdn_chunk_fwd_workspace_size(8192, 1, 4, 8)
-    assert wide < gdn.gdn_chunk_fwd_workspace_size(8192, 2, 4, 8) + 3 * 16 * 8 * state
+    wide = gdn.gdn_chunk_fwd_workspace_size(8192, 1, 4, 16)
+    assert wide < gdn.gdn_chunk_fwd_workspace_size(8192, 2, 4, 16) + 3 * 16 * 16 * state
     f32 = gdn.gdn_chunk_fwd_workspace_size(8192, 1, 1, 2, in_dtype=gdn.F32)
     assert f32 < gdn.gdn_chunk_fwd_workspace_size(8192, 2, 1, 2, in_dtype=gdn.F32) + 3 * 16 * 2 * state
 

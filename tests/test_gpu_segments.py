@@ -1,15 +1,17 @@
-"""GPU tests of the segment-parallel chunk prefill (one sequence, at most four value heads).
+"""GPU tests of the segment-parallel chunk prefill (one sequence, at most eight value heads).
 
-One sequence whose 16-column slices are few (nv * 8 <= 32) is split into P
+One sequence whose 16-column slices are few (nv * 8 <= 64) is split into P
 segments of whole chunks: a first pass runs every segment from a zero state
 and from the identity with v = 0, a small kernel chains the incoming states
 S_in[p + 1] = M_p S_in[p] + D_p, and a second pass reruns every segment from
 its incoming state. The segment count depends on the shape only
-(eight segments of at least four chunks each); GDN_SEGMENTS=<P> forces one
-(1 = unsplit). Its rounding differs from the unsplit call, so
+(eight segments of at least four chunks up to four value heads, four from
+five to eight heads for sequences of at least 256 chunks); GDN_SEGMENTS=<P>
+forces one (1 = unsplit). Its rounding differs from the unsplit call, so
 each case is compared with the fp64 oracle at the bf16 bar and with the
 unsplit call at the sum of the two bars. Cases: one GPU's share of the
-prefill workload under an 8-way head split (T = 8192, 2 -> 4 heads), ragged
+prefill workload under an 8-way head split (T = 8192, 2 -> 4 heads), eight
+value heads over 16384 tokens, ragged
 lengths, initial states, cu_seqlens given (same bits as without), bf16
 output, g and beta given, a slow decay in which the incoming states carry
 across segments, and segments of a single chunk. Each test prints its case
@@ -117,6 +119,13 @@ def test_segments_cases(ci):
     x = _inputs(c["T"], c["nk"], c["nv"], 20 + ci, 0.3 if c["s0"] else 0.0)
     o_dtype = torch.bfloat16 if c.get("o_dtype") == "bf16" else torch.float32
     _check(x, c["s0"], c["P"], c["name"], o_dtype)
+
+
+def test_segments_eight_heads_long():
+    """Eight value heads (2 -> 8) and T = 16384: four segments by default (sequences of 256 chunks or more)."""
+    _say("segments: T=16384, 2->8 heads, default count")
+    x = _inputs(16384, 2, 8, 61, 0.3)
+    _check(x, True, None, "eight heads")
 
 
 def test_segments_slow_decay():
