@@ -409,13 +409,17 @@ __device__ __forceinline__ void gram_pairs(const TIn* Ks, const TIn* Qs, int lr,
 // Causal conv1d (4 taps) + SiLU folded into the chunk kernels: x holds the
 // packed q | k | v channels (conv_dim = 2 nk D + nv D, bf16); the conv state
 // [n_seqs, conv_dim, state_len] (or none: zero history) supplies the three
-// inputs before each sequence's first token.
+// inputs before each sequence's first token. seq_split: the launch's
+// sequences are the segments of one sequence (starting at cu[0]), so the
+// three inputs before a segment's first token are x rows unless it is the
+// first segment.
 struct ConvIn {
   const float* w;          // [conv_dim, 4]
   const float* b;          // [conv_dim] or null
   const uint16_t* st;      // conv state in, or null
   int state_len;
   int conv_dim;
+  int seq_split;
 };
 
 // (at most 128 VGPRs: four waves per SIMD, i.e. four blocks per CU, which is
@@ -491,16 +495,19 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
       for (int j = 0; j < 4; ++j) wt[j][e] = cv.w[(ch0 + e) * 4 + j];
       bs[e] = cv.b ? cv.b[ch0 + e] : 0.0f;
     }
+    // the sequence's own first token and conv-state row (a split sequence's)
+    const int64_t hb = cv.seq_split ? cu[0] : s_begin;
+    const int hn = cv.seq_split ? 0 : n;
     uint4 raw[11];
 #pragma unroll
     for (int u = 0; u < 11; ++u) {
       const int r = 8 * rb - 3 + u;
       const int64_t t = t0 + r;
-      if (r < L && t >= s_begin)
+      if (r < L && t >= hb)
         raw[u] = *reinterpret_cast<const uint4*>(q + t * qs + ch0);
-      else if (t < s_begin && cv.st)   // history of the sequence (t - s_begin in -3 .. -1)
-        raw[u] = gather8_bf16(cv.st + (static_cast<int64_t>(n) * cv.conv_dim + ch0) * cv.state_len + cv.state_len +
-                                  (t - s_begin),
+      else if (t < hb && cv.st)   // history of the sequence (t - hb in -3 .. -1)
+        raw[u] = gather8_bf16(cv.st + (static_cast<int64_t>(hn) * cv.conv_dim + ch0) * cv.state_len + cv.state_len +
+                                  (t - hb),
                               cv.state_len);
       else
         raw[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -863,6 +870,10 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
   seq_bounds(cu, n, T, s_begin, s_end);
   int cbase, nchunks;
   chunk_span(chunk_off, cu, T, n, cbase, nchunks);
+  // with the conv: the sequence's own first token and conv-state row (those
+  // of the split sequence when the launch's sequences are its segments)
+  const int64_t hb = cv.seq_split ? cu[0] : s_begin;
+  const int hn = cv.seq_split ? 0 : n;
 
   if (w < 2) {
     // ================================================================ recurrence waves
@@ -1224,12 +1235,12 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
       }
       if constexpr (CV) {
         // window rows ctok - 3 .. ctok of x; the resource starts 3 rows early
-        // when those rows lie in the sequence (every chunk but the first) and
-        // ends at the last valid row, so rows before the sequence (offsets that
-        // wrap below zero) and after it read as zeros
+        // when those rows lie in the sequence (every chunk but the sequence's
+        // first) and ends at the last valid row, so rows before the sequence
+        // (offsets that wrap below zero) and after it read as zeros
         const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
         const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
-        const int pre = cc > 0 ? 3 : 0;
+        const int pre = static_cast<int>(min<int64_t>(3, t0 - hb));
         const rsrc_t rv = make_rsrc(v + (t0 - pre) * vs + static_cast<int64_t>(h) * D,
                                     static_cast<uint32_t>(((L - 1 + pre) * vs + D) * 2));
 #pragma unroll
@@ -1268,18 +1279,19 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
         const int t = ctok;
         const float be = TW ? cbeta : SCS[buf][3 * CH + t];   // wave 3 wrote SCS above
         uint4 win[4] = {cxr[0], cxr[1], cxr[2], cxr[3]};
-        if (cs == 0 && t < 3 && cv.st) {   // the sequence's history from the conv state
+        if (cs == 0 && s_begin == hb && t < 3 && cv.st) {   // the sequence's history from the conv state
 #pragma unroll
           for (int j = 0; j < 3; ++j)
             if (t - 3 + j < 0)
-              win[j] = gather8_bf16(cv.st + (static_cast<int64_t>(n) * cv.conv_dim + cch) * cv.state_len +
+              win[j] = gather8_bf16(cv.st + (static_cast<int64_t>(hn) * cv.conv_dim + cch) * cv.state_len +
                                         cv.state_len + (t - 3 + j),
                                     cv.state_len);
         }
         float y[8];
         conv4_silu8_bf16(win, cwt, cbs, y);
         const int64_t t0 = s_begin + static_cast<int64_t>(last(cs)) * CH;
-        const bool pad = t0 + t >= s_end;   // rows past the sequence end stage zeros
+        // rows past the sequence end stage zeros, and so does a transition run (v = 0)
+        const bool pad = t0 + t >= s_end || trans;
         float* bvs = reinterpret_cast<float*>(&BVS[buf][0][0]);
         float* base = bvs + ((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
 #pragma unroll
@@ -2191,7 +2203,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
                           int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
                           const ConvIn* cvp, hipStream_t s) {
   constexpr bool BF = sizeof(TIn) == 2;
-  const ConvIn cv = cvp ? *cvp : ConvIn{nullptr, nullptr, nullptr, 0, 0};
+  ConvIn cv = cvp ? *cvp : ConvIn{nullptr, nullptr, nullptr, 0, 0, 0};
   const WsLayout lay = ws_layout(T, n_seqs, nk, nv, BF);
   char* base = static_cast<char*>(ws);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + lay.off_chunk_off);
@@ -2206,8 +2218,9 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
   hipError_t e = hipSuccess;
   // segment-parallel prefill: the segments become the sequences of the chunk table
   int seg_chunks = 0;
-  const int P = cvp ? 1 : segment_count(T, n_seqs, nv, BF, seg_chunks);
+  const int P = segment_count(T, n_seqs, nv, BF, seg_chunks);
   if (P > 1) {
+    cv.seq_split = 1;
     int32_t* seg_cu = reinterpret_cast<int32_t*>(base + lay.off_segcu);
     segment_table_kernel<<<1, 64, 0, s>>>(cu, T, seg_chunks, P, seg_cu, chunk_off, order);
     e = hipGetLastError();
@@ -2263,6 +2276,10 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
                                   optr, cv, SegRun{0, 0, P - 1});
         return hipGetLastError();
       };
+      if (cvp) {
+        if (o_bf16) return passes(chunk_state_bf16_kernel<uint16_t, true, false>, static_cast<uint16_t*>(o));
+        return passes(chunk_state_bf16_kernel<float, true, false>, static_cast<float*>(o));
+      }
       if (o_bf16) return passes(chunk_state_bf16_kernel<uint16_t, false, false>, static_cast<uint16_t*>(o));
       return passes(chunk_state_bf16_kernel<float, false, false>, static_cast<float*>(o));
     }
@@ -2383,7 +2400,7 @@ hipError_t launch_chunk_fwd_conv(const void* x, int64_t xs, const float* conv_w,
                                  int nk, int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16,
                                  void* ws, hipStream_t s) {
   const int conv_dim = (2 * nk + nv) * D;
-  const ConvIn cv{conv_w, conv_b, static_cast<const uint16_t*>(conv_st), state_len, conv_dim};
+  const ConvIn cv{conv_w, conv_b, static_cast<const uint16_t*>(conv_st), state_len, conv_dim, 0};
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   return chunk_dispatch<uint16_t>(xb, xb + nk * D, xb + 2 * nk * D, xs, xs, xs, a, b, gm, A_log, dt_bias, cu, n_seqs,
                                   T, nk, nv, scale, l2, S0, ST, o, o_bf16, ws, &cv, s);

@@ -114,7 +114,9 @@ int gdn_gating(const void* a, const void* b, int ab_dtype,
  * chains the incoming states in segment order, and a second pass reruns every
  * segment from its incoming state, writing o and the final state. The split
  * depends on the shape only, so results do not depend on the device; they
- * differ from the unsplit call by rounding only. GDN_SEGMENTS=<P> in the
+ * differ from the unsplit call by rounding only. gdn_prefill_fused splits the
+ * same way (the conv inputs before a segment's first token are then x rows;
+ * the conv state only precedes the first segment). GDN_SEGMENTS=<P> in the
  * environment (read at each call) forces P segments, 1 = unsplit. The
  * workspace size includes room for up to 16 segments whenever the shape
  * allows the split.

@@ -9,7 +9,9 @@ its incoming state. The segment count depends on the shape only
 five to eight heads for sequences of at least 256 chunks); GDN_SEGMENTS=<P>
 forces one (1 = unsplit). Its rounding differs from the unsplit call, so
 each case is compared with the fp64 oracle at the bf16 bar and with the
-unsplit call at the sum of the two bars. Cases: one GPU's share of the
+unsplit call at the sum of the two bars. The fused prefill (conv inside the
+chunk kernels) splits the same way and must equal its separate launches bit
+for bit. Cases: one GPU's share of the
 prefill workload under an 8-way head split (T = 8192, 2 -> 4 heads), eight
 value heads over 16384 tokens, ragged
 lengths, initial states, cu_seqlens given (same bits as without), bf16
@@ -26,6 +28,7 @@ import torch
 
 import gated_deltanet_gdn_amd as gdn
 import oracle
+import test_gpu_prefill_fused as PF
 import workloads as W
 from gpu_common import TOL, assert_close, dev, f64
 
@@ -164,3 +167,39 @@ def test_segments_given_g_beta():
                                      threads=THREADS)
     assert_close(o, o_ref, TOL["bf16"], "given g, beta: o")
     assert_close(st, s_ref, TOL["bf16"], "given g, beta: final state")
+
+
+FUSED_CASES = [
+    dict(name="fused_ragged_bias_history_P4", T=5000, nk=1, nv=2, bias=True, conv_state=True, s0=True, P=4),
+    dict(name="fused_history5_P3_bf16_out", T=1000, nk=2, nv=4, conv_state=True, state_len=5, o_dtype="bf16", P=3),
+    dict(name="fused_eight_heads_default_count", T=16384, nk=2, nv=8, conv_state=True, P=None),
+    dict(name="fused_strided_x_f32_gating_P8", T=3000, nk=1, nv=4, bias=True, s0=True, ab="f32", pad=64, P=8),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(FUSED_CASES)), ids=[c["name"] for c in FUSED_CASES])
+def test_segments_fused_prefill(ci):
+    """gdn_prefill_fused split into segments: the conv inputs before a segment's first token are x rows (the
+    conv state only before the first segment), and a transition run stages zero values. It must equal the
+    separate conv, gating and (equally split) chunk launches bit for bit, write the same conv state as the
+    unsplit call, and match the unsplit call's o and final state at the sum of the two bars."""
+    c = FUSED_CASES[ci]
+    _say("segments, fused prefill", c)
+    d = PF._inputs(c, 80 + ci)
+    with _segments(c["P"]):
+        o_s, st_s, cs_s = PF._separate(d, c["nk"], c["nv"])
+        o_f, st_f, cs_f = PF._fused(d, c["nk"], c["nv"])
+    with _segments(1):
+        o_u, st_u, cs_u = PF._fused(d, c["nk"], c["nv"])
+    torch.cuda.synchronize()
+    PF._same(o_f, o_s, "o")
+    PF._same(st_f, st_s, "final state")
+    PF._same(cs_f, cs_s, "conv state out")
+    assert torch.equal(cs_f, cs_u), "conv state out differs from the unsplit call"
+    if d["o_dtype"] == torch.float32:
+        assert_close(o_f, f64(o_u), 2 * TOL["bf16"], f"{c['name']} segmented vs unsplit o")
+    else:
+        ref = f64(o_u)
+        rms = np.sqrt(np.mean(ref ** 2))
+        assert np.all(np.abs(f64(o_f) - ref) <= 2 * TOL["bf16"] * rms + np.abs(ref) * 2.0 ** -7 + 1e-30)
+    assert_close(st_f, f64(st_u), 2 * TOL["bf16"], f"{c['name']} segmented vs unsplit final state")
