@@ -153,6 +153,30 @@ def test_segments_cu_seqlens_same_bits():
     assert torch.equal(o_a, o_b) and torch.equal(s_a, s_b)
 
 
+def test_segments_sequence_shorter_than_the_buffer():
+    """cu_seqlens = [0, 2300] over buffers of 4096 tokens: the segments are cut from the sequence's own length
+    (those past its end are empty), and the tokens it holds match the oracle and the unsplit call."""
+    _say("segments: one sequence of 2300 tokens in buffers of 4096, 1->2 heads, P=8")
+    x = _inputs(4096, 1, 2, 43, 0.3)
+    Ts = 2300
+    d = _dev(x)
+    cu = torch.tensor([0, Ts], dtype=torch.int32, device=dev())
+    call = lambda: gdn.gdn_chunk_fwd_gated(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                           cu_seqlens=cu, initial_state=d["S0"])
+    with _segments(8):
+        o_s, s_s = call()
+    with _segments(1):
+        o_u, s_u = call()
+    torch.cuda.synchronize()
+    xs = {k: (v[:Ts] if isinstance(v, torch.Tensor) and k in ("q", "k", "v", "a", "b") else v) for k, v in x.items()}
+    xs["cu_seqlens"] = torch.tensor([0, Ts], dtype=torch.int32)
+    o_ref, s_ref = _oracle(xs, True)
+    assert_close(o_s[:Ts], o_ref, TOL["bf16"], "short sequence: segmented o")
+    assert_close(s_s, s_ref, TOL["bf16"], "short sequence: segmented final state")
+    assert_close(o_s[:Ts], f64(o_u[:Ts]), 2 * TOL["bf16"], "short sequence: segmented vs unsplit o")
+    assert_close(s_s, f64(s_u), 2 * TOL["bf16"], "short sequence: segmented vs unsplit final state")
+
+
 def test_segments_given_g_beta():
     """gdn_chunk_fwd (g and beta given), segmented, against the oracle."""
     _say("segments: g and beta given, T=2500, 2->4 heads, P=6")
