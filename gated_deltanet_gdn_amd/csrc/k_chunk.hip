@@ -1370,6 +1370,11 @@ __global__ void __launch_bounds__(256) chunk_state_bf16_kernel(
 // Staging: wave 2 the masked T blocks, wave 3 the per-token scalars and
 // exp(G_C), both one chunk ahead; wave 2 stages beta v for slice 2 p, wave 3
 // for slice 2 p + 1, each for all 64 tokens of a chunk (beta from memory).
+// With the conv (CV) the workgroup has eight waves: waves 4-7 stage beta v
+// instead, each convolving one token per lane for one slice and half of the
+// chunk (waves 4, 5: slice 2 p, tokens 0-31 and 32-63; waves 6, 7: slice
+// 2 p + 1), so the output waves, which set the pace when they convolve, keep
+// only their products and the T and scalar staging.
 // One barrier per chunk; every LDS buffer shared between waves is
 // double-buffered by chunk parity as in the four-wave form.
 __device__ __forceinline__ void wide_unit_pair(int b, int n_units, int r, int& unit_slot, int& pair) {
@@ -1389,7 +1394,7 @@ __device__ __forceinline__ void wide_unit_pair(int b, int n_units, int r, int& u
 }
 
 template <typename TO, bool CV>
-__global__ void __launch_bounds__(256) chunk_state_wide_kernel(
+__global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
     const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
     int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
     const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
@@ -1589,6 +1594,82 @@ __global__ void __launch_bounds__(256) chunk_state_wide_kernel(
     return;
   }
 
+  auto last = [&](int c) { return min(c, nchunks - 1); };
+  if constexpr (CV) {
+    if (w >= 4) {
+      // ============================================================== conv waves
+      if (nchunks == 0) return;
+      const int j = (w - 4) >> 1;          // slice 2 pair + j
+      const int t = 32 * ((w - 4) & 1) + (lane >> 1);   // this lane's token in a chunk
+      const int vcol = (2 * pair + j) * 16 + 8 * (lane & 1);
+      const int cch = 2 * nk * D + h * D + vcol;   // first conv channel of those columns
+      float cwt[4][8], cbs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) cwt[q4][e] = cv.w[(cch + e) * 4 + q4];
+        cbs[e] = cv.b ? cv.b[cch + e] : 0.0f;
+      }
+      uint4 cxr[4];                        // window rows t - 3 .. t
+      float sb = 0.0f;                     // beta of the token
+      // the resource starts 3 rows early when those rows lie in the sequence
+      // (every chunk but the first) and ends at the last valid row, so rows
+      // before the sequence (offsets that wrap below zero) and after it read
+      // as zeros
+      auto load_conv = [&](int cc) {
+        const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;
+        sb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           make_rsrc(scp + ct * 4 * CH + 3 * CH, CH * 4),
+                                           static_cast<uint32_t>(t * 4), 0, 0));
+        const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+        const int pre = cc > 0 ? 3 : 0;
+        const rsrc_t rv = make_rsrc(v + (t0 - pre) * vs + static_cast<int64_t>(h) * D,
+                                    static_cast<uint32_t>(((L - 1 + pre) * vs + D) * 2));
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r = t - 3 + q4 + pre;   // row from the resource start (may be < 0)
+          cxr[q4] = bload16(rv, static_cast<uint32_t>((static_cast<int64_t>(r) * vs + vcol) * 2));
+        }
+      };
+      // beta v of chunk cs (its loads are in cxr, sb) into LDS buffer cs & 1
+      auto stage_conv = [&](int cs) {
+        const int buf = cs & 1;
+        uint4 win[4] = {cxr[0], cxr[1], cxr[2], cxr[3]};
+        if (cs == 0 && t < 3 && cv.st) {   // the sequence's history from the conv state
+#pragma unroll
+          for (int q4 = 0; q4 < 3; ++q4)
+            if (t - 3 + q4 < 0)
+              win[q4] = gather8_bf16(cv.st + (static_cast<int64_t>(n) * cv.conv_dim + cch) * cv.state_len +
+                                         cv.state_len + (t - 3 + q4),
+                                     cv.state_len);
+        }
+        float y[8];
+        conv4_silu8_bf16(win, cwt, cbs, y);
+        const int64_t t0 = s_begin + static_cast<int64_t>(last(cs)) * CH;
+        const bool pad = t0 + t >= s_end;   // rows past the sequence end stage zeros
+        float* bvs = reinterpret_cast<float*>(&BVS[j][buf][0][0]);
+        // slot of (t, column c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
+        float* base = bvs + ((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) base[(8 * (lane & 1) + e) * 4] = pad ? 0.0f : sb * y[e];
+      };
+      // the same staging order as the output waves' (chunk c + 1 between B(c) and B(c + 1))
+      load_conv(0);
+      stage_conv(0);
+      load_conv(last(1));
+      __syncthreads();                     // B(0)
+      stage_conv(1);
+      load_conv(last(2));
+      for (int c = 1; c <= nchunks; ++c) {
+        __syncthreads();                   // B(c)
+        stage_conv(c + 1);
+        load_conv(last(c + 2));
+      }
+      return;
+    }
+  }
+
   // ================================================================ output waves
   if (nchunks == 0) return;
   const int ow = w - 2;
@@ -1610,23 +1691,13 @@ __global__ void __launch_bounds__(256) chunk_state_wide_kernel(
     pm[b] = make_uint4(mm[0], mm[1], mm[2], mm[3]);
     po[b] = static_cast<uint32_t>((2 * (3 - m) + 1 - s) * BLK_BYTES + (63 - lane) * 16);
   }
-  // beta v staging for slice 2 p + ow: lane l takes tokens l / 2 and 32 + l / 2,
-  // columns 8 (l % 2) .. +7 of the head (offsets from the head's first value column)
+  // beta v staging for slice 2 p + ow (without the conv): lane l takes tokens
+  // l / 2 and 32 + l / 2, columns 8 (l % 2) .. +7 of the head (offsets from
+  // the head's first value column)
   const int vcol = (2 * pair + ow) * 16 + 8 * (lane & 1);
   const uint32_t vo0 = static_cast<uint32_t>(((lane >> 1) * vs + vcol) * 2);
-  const int cch = 2 * nk * D + h * D + vcol;   // first conv channel of those columns
-  float cwt[4][8], cbs[8];
-  uint4 cxr[2][4];                       // staging: window rows of both tokens
   uint4 svr[2];                          // staging: value rows of both tokens
   float sbeta[2];                        // staging: beta of both tokens
-  if constexpr (CV) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cwt[j][e] = cv.w[(cch + e) * 4 + j];
-      cbs[e] = cv.b ? cv.b[cch + e] : 0.0f;
-    }
-  }
   uint2 dm;                              // T staging masks as in the four-wave form
   {
     uint32_t mm[2];
@@ -1736,7 +1807,6 @@ __global__ void __launch_bounds__(256) chunk_state_wide_kernel(
   // stages beta v for its slice
   auto run = [&](auto tstager) {
     constexpr bool TW = decltype(tstager)::value;
-    auto last = [&](int c) { return min(c, nchunks - 1); };
     auto load_stage = [&](int cc) {
       const size_t ct = static_cast<size_t>(cbase + cc) * nv + h;
       if constexpr (TW) {
@@ -1751,37 +1821,22 @@ __global__ void __launch_bounds__(256) chunk_state_wide_kernel(
         sg[0] = bload16(make_rsrc(scp + ct * 4 * CH, 4 * CH * 4), lo16);
         eg = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(egc + ct, 4), lo16 & 0u, 0, 0);
       }
-      const rsrc_t rb = make_rsrc(scp + ct * 4 * CH + 3 * CH, CH * 4);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        sbeta[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 rb, static_cast<uint32_t>((32 * i + (lane >> 1)) * 4), 0, 0));
-      const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
-      const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
       if constexpr (!CV) {
+        const rsrc_t rb = make_rsrc(scp + ct * 4 * CH + 3 * CH, CH * 4);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          sbeta[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rb, static_cast<uint32_t>((32 * i + (lane >> 1)) * 4), 0, 0));
         // V rows past the sequence end read as zeros (resource sized to the valid rows)
+        const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
         const rsrc_t rv =
             make_rsrc(v + t0 * vs + static_cast<int64_t>(h) * D, static_cast<uint32_t>(((L - 1) * vs + D) * 2));
         svr[0] = bload16(rv, vo0);
         svr[1] = bload16(rv, vo0 + static_cast<uint32_t>(32 * vs * 2));
-      } else {
-        // window rows t - 3 .. t of x for both tokens; the resource starts 3
-        // rows early when those rows lie in the sequence (every chunk but the
-        // first) and ends at the last valid row, so rows before the sequence
-        // (offsets that wrap below zero) and after it read as zeros
-        const int pre = cc > 0 ? 3 : 0;
-        const rsrc_t rv = make_rsrc(v + (t0 - pre) * vs + static_cast<int64_t>(h) * D,
-                                    static_cast<uint32_t>(((L - 1 + pre) * vs + D) * 2));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 32 * i + (lane >> 1) - 3 + j + pre;   // row from the resource start (may be < 0)
-            cxr[i][j] = bload16(rv, static_cast<uint32_t>((static_cast<int64_t>(r) * vs + vcol) * 2));
-          }
       }
     };
-    // stage chunk cs (its loads are in sg, svr / cxr, sbeta) in LDS buffer cs & 1
+    // stage chunk cs (its loads are in sg, svr, sbeta) in LDS buffer cs & 1
     auto stage = [&](int cs) {
       const int buf = cs & 1;
       if constexpr (TW) {
@@ -1802,29 +1857,13 @@ __global__ void __launch_bounds__(256) chunk_state_wide_kernel(
         *reinterpret_cast<uint4*>(&SCS[buf][4 * lane]) = sg[0];
         if (lane == 0) EGS[buf] = bits_f(eg);
       }
-      float* bvs = reinterpret_cast<float*>(&BVS[ow][buf][0][0]);
-      const int64_t t0 = s_begin + static_cast<int64_t>(last(cs)) * CH;
+      if constexpr (!CV) {
+        float* bvs = reinterpret_cast<float*>(&BVS[ow][buf][0][0]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = 32 * i + (lane >> 1);
-        // slot of (t, column c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
-        float* base = bvs + ((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
-        if constexpr (CV) {
-          uint4 win[4] = {cxr[i][0], cxr[i][1], cxr[i][2], cxr[i][3]};
-          if (i == 0 && cs == 0 && t < 3 && cv.st) {   // the sequence's history from the conv state
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-              if (t - 3 + j < 0)
-                win[j] = gather8_bf16(cv.st + (static_cast<int64_t>(n) * cv.conv_dim + cch) * cv.state_len +
-                                          cv.state_len + (t - 3 + j),
-                                      cv.state_len);
-          }
-          float y[8];
-          conv4_silu8_bf16(win, cwt, cbs, y);
-          const bool pad = t0 + t >= s_end;   // rows past the sequence end stage zeros
-#pragma unroll
-          for (int e = 0; e < 8; ++e) base[(8 * (lane & 1) + e) * 4] = pad ? 0.0f : sbeta[i] * y[e];
-        } else {
+        for (int i = 0; i < 2; ++i) {
+          const int t = 32 * i + (lane >> 1);
+          // slot of (t, column c): tile t / 16, lane c + 16 ((t % 16) / 4), row t % 4
+          float* base = bvs + ((t >> 4) * 64 + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
           const uint32_t d[4] = {svr[i].x, svr[i].y, svr[i].z, svr[i].w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -2285,9 +2324,9 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     }
     if (use_wide_state(static_cast<int64_t>(grid))) {
       const unsigned wgrid = grid / 2;   // two slices per workgroup
-      auto launch_wide = [&](auto kern, auto* optr) {
-        kern<<<wgrid, 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order, S0, ST,
-                                   optr, cv);
+      auto launch_wide = [&](auto kern, auto* optr) {   // eight waves with the conv (conv waves), else four
+        kern<<<wgrid, cvp ? 512 : 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order,
+                                              S0, ST, optr, cv);
         return hipGetLastError();
       };
       if (cvp) {
