@@ -20,7 +20,7 @@ __all__ = [
     "gdn_abi_version", "gdn_status_string", "gdn_last_error",
     "gdn_gating", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_gated", "gdn_recurrent_fwd",
     "gdn_causal_conv1d", "gdn_causal_conv1d_update", "gdn_gated_rmsnorm", "gdn_decode_step_fused",
-    "gdn_prefill_fused", "gdn_chunk_fwd_noalloc_max_bytes", "gdn_chunk_fwd_gated_noalloc",
+    "gdn_prefill_fused", "gdn_chunk_fwd_noalloc_max_bytes", "gdn_chunk_fwd_gated_noalloc", "gdn_prefill_fused_norm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -65,6 +65,8 @@ def lib():
                                               i32, i32, i32, f32, i32, vp, vp, vp, i32, vp]),
         "gdn_prefill_fused": (i32, [vp, i32, i64, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i64,
                                     i32, i32, i32, i32, f32, i32, vp, vp, vp, i32, vp, sz, vp]),
+        "gdn_prefill_fused_norm": (i32, [vp, i32, i64, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i64,
+                                         i32, i32, i32, i32, f32, i32, vp, vp, vp, i32, vp, f32, vp, vp, sz, vp]),
         "gdn_decode_step_fused": (i32, [vp, i32, i64, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                         i32, i32, f32, i32, vp, vp, i32, vp, vp, i32, vp]),
     }
@@ -288,6 +290,50 @@ def gdn_prefill_fused(x, conv_weight, a, b, A_log, dt_bias, nk, nv, conv_bias=No
                                  _stream(stream))
     _check("gdn_prefill_fused", st)
     return o, final_state, conv_state_out
+
+
+def gdn_prefill_fused_norm(x, conv_weight, a, b, A_log, dt_bias, nk, nv, z, norm_weight, eps=1e-6,
+                           conv_bias=None, cu_seqlens=None, conv_state_in=None, conv_state_out=None, state_len=None,
+                           output_conv_state=True, initial_state=None, output_final_state=True, final_state=None,
+                           y=None, scale=None, qk_l2norm=True, workspace=None, stream=None):
+    """gdn_prefill_fused followed by the gated RMSNorm of its output, in one call: y [T, nv, 128] fp32 =
+    o rms(o)^-1 (1 + norm_weight) z sigmoid(z), with z [T, nv, 128] bf16 dense. Returns (y, final_state,
+    conv_state_out)."""
+    _need(x, "x", contiguous=False)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x: expected a [T, conv_dim] view with dense channels")
+    _need(conv_weight, "conv_weight", torch.float32)
+    _need(a, "a"); _need(b, "b", a.dtype)
+    _need(A_log, "A_log", torch.float32); _need(dt_bias, "dt_bias", torch.float32)
+    _need(z, "z"); _need(norm_weight, "norm_weight", torch.float32)
+    T, C = x.shape
+    K = conv_weight.shape[1]
+    dk = dv = 128
+    cu, n = _cu(cu_seqlens, T)
+    if state_len is None:
+        state_len = conv_state_in.shape[2] if conv_state_in is not None else K - 1
+    if conv_state_in is not None:
+        _need(conv_state_in, "conv_state_in", x.dtype)
+    if conv_state_out is None and output_conv_state:
+        conv_state_out = torch.empty((n, C, state_len), device=x.device, dtype=x.dtype)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, nv, dk, dv), device=x.device, dtype=torch.float32)
+    if y is None:
+        y = torch.empty((T, nv, dv), device=x.device, dtype=torch.float32)
+    need = gdn_chunk_fwd_workspace_size(T, n, nk, nv, dk, dv, _dt(x, "x"))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
+    st = lib().gdn_prefill_fused_norm(_ptr(x), _dt(x, "x"), x.stride(0), _ptr(conv_weight), _ptr(conv_bias), K,
+                                      _ptr(conv_state_in), _ptr(conv_state_out), state_len, _ptr(a), _ptr(b),
+                                      _dt(a, "a"), _ptr(A_log), _ptr(dt_bias), _ptr(cu), n, T, nk, nv, dk, dv,
+                                      float(scale or 0.0), int(bool(qk_l2norm)), _ptr(initial_state),
+                                      _ptr(final_state), _ptr(z), _dt(z, "z"), _ptr(norm_weight), float(eps),
+                                      _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
+    _check("gdn_prefill_fused_norm", st)
+    return y, final_state, conv_state_out
 
 
 def gdn_recurrent_fwd(q, k, v, g, beta, state, cu_seqlens=None, o=None, o_dtype=torch.float32, scale=None,

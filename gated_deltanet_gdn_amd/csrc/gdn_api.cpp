@@ -226,13 +226,17 @@ int gdn_chunk_fwd_gated_noalloc(const void* q, const void* k, const void* v, int
                   fn);
 }
 
-int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const float* conv_weight,
-                      const float* conv_bias, int K, const void* conv_state_in, void* conv_state_out, int state_len,
-                      const void* a, const void* b, int ab_dtype, const float* A_log, const float* dt_bias,
-                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv,
-                      float scale, int qk_l2norm, const float* initial_state, float* final_state, void* o,
-                      int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "gdn_prefill_fused";
+}  // extern "C"
+
+namespace {
+// gdn_prefill_fused and gdn_prefill_fused_norm: the same checks and launches;
+// ne (the norm epilogue) is null for the former.
+int prefill_fused_impl(const char* fn, const void* x, int dtype, int64_t x_tok_stride, const float* conv_weight,
+                       const float* conv_bias, int K, const void* conv_state_in, void* conv_state_out, int state_len,
+                       const void* a, const void* b, int ab_dtype, const float* A_log, const float* dt_bias,
+                       const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv,
+                       float scale, int qk_l2norm, const float* initial_state, float* final_state, void* o,
+                       int o_dtype, const gdn::NormEpi* ne, void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_dtype(dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not f32/bf16", fn, dtype);
   if (dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: only bf16 x is built", fn);
   if (!valid_dtype(ab_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: ab_dtype %d is not f32/bf16", fn, ab_dtype);
@@ -259,6 +263,8 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const floa
   if (!workspace) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace is required", fn);
   if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
   if (const int gst = check_chunk_grid(fn, T_tot, n_seqs, nv); gst != GDN_OK) return gst;
+  if (ne && !grid_fits((T_tot * nv + 7) / 8, 256))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many rows for one launch", fn);
   const size_t need = gdn::chunk_workspace_bytes(T_tot, n_seqs, nk, nv, 1);
   if (workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
@@ -276,11 +282,47 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const floa
   hipError_t e = gdn::launch_chunk_fwd_conv(x, x_tok_stride, conv_weight, conv_bias, conv_state_in, state_len, a, b,
                                             ab_dtype == GDN_BF16 ? 1 : 2, A_log, dt_bias, cu_seqlens, n_seqs, T_tot,
                                             nk, nv, scale, qk_l2norm != 0, initial_state, final_state, o,
-                                            o_dtype == GDN_BF16, workspace, s);
+                                            o_dtype == GDN_BF16, workspace, ne, s);
   if (e == hipSuccess && conv_state_out)   // after the chunk kernels, which read conv_state_in
     e = gdn::launch_conv_state_out(x, 1, x_tok_stride, cu_seqlens, n_seqs, T_tot, static_cast<int>(conv_dim),
                                    conv_state_in, conv_state_out, state_len, s);
   return launched(e, fn);
+}
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride, const float* conv_weight,
+                      const float* conv_bias, int K, const void* conv_state_in, void* conv_state_out, int state_len,
+                      const void* a, const void* b, int ab_dtype, const float* A_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv, int dk, int dv,
+                      float scale, int qk_l2norm, const float* initial_state, float* final_state, void* o,
+                      int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_fused_impl("gdn_prefill_fused", x, dtype, x_tok_stride, conv_weight, conv_bias, K, conv_state_in,
+                            conv_state_out, state_len, a, b, ab_dtype, A_log, dt_bias, cu_seqlens, n_seqs, T_tot, nk,
+                            nv, dk, dv, scale, qk_l2norm, initial_state, final_state, o, o_dtype, nullptr, workspace,
+                            workspace_bytes, stream);
+}
+
+int gdn_prefill_fused_norm(const void* x, int dtype, int64_t x_tok_stride, const float* conv_weight,
+                           const float* conv_bias, int K, const void* conv_state_in, void* conv_state_out,
+                           int state_len, const void* a, const void* b, int ab_dtype, const float* A_log,
+                           const float* dt_bias, const int32_t* cu_seqlens, int n_seqs, int64_t T_tot, int nk, int nv,
+                           int dk, int dv, float scale, int qk_l2norm, const float* initial_state, float* final_state,
+                           const void* z, int z_dtype, const float* norm_weight, float eps, float* y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_prefill_fused_norm";
+  if (!valid_dtype(z_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: z_dtype %d is not f32/bf16", fn, z_dtype);
+  if (z_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: only bf16 z is built", fn);
+  if (!norm_weight) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: norm_weight is required", fn);
+  if (!(eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: eps must be >= 0", fn);
+  if (T_tot > 0 && !z) return fail(GDN_ERR_INVALID_ARGUMENT, "%s: z is required", fn);
+  if (z && !aligned(z, 16)) return fail(GDN_ERR_UNSUPPORTED, "%s: z must be 16-byte aligned", fn);
+  const gdn::NormEpi ne{static_cast<const uint16_t*>(z), norm_weight, eps};
+  return prefill_fused_impl(fn, x, dtype, x_tok_stride, conv_weight, conv_bias, K, conv_state_in, conv_state_out,
+                            state_len, a, b, ab_dtype, A_log, dt_bias, cu_seqlens, n_seqs, T_tot, nk, nv, dk, dv,
+                            scale, qk_l2norm, initial_state, final_state, y, GDN_F32, &ne, workspace,
+                            workspace_bytes, stream);
 }
 
 int gdn_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype, int64_t q_tok_stride,

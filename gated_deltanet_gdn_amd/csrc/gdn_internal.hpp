@@ -68,13 +68,24 @@ hipError_t launch_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
                                     int64_t T, int nk, int nv, float scale, int l2, const float* S0, float* ST,
                                     void* o, int o_bf16, hipStream_t s);
 
+// Gated RMSNorm applied to the chunked path's output: y = o rms(o)^-1 (1 + w)
+// z sigmoid(z) per (token, value head) row of 128; z bf16 [T, nv, 128] dense.
+struct NormEpi {
+  const uint16_t* z;
+  const float* w;
+  float eps;
+};
+
 // The chunked path with the causal conv1d (4 taps) + SiLU folded in, bf16 x
 // [T, (2 nk + nv) 128] with token stride xs; gating inputs as for gm = 1 / 2.
-// The conv state out is not written here (launch_conv_state_out).
+// The conv state out is not written here (launch_conv_state_out). With ne,
+// o (fp32) receives the normalized output: inside the state kernel when its
+// wide form runs with every workgroup resident, else by the norm kernel in
+// place afterwards.
 hipError_t launch_chunk_fwd_conv(const void* x, int64_t xs, const float* conv_w, const float* conv_b,
                                  const void* conv_st, int state_len, const void* a, const void* b, int gm,
                                  const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs, int64_t T,
                                  int nk, int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16,
-                                 void* ws, hipStream_t s);
+                                 void* ws, const NormEpi* ne, hipStream_t s);
 
 }  // namespace gdn

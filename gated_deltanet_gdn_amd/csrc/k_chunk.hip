@@ -71,8 +71,12 @@ constexpr int kMaxSeg = 16;
 inline bool seg_eligible(int n_seqs, int nv, bool bf16) { return bf16 && n_seqs == 1 && nv <= 8; }
 
 struct WsLayout {
-  size_t off_chunk_off, off_order, off_tp, off_sc, off_egc, off_kf, off_qf, off_segcu, off_sega, off_segs, total;
+  size_t off_chunk_off, off_order, off_tp, off_sc, off_egc, off_kf, off_qf, off_segcu, off_sega, off_segs, off_ring,
+      total;
 };
+// ring of the norm epilogue's row partial sums: per (sequence, value head)
+// 6 chunk slots x 4 column pairs x 64 rows of 8 bytes (EPI_RING, below)
+constexpr size_t kRingBytesPerUnit = size_t(6) * 4 * 64 * 8;
 inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
   const int64_t nch = T / CH + n_seqs;   // >= sum_n ceil(len_n / 64), also for segments of whole chunks
   const bool seg = seg_eligible(n_seqs, nv, bf16);
@@ -97,6 +101,8 @@ inline WsLayout ws_layout(int64_t T, int n_seqs, int nk, int nv, bool bf16) {
     w.off_sega = o;  o += 2 * kMaxSeg * state_bytes;
     w.off_segs = o;  o += kMaxSeg * state_bytes;
   }
+  w.off_ring = o;
+  if (bf16) { o += static_cast<size_t>(n_seqs) * nv * kRingBytesPerUnit; o = (o + 255) & ~size_t(255); }
   w.total = o;
   return w;
 }
@@ -421,6 +427,34 @@ struct ConvIn {
   int conv_dim;
   int seq_split;
 };
+
+// Gated RMSNorm epilogue inside the wide state kernel (with the conv): the
+// kernel writes y = o rms(o)^-1 (1 + w) z sigmoid(z) per (token, value head)
+// row of 128 in place of o. A row's 128 columns come from the four workgroups
+// (column pairs) of its head: each publishes its row partial sums of squares
+// of chunk c in ring slot c % EPI_RING as one 64-bit word (the fp32 bits, and
+// c + 1 in the high half, so a reader needs no separate flag or fence), and
+// normalizes chunk c, kept in an LDS ring, EPI_LAG chunks later, once the
+// four words of each row carry that tag. A workgroup publishes chunk c before
+// it waits for chunk c - EPI_LAG, so waits only ever point at older chunks,
+// and the launch is cooperative (all workgroups resident). Each wait is
+// bounded (EPI_SPIN polls); a row whose partial sums never arrive comes out
+// NaN rather than hanging the device. The ring is cleared before each launch.
+struct EpiIn {
+  const uint16_t* z;             // [T, nv, 128] bf16, dense
+  const float* w;                // [128]
+  float eps;
+  unsigned long long* ring;      // [n_units][EPI_RING][4 pairs][64 rows]
+};
+constexpr int EPI_LAG = 2;
+constexpr int EPI_RING = 6;      // >= 2 EPI_LAG + 1: no slot is rewritten before its last reader read it
+static_assert(kRingBytesPerUnit == size_t(EPI_RING) * 4 * CH * 8, "ring size");
+
+__global__ void __launch_bounds__(256) clear_u64_kernel(unsigned long long* __restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+constexpr int EPI_SPIN = 1 << 20;
 
 // (at most 128 VGPRs: four waves per SIMD, i.e. four blocks per CU, which is
 // also what the LDS holds)
@@ -1393,13 +1427,18 @@ __device__ __forceinline__ void wide_unit_pair(int b, int n_units, int r, int& u
   }
 }
 
-template <typename TO, bool CV>
+// EPI (with CV only): the gated RMSNorm epilogue described at EpiIn; the
+// output waves keep o in an LDS ring and publish row partial sums, and the conv
+// waves normalize each chunk EPI_LAG chunks later and store y in place of o.
+// One more barrier follows the last chunk.
+template <typename TO, bool CV, bool EPI>
 __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
     const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu, int n_seqs, int64_t T, int nk,
     int nv, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ xf, const float* __restrict__ scp,
     const float* __restrict__ egc, const uint16_t* __restrict__ kf, const uint16_t* __restrict__ qf,
     const int32_t* __restrict__ order, const float* __restrict__ S0, float* __restrict__ ST, TO* __restrict__ o,
-    ConvIn cv) {
+    ConvIn cv, EpiIn ep) {
+  static_assert(!EPI || CV, "the epilogue runs on the conv waves");
   __shared__ uint4 SBX[2][2][2][4][64];  // S as B operand: [slice][parity][hi | lo][dk k-step][lane]
   __shared__ f32x4 UXF[2][2][4][64];     // U: [slice][parity][token tile][lane]
   __shared__ f32x4 BVS[2][2][4][64];     // beta * v: [slice][parity][token tile][lane]
@@ -1409,6 +1448,8 @@ __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char KLX[2][16][KL_BLK];
   __shared__ __attribute__((aligned(16))) float SCS[2][4 * CH];   // planes a | b | c | beta
   __shared__ float EGS[2];               // exp(G_C)
+  // epilogue: o of the last EPI_LAG + 1 chunks, [chunk % 3][token][the pair's 32 columns]
+  __shared__ __attribute__((aligned(16))) float ORX[EPI ? EPI_LAG + 1 : 1][EPI ? CH : 1][EPI ? 32 : 4];
 
   int slot, pair;
   wide_unit_pair(blockIdx.x, gridDim.x / 4, nv / nk, slot, pair);
@@ -1591,6 +1632,8 @@ __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
         for (int i = 0; i < 4; ++i)
           ST[(static_cast<int64_t>(unit) * D + 16 * tt + 4 * lg + i) * D + col] = S[tt][i];
     }
+    if constexpr (EPI)
+      if (nchunks > 0) __syncthreads();   // B(n + 1): the conv waves normalize the last chunks
     return;
   }
 
@@ -1654,17 +1697,128 @@ __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) base[(8 * (lane & 1) + e) * 4] = pad ? 0.0f : sb * y[e];
       };
-      // the same staging order as the output waves' (chunk c + 1 between B(c) and B(c + 1))
+      // epilogue: this wave normalizes token tile w - 4 of a chunk; lane l
+      // takes row 16 (w - 4) + l / 4 and the pair's columns 8 (l % 4) .. +7,
+      // and polls pair l % 4's partial sum of that row
+      const int etok = 16 * (w - 4) + (lane >> 2), eq = lane & 3;
+      const int ecol = 32 * pair + 8 * eq;   // first column in the head
+      float ew[8];
+      if constexpr (EPI) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ew[e] = ep.w[ecol + e];
+      }
+      // the partial-sum word and z of chunk cn are fetched at the start of
+      // period cn + 2, right after its barrier, into register set cn & 1, and
+      // used at the end of period cn + 3: the conv loads issued after them in
+      // period cn + 2 are waited for at the start of period cn + 3, so by then
+      // they have had a whole period and nothing waits on them inside one.
+      // Every period issues the same loads (the chunk index clamped into the
+      // sequence), so the compiler's waits stay the same from period to
+      // period; the loop runs two periods per pass so that each set index is
+      // a constant (a run-time select would wait for both sets).
+      unsigned long long word[2] = {0ull, 0ull};
+      uint4 zr[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+      auto ring_word = [&](int cn) {
+        return ep.ring + ((static_cast<size_t>(unit) * EPI_RING + cn % EPI_RING) * 4 + eq) * CH + etok;
+      };
+      auto epi_fetch = [&](int cn, auto set) {
+        constexpr int SET = decltype(set)::value;
+        const int cc = max(0, min(cn, nchunks - 1));
+        const unsigned long long wv = __hip_atomic_load(ring_word(cc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t t0 = s_begin + static_cast<int64_t>(cc) * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+        const rsrc_t rz = make_rsrc(ep.z + (t0 * nv + h) * static_cast<int64_t>(D),
+                                    static_cast<uint32_t>(((L - 1) * nv * D + D) * 2));
+        word[SET] = wv;
+        zr[SET] = bload16(rz, static_cast<uint32_t>((etok * nv * D + ecol) * 2));
+      };
+      auto normalize = [&](int cn, auto set) {
+        constexpr int SET = decltype(set)::value;
+        const float4 o0 = *reinterpret_cast<const float4*>(&ORX[cn % (EPI_LAG + 1)][etok][8 * eq]);
+        const float4 o1 = *reinterpret_cast<const float4*>(&ORX[cn % (EPI_LAG + 1)][etok][8 * eq + 4]);
+        const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        unsigned long long* wp = ring_word(cn);
+        const uint32_t want = static_cast<uint32_t>(cn) + 1u;
+        unsigned long long wd = word[SET];
+        const uint4 zc = zr[SET];
+        bool ok = static_cast<uint32_t>(wd >> 32) == want;
+        for (int it = 0; it < EPI_SPIN && !__all(ok); ++it) {
+          __builtin_amdgcn_s_sleep(1);
+          if (!ok) {
+            wd = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = static_cast<uint32_t>(wd >> 32) == want;
+          }
+        }
+        // rows' sums in a fixed order, the same in all four lanes of a row
+        float ss = ok ? __uint_as_float(static_cast<uint32_t>(wd)) : __builtin_nanf("");
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + ep.eps);
+        const int64_t t0 = s_begin + static_cast<int64_t>(cn) * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
+        const uint32_t zw[4] = {zc.x, zc.y, zc.z, zc.w};
+        float yv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float zv = __uint_as_float((e & 1) ? (zw[e >> 1] & 0xffff0000u) : (zw[e >> 1] << 16));
+          yv[e] = ov[e] * inv * (1.0f + ew[e]) * siluf_(zv);
+        }
+        const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
+                                    static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
+        const uint32_t oo = static_cast<uint32_t>((etok * nv * D + ecol) * sizeof(TO));
+        if constexpr (sizeof(TO) == 4) {
+          bstore16_nt(ro, oo, make_uint4(__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]),
+                                         __float_as_uint(yv[3])));
+          bstore16_nt(ro, oo + 16, make_uint4(__float_as_uint(yv[4]), __float_as_uint(yv[5]),
+                                              __float_as_uint(yv[6]), __float_as_uint(yv[7])));
+        } else {
+          bstore16_nt(ro, oo, pack8_bf16(yv));
+        }
+      };
+      // the same staging order as the output waves' (chunk c + 1 between B(c)
+      // and B(c + 1)); with the epilogue, chunk c - 1 - EPI_LAG is normalized
+      // in step c and the last ones after one more barrier
       load_conv(0);
       stage_conv(0);
       load_conv(last(1));
       __syncthreads();                     // B(0)
       stage_conv(1);
       load_conv(last(2));
-      for (int c = 1; c <= nchunks; ++c) {
+      using S0_ = std::integral_constant<int, 0>;
+      using S1_ = std::integral_constant<int, 1>;
+      // period c; F = (c - EPI_LAG) & 1 = c & 1, the set fetched into
+      auto period = [&](int c, auto f) {
+        constexpr int F = decltype(f)::value;
         __syncthreads();                   // B(c)
+        if constexpr (EPI) {
+          epi_fetch(c - EPI_LAG, std::integral_constant<int, F>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
         stage_conv(c + 1);
         load_conv(last(c + 2));
+        if constexpr (EPI)
+          if (c - 1 - EPI_LAG >= 0) normalize(c - 1 - EPI_LAG, std::integral_constant<int, 1 - F>{});
+      };
+      for (int c = 1; c <= nchunks; c += 2) {
+        period(c, S1_{});
+        if (c + 1 <= nchunks) period(c + 1, S0_{});
+      }
+      if constexpr (EPI) {
+        __syncthreads();                   // B(n + 1)
+        // chunk n - 2 was fetched in period n (when n >= 2); fetch the rest
+        for (int cn = max(0, nchunks - EPI_LAG); cn < nchunks; ++cn) {
+          if (cn == nchunks - EPI_LAG) continue;
+          if (cn & 1)
+            epi_fetch(cn, S1_{});
+          else
+            epi_fetch(cn, S0_{});
+        }
+        for (int cn = max(0, nchunks - EPI_LAG); cn < nchunks; ++cn) {
+          if (cn & 1)
+            normalize(cn, S1_{});
+          else
+            normalize(cn, S0_{});
+        }
       }
       return;
     }
@@ -1754,12 +1908,15 @@ __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
     for (int u = 0; u < 2; ++u) a[u] = SCS[buf][16 * mt[u] + lr];
   };
   // O^T = a Y^T + U^T P^T of chunk c for both slices, stored non-temporally
+  // (with the epilogue: kept in the LDS ring, and the rows' partial sums of
+  // squares over the pair's 32 columns published)
   auto out_o = [&](int c, const f32x4 (&Y)[2][2], const float (&a)[2]) {
     const int buf = c & 1;
     const int64_t t0 = s_begin + static_cast<int64_t>(c) * CH;
     const int L = static_cast<int>(min<int64_t>(CH, s_end - t0));
     const rsrc_t ro = make_rsrc(o + (t0 * nv + h) * static_cast<int64_t>(D),
                                 static_cast<uint32_t>(((L - 1) * nv * D + D) * sizeof(TO)));
+    float ssp[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       // U^T as A operand (token k-steps 0, 1), slots reversed to match the turned P blocks
@@ -1790,15 +1947,38 @@ __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
       const int ocol = (2 * pair + j) * 16 + 4 * lg;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const uint32_t oo = static_cast<uint32_t>(((16 * mt[u] + lr) * nv * D + ocol) * sizeof(TO));
-        if constexpr (sizeof(TO) == 4) {
-          bstore16_nt(ro, oo, make_uint4(__float_as_uint(O[u][0]), __float_as_uint(O[u][1]),
-                                         __float_as_uint(O[u][2]), __float_as_uint(O[u][3])));
+        if constexpr (EPI) {
+          *reinterpret_cast<float4*>(&ORX[c % (EPI_LAG + 1)][16 * mt[u] + lr][16 * j + 4 * lg]) =
+              make_float4(O[u][0], O[u][1], O[u][2], O[u][3]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ssp[u] = fmaf(O[u][i], O[u][i], ssp[u]);
         } else {
-          bstore8_nt(ro, oo,
-                     make_uint2(f32_to_bf16(O[u][0]) | (static_cast<uint32_t>(f32_to_bf16(O[u][1])) << 16),
-                                f32_to_bf16(O[u][2]) | (static_cast<uint32_t>(f32_to_bf16(O[u][3])) << 16)));
+          const uint32_t oo = static_cast<uint32_t>(((16 * mt[u] + lr) * nv * D + ocol) * sizeof(TO));
+          if constexpr (sizeof(TO) == 4) {
+            bstore16_nt(ro, oo, make_uint4(__float_as_uint(O[u][0]), __float_as_uint(O[u][1]),
+                                           __float_as_uint(O[u][2]), __float_as_uint(O[u][3])));
+          } else {
+            bstore8_nt(ro, oo,
+                       make_uint2(f32_to_bf16(O[u][0]) | (static_cast<uint32_t>(f32_to_bf16(O[u][1])) << 16),
+                                  f32_to_bf16(O[u][2]) | (static_cast<uint32_t>(f32_to_bf16(O[u][3])) << 16)));
+          }
         }
+      }
+    }
+    if constexpr (EPI) {
+      // a row's 8 values per lane, then its 4 lanes (lanes lr + 16 lg)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        ssp[u] += __shfl_xor(ssp[u], 16, 64);
+        ssp[u] += __shfl_xor(ssp[u], 32, 64);
+      }
+      if (lg == 0) {
+        const unsigned long long tag = static_cast<unsigned long long>(static_cast<uint32_t>(c) + 1u) << 32;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          __hip_atomic_store(ep.ring + ((static_cast<size_t>(unit) * EPI_RING + c % EPI_RING) * 4 + pair) * CH +
+                                 16 * mt[u] + lr,
+                             tag | __float_as_uint(ssp[u]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   };
@@ -1905,6 +2085,7 @@ __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
 #pragma unroll
       for (int u = 0; u < 2; ++u) a[u] = an[u];
     }
+    if constexpr (EPI) __syncthreads();   // B(n + 1)
   };
   if (w == 2)
     run(std::true_type{});
@@ -2240,7 +2421,8 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
                           const void* ga, const void* gb, int gm, const float* A_log, const float* dt_bias,
                           const int32_t* cu, int n_seqs, int64_t T, int nk,
                           int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16, void* ws,
-                          const ConvIn* cvp, hipStream_t s) {
+                          const ConvIn* cvp, const NormEpi* ne, bool* normalized, hipStream_t s) {
+  if (normalized) *normalized = false;
   constexpr bool BF = sizeof(TIn) == 2;
   ConvIn cv = cvp ? *cvp : ConvIn{nullptr, nullptr, nullptr, 0, 0, 0};
   const WsLayout lay = ws_layout(T, n_seqs, nk, nv, BF);
@@ -2324,17 +2506,55 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     }
     if (use_wide_state(static_cast<int64_t>(grid))) {
       const unsigned wgrid = grid / 2;   // two slices per workgroup
+      if (ne && cvp && !o_bf16) {
+        // the norm epilogue inside the kernel when all its workgroups can be
+        // resident at once (cooperative launch); else the caller normalizes
+        auto kern = chunk_state_wide_kernel<float, true, true>;
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 512, 0) ==
+                hipSuccess &&
+            static_cast<int64_t>(per_cu) * device_cus() >= static_cast<int64_t>(wgrid)) {
+          unsigned long long* ring = reinterpret_cast<unsigned long long*>(base + lay.off_ring);
+          const int64_t nw = static_cast<int64_t>(n_seqs) * nv * static_cast<int64_t>(kRingBytesPerUnit / 8);
+          clear_u64_kernel<<<static_cast<unsigned>((nw + 255) / 256), 256, 0, s>>>(ring, nw);
+          e = hipGetLastError();
+          if (e != hipSuccess) return e;
+          const uint16_t* a_v = vb;
+          int64_t a_vs = vs;
+          const int32_t* a_cu = cu;
+          int a_n = n_seqs;
+          int64_t a_T = T;
+          int a_nk = nk, a_nv = nv;
+          const int32_t* a_off = chunk_off;
+          const uint16_t* a_xf = xf;
+          const float* a_scp = scp;
+          const float* a_egc = egc;
+          const uint16_t* a_kf = kf;
+          const uint16_t* a_qf = qf;
+          const int32_t* a_order = order;
+          const float* a_S0 = S0;
+          float* a_ST = ST;
+          float* a_o = static_cast<float*>(o);
+          ConvIn a_cv = cv;
+          EpiIn a_ep{ne->z, ne->w, ne->eps, ring};
+          void* args[] = {&a_v,   &a_vs,  &a_cu,    &a_n,  &a_T,  &a_nk, &a_nv, &a_off, &a_xf, &a_scp,
+                          &a_egc, &a_kf,  &a_qf,    &a_order, &a_S0, &a_ST, &a_o, &a_cv, &a_ep};
+          e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(wgrid), dim3(512), args, 0, s);
+          if (e == hipSuccess && normalized) *normalized = true;
+          return e;
+        }
+      }
       auto launch_wide = [&](auto kern, auto* optr) {   // eight waves with the conv (conv waves), else four
         kern<<<wgrid, cvp ? 512 : 256, 0, s>>>(vb, vs, cu, n_seqs, T, nk, nv, chunk_off, xf, scp, egc, kf, qf, order,
-                                              S0, ST, optr, cv);
+                                              S0, ST, optr, cv, EpiIn{});
         return hipGetLastError();
       };
       if (cvp) {
-        if (o_bf16) return launch_wide(chunk_state_wide_kernel<uint16_t, true>, static_cast<uint16_t*>(o));
-        return launch_wide(chunk_state_wide_kernel<float, true>, static_cast<float*>(o));
+        if (o_bf16) return launch_wide(chunk_state_wide_kernel<uint16_t, true, false>, static_cast<uint16_t*>(o));
+        return launch_wide(chunk_state_wide_kernel<float, true, false>, static_cast<float*>(o));
       }
-      if (o_bf16) return launch_wide(chunk_state_wide_kernel<uint16_t, false>, static_cast<uint16_t*>(o));
-      return launch_wide(chunk_state_wide_kernel<float, false>, static_cast<float*>(o));
+      if (o_bf16) return launch_wide(chunk_state_wide_kernel<uint16_t, false, false>, static_cast<uint16_t*>(o));
+      return launch_wide(chunk_state_wide_kernel<float, false, false>, static_cast<float*>(o));
     }
     // Several sequences (cu_seqlens): two workgroups per CU, so that a CU can
     // take another (sequence, head, slice) while one runs a long sequence;
@@ -2415,9 +2635,9 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, int bf1
                             hipStream_t s) {
   if (bf16)
     return chunk_dispatch<uint16_t>(q, k, v, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2,
-                                    S0, ST, o, o_bf16, ws, nullptr, s);
+                                    S0, ST, o, o_bf16, ws, nullptr, nullptr, nullptr, s);
   return chunk_dispatch<float>(q, k, v, qs, ks, vs, ga, gb, gm, A_log, dt_bias, cu, n_seqs, T, nk, nv, scale, l2, S0,
-                               ST, o, o_bf16, ws, nullptr, s);
+                               ST, o, o_bf16, ws, nullptr, nullptr, nullptr, s);
 }
 
 hipError_t launch_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int bf16, int64_t qs, int64_t ks,
@@ -2437,12 +2657,17 @@ hipError_t launch_chunk_fwd_conv(const void* x, int64_t xs, const float* conv_w,
                                  const void* conv_st, int state_len, const void* a, const void* b, int gm,
                                  const float* A_log, const float* dt_bias, const int32_t* cu, int n_seqs, int64_t T,
                                  int nk, int nv, float scale, int l2, const float* S0, float* ST, void* o, int o_bf16,
-                                 void* ws, hipStream_t s) {
+                                 void* ws, const NormEpi* ne, hipStream_t s) {
   const int conv_dim = (2 * nk + nv) * D;
   const ConvIn cv{conv_w, conv_b, static_cast<const uint16_t*>(conv_st), state_len, conv_dim, 0};
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  return chunk_dispatch<uint16_t>(xb, xb + nk * D, xb + 2 * nk * D, xs, xs, xs, a, b, gm, A_log, dt_bias, cu, n_seqs,
-                                  T, nk, nv, scale, l2, S0, ST, o, o_bf16, ws, &cv, s);
+  bool normalized = false;
+  hipError_t e = chunk_dispatch<uint16_t>(xb, xb + nk * D, xb + 2 * nk * D, xs, xs, xs, a, b, gm, A_log, dt_bias, cu,
+                                          n_seqs, T, nk, nv, scale, l2, S0, ST, o, o_bf16, ws, &cv, ne, &normalized, s);
+  // the epilogue did not run inside the state kernel: o (fp32) is normalized in place
+  if (e == hipSuccess && ne && !normalized && T > 0)
+    e = launch_gated_rmsnorm(o, 0, ne->z, 1, ne->w, T * nv, D, ne->eps, o, 0, s);
+  return e;
 }
 
 }  // namespace gdn

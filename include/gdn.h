@@ -220,6 +220,36 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_prefill_fused followed by the layer's gated RMSNorm of its output, in
+ * one call ("Qwen3.5 Dense Model Architecture", Linear Attention, minimal
+ * example: the core output goes straight into the gated norm with z;
+ * "Qwen3.5 Simulation Support Design Document" 2.2, the decomposed op flow):
+ *   y[t,h,:] = o[t,h,:] (mean(o[t,h,:]^2) + eps)^-1/2 (1 + norm_weight) z[t,h,:] sigmoid(z[t,h,:])
+ * where o is what gdn_prefill_fused would write (fp32).
+ *   z          : [T_tot, nv, dv] bf16, dense, 16-byte aligned
+ *   norm_weight: [dv] fp32;  eps >= 0
+ *   y          : [T_tot, nv, dv] fp32 output (o is not written anywhere)
+ * Every other argument is as for gdn_prefill_fused (same workspace size).
+ * When the launch runs the wide form of the state kernel and all of its
+ * workgroups fit the device at once, the norm runs inside the state kernel: o
+ * never leaves the CU, and the four workgroups that hold a row's 128 columns
+ * exchange their partial sums of squares through a small ring in the
+ * workspace. Otherwise o is written to y and normalized there by a second
+ * launch. The two routes differ by the order of the sum of squares only.
+ */
+int gdn_prefill_fused_norm(const void* x, int dtype, int64_t x_tok_stride,
+                           const float* conv_weight, const float* conv_bias, int K,
+                           const void* conv_state_in, void* conv_state_out, int state_len,
+                           const void* a, const void* b, int ab_dtype,
+                           const float* A_log, const float* dt_bias,
+                           const int32_t* cu_seqlens, int n_seqs, int64_t T_tot,
+                           int nk, int nv, int dk, int dv, float scale, int qk_l2norm,
+                           const float* initial_state, float* final_state,
+                           const void* z, int z_dtype, const float* norm_weight, float eps,
+                           float* y,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Recurrent gated delta rule, the decode path ("Qwen3.5 Simulation Support
  * Design Document", 2.2 op 5 and 2.3: decode batches, including multi-token
  * MTP decode, take the token-by-token path; "Qwen3.5 Dense Model

@@ -129,9 +129,13 @@ def long_run():
     _say(wl.name, "gpu fused prefill")
     fo, fst, fcs = gdn.gdn_prefill_fused(x["x"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"], wl.nk, wl.nv,
                                          state_len=wl.state_len)
+    _say(wl.name, "gpu fused prefill with the norm")
+    ny, nst, _ = gdn.gdn_prefill_fused_norm(x["x"], x["conv_w"], x["a"], x["b"], x["A_log"], x["dt_bias"], wl.nk,
+                                            wl.nv, x["z"], x["norm_w"], eps=1e-6, state_len=wl.state_len,
+                                            output_conv_state=False)
     torch.cuda.synchronize()
     return dict(wl=wl, x=x, y=y, cs=cs, g=g, beta=beta, o=o, st=st, out=out, T=T, C=C, kd=kd, fo=fo, fst=fst,
-                fcs=fcs)
+                fcs=fcs, ny=ny, nst=nst)
 
 
 def test_long_prefill_fused_equals_pipeline(long_run):
@@ -144,6 +148,25 @@ def test_long_prefill_fused_equals_pipeline(long_run):
         diff = (a.double() - b.double()).abs().max().item()
         print(f"[exact] {what}: max |fused - separate| = {diff:.3e}", flush=True)
         assert torch.equal(a, b), what
+
+
+def test_long_prefill_fused_norm_equals_pipeline(long_run):
+    """The fused prefill with the norm inside the state kernel against the fused prefill followed by the
+    norm launch on the full long workload: final state bit for bit; y within 2e-5 of |y| per element (the
+    two routes sum a row's 128 squares in different orders, at most 2 * 127 u apart, which moves rms^-1 by
+    half of that), and not bit-equal everywhere, which shows the in-kernel route ran."""
+    r = long_run
+    _say(r["wl"].name, "fused prefill with the norm against the two launches")
+    assert torch.equal(r["nst"], r["fst"]), "final state"
+    ny, out = r["ny"], r["out"]
+    worst = 0.0
+    for t0 in range(0, r["T"], 16384):   # in slabs, to bound the temporaries
+        a, b = ny[t0:t0 + 16384].double(), out[t0:t0 + 16384].double()
+        err = (a - b).abs()
+        worst = max(worst, (err / b.abs().clamp_min(1e-30)).max().item())
+        assert (err <= 2e-5 * b.abs()).all(), f"y beyond 2e-5 of |ref| in tokens {t0}.."
+    print(f"[tol] y: max |fused - pipeline| / |pipeline| = {worst:.3e}", flush=True)
+    assert not torch.equal(ny, out), "the norm did not run inside the state kernel"
 
 
 def test_long_conv_windows(long_run):
