@@ -44,15 +44,40 @@ constexpr int RPT = D / RGN;      // rows per thread
 __device__ __forceinline__ float act_round(float v, float) { return v; }
 __device__ __forceinline__ float act_round(float v, uint16_t) { return bf16_to_f32(f32_to_bf16(v)); }
 
+// k and q of a token sit in LDS grouped by row group: row r at slot
+// (r % RGN) * RPT + r / RGN, so a thread's 16 rows (r = rg + RGN i) are the
+// 16 consecutive floats at rg * RPT (four 16-byte reads).
+__device__ __forceinline__ int kq_slot(int r) { return (r % RGN) * RPT + r / RGN; }
+
+// Within a sequence's tokens the state is carried as S = E St with a scalar E
+// per state (the product of the decays since the last fold, the same in every
+// thread), so a token's update is one fma per element, St += k (rk delta /
+// E')^T with E' = e E, instead of a decay multiply and an fma. A token at
+// which E' would fall below kStateScaleMin folds E' into St instead
+// (St' = E' St + k (rk delta)^T, E = 1). S = E St is formed where the state
+// leaves the thread (the final store, a snapshot), the same way after every
+// token, so the state after token t does not depend on whether more tokens
+// follow (a snapshot after token t equals the final state of the same step
+// run on the tokens up to t).
+constexpr float kStateScaleMin = 0x1p-64f;
+
+// a value that is the same in every lane (a butterfly wave sum, per-state
+// gating), moved to a scalar register
+__device__ __forceinline__ float uni(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 // One token of the recurrence for a state held by 256 threads (thread t256:
 // columns 4 (t256 % 32) .. +3, rows t256 / 32 + 8 i), in two halves around a
-// barrier of the whole workgroup. ks and qs are this token's k and q of the
-// key head (fp32 in LDS, written before a barrier that precedes the first
-// half); red is LDS scratch [4 waves][a | b][128 columns]. The first half
-// forms the norms and this thread's partial sums of S^T k and S^T q and
-// writes them to red; the second half (after the barrier) adds them up,
-// stores o (row element offset ob, the thread's first column; rows of group
-// rg == 0 store) and updates S. ks must still hold the token's k then.
+// barrier of the whole workgroup. ks and qs are this token's raw k and q of
+// the key head (fp32 in LDS in kq_slot order, written before a barrier that
+// precedes the first half); red is LDS scratch [4 waves][a | b][128 columns].
+// The first half forms the norms and this thread's partial sums of St^T k and
+// St^T q (raw k and q: the norms, the scale and E multiply the sums after the
+// reduction) and writes them to red; the second half (after the barrier)
+// adds them up, stores o (row element offset ob, the thread's first column;
+// rows of group rg == 0 store) and updates St and E. ks must still hold the
+// token's k then.
 struct RecNorms { float rk, rq, kq; };
 __device__ __forceinline__ RecNorms rec_pass(const float (&S)[RPT][4], const float* ks, const float* qs, float* red,
                                              int t256, float scale, int l2) {
@@ -63,20 +88,24 @@ __device__ __forceinline__ RecNorms rec_pass(const float (&S)[RPT][4], const flo
   const float skk = wave_sum(k0 * k0 + k1 * k1);
   const float sqq = wave_sum(q0 * q0 + q1 * q1);
   const float sqk = wave_sum(q0 * k0 + q1 * k1);
-  const float rk = l2 ? 1.0f / sqrtf(skk + 1e-6f) : 1.0f;
-  const float rq = (l2 ? 1.0f / sqrtf(sqq + 1e-6f) : 1.0f) * scale;
-  const float kq = sqk * rk * rq;
+  const float rk = uni(l2 ? 1.0f / sqrtf(skk + 1e-6f) : 1.0f);
+  const float rq = uni((l2 ? 1.0f / sqrtf(sqq + 1e-6f) : 1.0f) * scale);
+  const float kq = uni(sqk * rk * rq);
 
   float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+  const float4* k4 = reinterpret_cast<const float4*>(ks + rg * RPT);
+  const float4* q4 = reinterpret_cast<const float4*>(qs + rg * RPT);
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const float kh = ks[rg + RGN * i] * rk;
-    const float qh = qs[rg + RGN * i] * rq;
+  for (int i4 = 0; i4 < RPT / 4; ++i4) {
+    const float4 kk = k4[i4], qq = q4[i4];
+    const float kr[4] = {kk.x, kk.y, kk.z, kk.w}, qr[4] = {qq.x, qq.y, qq.z, qq.w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      pa[c] = fmaf(S[i][c], kh, pa[c]);
-      pb[c] = fmaf(S[i][c], qh, pb[c]);
-    }
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pa[c] = fmaf(S[4 * i4 + u][c], kr[u], pa[c]);
+        pb[c] = fmaf(S[4 * i4 + u][c], qr[u], pb[c]);
+      }
   }
   // the two row groups of a wave sit in lanes l and l ^ 32
 #pragma unroll
@@ -94,12 +123,11 @@ __device__ __forceinline__ RecNorms rec_pass(const float (&S)[RPT][4], const flo
   return {rk, rq, kq};
 }
 template <typename TO>
-__device__ __forceinline__ void rec_finish(float (&S)[RPT][4], const float* ks, const float (&vv)[4], float gt,
-                                           float bt, const float* red, int t256, RecNorms nr, TO* __restrict__ o,
-                                           int64_t ob) {
+__device__ __forceinline__ void rec_finish(float (&S)[RPT][4], float& E, const float* ks, const float (&vv)[4],
+                                           float gt, float bt, const float* red, int t256, RecNorms nr,
+                                           TO* __restrict__ o, int64_t ob) {
   const int cg = t256 % CGN, rg = t256 / CGN;
-  const float rk = nr.rk, kq = nr.kq;
-  const float e = expf(gt);
+  const float e = uni(expf(gt));
   float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -108,29 +136,49 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], const float* ks, 
     a4[0] += ra.x; a4[1] += ra.y; a4[2] += ra.z; a4[3] += ra.w;
     b4[0] += rb.x; b4[1] += rb.y; b4[2] += rb.z; b4[3] += rb.w;
   }
+  // a = S^T k_hat = E rk St^T k, b = S^T q_hat = E rq St^T q
+  const float sa = E * nr.rk, sb = E * nr.rq;
   float dl[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) dl[c] = bt * (vv[c] - e * a4[c]);
+  for (int c = 0; c < 4; ++c) dl[c] = bt * (vv[c] - e * (a4[c] * sa));
   if (rg == 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) Elem<TO>::store(o, ob + c, fmaf(e, b4[c], kq * dl[c]));
+    for (int c = 0; c < 4; ++c) Elem<TO>::store(o, ob + c, fmaf(e, b4[c] * sb, nr.kq * dl[c]));
   }
-  // (k re-read from LDS rather than held across the barrier: fewer VGPRs,
-  // one more workgroup per CU)
+  // S' = e S + k_hat delta^T: St' = St + k (rk delta / E')^T with E' = e E,
+  // or, below the floor, St' = E' St + k (rk delta)^T and E = 1 (k re-read
+  // from LDS rather than held across the barrier: fewer VGPRs)
+  const float En = uni(e * E);
+  const bool keep = En >= kStateScaleMin;
+  const float f = uni(keep ? nr.rk / En : nr.rk);
+  float d2[4];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const float kh = ks[rg + RGN * i] * rk;
+  for (int c = 0; c < 4; ++c) d2[c] = dl[c] * f;
+  if (!keep) {   // fold E' into St (a uniform branch)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[i][c] = fmaf(e, S[i][c], kh * dl[c]);
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S[i][c] *= En;
   }
+  const float4* k4 = reinterpret_cast<const float4*>(ks + rg * RPT);
+#pragma unroll
+  for (int i4 = 0; i4 < RPT / 4; ++i4) {
+    const float4 kk = k4[i4];
+    const float kr[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S[4 * i4 + u][c] = fmaf(kr[u], d2[c], S[4 * i4 + u][c]);
+  }
+  E = uni(keep ? En : 1.0f);
 }
 template <typename TO>
-__device__ __forceinline__ void rec_token(float (&S)[RPT][4], const float* ks, const float* qs, const float (&vv)[4],
-                                          float gt, float bt, float* red, int t256, float scale, int l2,
-                                          TO* __restrict__ o, int64_t ob) {
+__device__ __forceinline__ void rec_token(float (&S)[RPT][4], float& E, const float* ks, const float* qs,
+                                          const float (&vv)[4], float gt, float bt, float* red, int t256, float scale,
+                                          int l2, TO* __restrict__ o, int64_t ob) {
   const RecNorms nr = rec_pass(S, ks, qs, red, t256, scale, l2);
   __syncthreads();
-  rec_finish<TO>(S, ks, vv, gt, bt, red, t256, nr, o, ob);
+  rec_finish<TO>(S, E, ks, vv, gt, bt, red, t256, nr, o, ob);
 }
 
 // G consecutive (sequence, value head) states per workgroup, 256 threads
@@ -142,7 +190,7 @@ recurrent_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
                  int64_t ks, int64_t vs, const float* __restrict__ g, const float* __restrict__ beta,
                  const int32_t* __restrict__ cu, int64_t T, int nk, int nv, float scale, int l2,
                  float* __restrict__ state, TO* __restrict__ o) {
-  __shared__ float kq_s[2][G][2][D];    // [parity][state][k|q][D]
+  __shared__ __attribute__((aligned(16))) float kq_s[2][G][2][D];    // [parity][state][k|q][kq_slot]
   __shared__ float red[2][G][4][2][D];  // [parity][state][wave][a|b][column]
 
   const int tid = threadIdx.x, t256 = tid & 255;
@@ -190,19 +238,24 @@ recurrent_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     }
   }
 
+  float E = 1.0f;   // S = E St (see kStateScaleMin)
   int par = 0;
   for (int64_t t = t0; t < t1; ++t, par ^= 1) {
-    const float kqv = Elem<TIn>::cvt(kq_n), gt = gt_n, bt = bt_n;
+    const float kqv = Elem<TIn>::cvt(kq_n), gt = uni(gt_n), bt = uni(bt_n);
     float vv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) vv[c] = Elem<TIn>::cvt(vv_n[c]);
     if (t + 1 < t1) load_token(t + 1);   // the next token's inputs
     // stage k and q of this token's key head in LDS (fp32)
-    kq_s[par][rho][t256 < D ? 0 : 1][t256 & (D - 1)] = kqv;
+    kq_s[par][rho][t256 < D ? 0 : 1][kq_slot(t256 & (D - 1))] = kqv;
     __syncthreads();
-    rec_token<TO>(S, kq_s[par][rho][0], kq_s[par][rho][1], vv, gt, bt, &red[par][rho][0][0][0], t256, scale, l2, o,
-                  t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
+    rec_token<TO>(S, E, kq_s[par][rho][0], kq_s[par][rho][1], vv, gt, bt, &red[par][rho][0][0][0], t256, scale, l2,
+                  o, t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
   }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)   // S = E St
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[i][c] *= E;
   {
     const int rg = t256 / CGN;
 #pragma unroll
@@ -231,7 +284,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
   constexpr int NT = 256 * R;
   constexpr int CPT = (NCH + NT - 1) / NT;
   constexpr int KW = 4;
-  __shared__ float kqv_s[3][NCH];       // [token % 3][q | k | v]: conv outputs
+  __shared__ __attribute__((aligned(16))) float kqv_s[3][NCH];   // [token % 3][q | k (kq_slot) | v]: conv outputs
   __shared__ float red[2][R][4][2][D];  // [parity][value head][wave][a|b][column]
 
   const int n = blockIdx.x / nk, hk = blockIdx.x % nk;
@@ -297,7 +350,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
 #pragma unroll
         for (int i = 0; i < KW - 1; ++i) acc = fmaf(cw[c * KW + i], hist[u][i], acc);
         acc = fmaf(cw[c * KW + KW - 1], xv, acc);
-        kqv_s[buf][j] = act_round(siluf_(acc), T{});
+        kqv_s[buf][j < 2 * D ? (j & ~(D - 1)) + kq_slot(j & (D - 1)) : j] = act_round(siluf_(acc), T{});
 #pragma unroll
         for (int i = 0; i + 1 < KW - 1; ++i) hist[u][i] = hist[u][i + 1];
         hist[u][KW - 2] = xv;
@@ -310,13 +363,14 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
   // is one phase behind may still read it.
   if (t0 < t1) conv_token(t0, 0);
   __syncthreads();
+  float E = 1.0f;   // S = E St (see kStateScaleMin)
   int buf = 0, par = 0;
   for (int64_t t = t0; t < t1; ++t) {
     // gating, as the separate gating kernel computes it
     const float av = Elem<T>::cvt(a_n), bv = Elem<T>::cvt(b_n);
     if (t + 1 < t1) { a_n = a[(t + 1) * nv + h]; b_n = b[(t + 1) * nv + h]; }
-    const float gt = -exp_(alog) * softplusf_(av + dtb);
-    const float bt = sigmoidf_(bv);
+    const float gt = uni(-exp_(alog) * softplusf_(av + dtb));
+    const float bt = uni(sigmoidf_(bv));
     float* rd = &red[par][rho][0][0][0];
     const RecNorms nr = rec_pass(S, &kqv_s[buf][D], &kqv_s[buf][0], rd, t256, scale, l2);
     const int nbuf = buf == 2 ? 0 : buf + 1;
@@ -324,7 +378,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
     __syncthreads();
     const float4 v4 = *reinterpret_cast<const float4*>(&kqv_s[buf][2 * D + rho * D + col]);
     const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-    rec_finish<TO>(S, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
+    rec_finish<TO>(S, E, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
                    t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
     if constexpr (SNAP) {   // the state after this token, for rolling back rejected draft tokens
       // (buffer stores off one per-lane offset: the row addresses are not kept live)
@@ -333,12 +387,16 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
         bstore16_nt(rs, vo + static_cast<uint32_t>(RGN * D * 4 * i),
-                    make_uint4(__float_as_uint(S[i][0]), __float_as_uint(S[i][1]), __float_as_uint(S[i][2]),
-                               __float_as_uint(S[i][3])));
+                    make_uint4(__float_as_uint(S[i][0] * E), __float_as_uint(S[i][1] * E),
+                               __float_as_uint(S[i][2] * E), __float_as_uint(S[i][3] * E)));
     }
     buf = nbuf;
     par ^= 1;
   }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)   // S = E St
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[i][c] *= E;
   {
     const int rg = t256 / CGN;
 #pragma unroll

@@ -195,6 +195,31 @@ def test_recurrent_multi_token_varlen(dtype):
     assert_close(state, S_ref, TOL[dtype], "recurrent varlen state")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_recurrent_strong_decay_rescale(dtype):
+    """The decode kernels carry the state as E times a rescaled state, E the product of the decays since the
+    last rescale, and fold E in once it would fall below 2^-64. Decays of e^-30 per token cross that floor
+    on the third token of a sequence, e^-120 underflows to zero in fp32 (the state is then replaced by the
+    update alone), and mixed runs alternate; each against the oracle, with g and beta given directly."""
+    _say("recurrent strong decay", dtype)
+    lengths = [6, 5, 4, 1]
+    x = _inputs(dtype, lengths, 1, 2, s0_std=0.5)
+    T = sum(lengths)
+    gvals = np.concatenate([np.full(6, -30.0), np.full(5, -120.0), np.array([-0.1, -45.0, -0.2, -60.0]),
+                            np.array([-200.0])])
+    g = np.stack([gvals, gvals * 0.5], 1).astype(np.float32)              # [T, nv]
+    beta = np.full((T, 2), 0.7, dtype=np.float32)
+    d = _to(x, dev())
+    state = d["S0"].clone()
+    o = gdn.gdn_recurrent_fwd(d["q"], d["k"], d["v"], torch.from_numpy(g).to(dev()),
+                              torch.from_numpy(beta).to(dev()), state, cu_seqlens=d["cu_seqlens"])
+    o_ref, S_ref = oracle.delta_rule(f64(x["q"]), f64(x["k"]), f64(x["v"]), g.astype(np.float64),
+                                     beta.astype(np.float64), cu_seqlens=x["cu_seqlens"].numpy(),
+                                     initial_state=f64(x["S0"]))
+    assert_close(o, o_ref, TOL[dtype], "recurrent strong decay o")
+    assert_close(state, S_ref, TOL[dtype], "recurrent strong decay state")
+
+
 # ------------------------------------------------------------------ chunk with the gating folded in
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
