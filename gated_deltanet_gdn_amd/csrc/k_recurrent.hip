@@ -49,7 +49,8 @@ __device__ __forceinline__ float act_round(float v, uint16_t) { return bf16_to_f
 // 16 consecutive floats at rg * RPT (four 16-byte reads).
 __device__ __forceinline__ int kq_slot(int r) { return (r % RGN) * RPT + r / RGN; }
 
-// Within a sequence's tokens the state is carried as S = E St with a scalar E
+// In a launch with several tokens per sequence (cu_seqlens given), within a
+// sequence's tokens the state is carried as S = E St with a scalar E
 // per state (the product of the decays since the last fold, the same in every
 // thread), so a token's update is one fma per element, St += k (rk delta /
 // E')^T with E' = e E, instead of a decay multiply and an fma. A token at
@@ -58,7 +59,9 @@ __device__ __forceinline__ int kq_slot(int r) { return (r % RGN) * RPT + r / RGN
 // leaves the thread (the final store, a snapshot), the same way after every
 // token, so the state after token t does not depend on whether more tokens
 // follow (a snapshot after token t equals the final state of the same step
-// run on the tokens up to t).
+// run on the tokens up to t). A launch of one token per sequence (no
+// cu_seqlens) updates S directly, S' = e S + k (rk delta)^T, and skips the
+// final multiply (DEFER = false).
 constexpr float kStateScaleMin = 0x1p-64f;
 
 // a value that is the same in every lane (a butterfly wave sum, per-state
@@ -122,7 +125,7 @@ __device__ __forceinline__ RecNorms rec_pass(const float (&S)[RPT][4], const flo
   }
   return {rk, rq, kq};
 }
-template <typename TO>
+template <typename TO, bool DEFER>
 __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], float& E, const float* ks, const float (&vv)[4],
                                            float gt, float bt, const float* red, int t256, RecNorms nr,
                                            TO* __restrict__ o, int64_t ob) {
@@ -148,6 +151,22 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], float& E, const f
   // S' = e S + k_hat delta^T: St' = St + k (rk delta / E')^T with E' = e E,
   // or, below the floor, St' = E' St + k (rk delta)^T and E = 1 (k re-read
   // from LDS rather than held across the barrier: fewer VGPRs)
+  const float4* k4 = reinterpret_cast<const float4*>(ks + rg * RPT);
+  if constexpr (!DEFER) {
+    float d2[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) d2[c] = dl[c] * nr.rk;
+#pragma unroll
+    for (int i4 = 0; i4 < RPT / 4; ++i4) {
+      const float4 kk = k4[i4];
+      const float kr[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) S[4 * i4 + u][c] = fmaf(e, S[4 * i4 + u][c], kr[u] * d2[c]);
+    }
+    return;
+  }
   const float En = uni(e * E);
   const bool keep = En >= kStateScaleMin;
   const float f = uni(keep ? nr.rk / En : nr.rk);
@@ -160,7 +179,6 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], float& E, const f
 #pragma unroll
       for (int c = 0; c < 4; ++c) S[i][c] *= En;
   }
-  const float4* k4 = reinterpret_cast<const float4*>(ks + rg * RPT);
 #pragma unroll
   for (int i4 = 0; i4 < RPT / 4; ++i4) {
     const float4 kk = k4[i4];
@@ -172,19 +190,19 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], float& E, const f
   }
   E = uni(keep ? En : 1.0f);
 }
-template <typename TO>
+template <typename TO, bool DEFER>
 __device__ __forceinline__ void rec_token(float (&S)[RPT][4], float& E, const float* ks, const float* qs,
                                           const float (&vv)[4], float gt, float bt, float* red, int t256, float scale,
                                           int l2, TO* __restrict__ o, int64_t ob) {
   const RecNorms nr = rec_pass(S, ks, qs, red, t256, scale, l2);
   __syncthreads();
-  rec_finish<TO>(S, E, ks, vv, gt, bt, red, t256, nr, o, ob);
+  rec_finish<TO, DEFER>(S, E, ks, vv, gt, bt, red, t256, nr, o, ob);
 }
 
 // G consecutive (sequence, value head) states per workgroup, 256 threads
 // each; G divides nv, so all G belong to one sequence and run the same
 // token loop (its barriers are the whole workgroup's).
-template <typename TIn, typename TO, int G>
+template <typename TIn, typename TO, int G, bool DEFER>
 __global__ void __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(4)))
 recurrent_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, int64_t qs,
                  int64_t ks, int64_t vs, const float* __restrict__ g, const float* __restrict__ beta,
@@ -249,13 +267,15 @@ recurrent_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     // stage k and q of this token's key head in LDS (fp32)
     kq_s[par][rho][t256 < D ? 0 : 1][kq_slot(t256 & (D - 1))] = kqv;
     __syncthreads();
-    rec_token<TO>(S, E, kq_s[par][rho][0], kq_s[par][rho][1], vv, gt, bt, &red[par][rho][0][0][0], t256, scale, l2,
+    rec_token<TO, DEFER>(S, E, kq_s[par][rho][0], kq_s[par][rho][1], vv, gt, bt, &red[par][rho][0][0][0], t256, scale, l2,
                   o, t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
   }
+  if constexpr (DEFER) {
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)   // S = E St
+    for (int i = 0; i < RPT; ++i)   // S = E St
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[i][c] *= E;
+      for (int c = 0; c < 4; ++c) S[i][c] *= E;
+  }
   {
     const int rg = t256 / CGN;
 #pragma unroll
@@ -272,7 +292,7 @@ recurrent_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
 // heads R hk .. R hk + R - 1; one or two channels per thread. The gating
 // inputs are wave-uniform (one value head per wave), so every thread computes
 // g and beta itself from scalar loads.
-template <typename T, typename TO, int R, bool SNAP>
+template <typename T, typename TO, int R, bool SNAP, bool DEFER>
 __global__ void __launch_bounds__(256 * R) __attribute__((amdgpu_waves_per_eu(R == 1 ? 3 : 4)))
 decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, int state_len,
                     const float* __restrict__ cw, const float* __restrict__ cb, const T* __restrict__ a,
@@ -378,7 +398,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
     __syncthreads();
     const float4 v4 = *reinterpret_cast<const float4*>(&kqv_s[buf][2 * D + rho * D + col]);
     const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-    rec_finish<TO>(S, E, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
+    rec_finish<TO, DEFER>(S, E, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
                    t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
     if constexpr (SNAP) {   // the state after this token, for rolling back rejected draft tokens
       // (buffer stores off one per-lane offset: the row addresses are not kept live)
@@ -393,10 +413,12 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
     buf = nbuf;
     par ^= 1;
   }
+  if constexpr (DEFER) {
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)   // S = E St
+    for (int i = 0; i < RPT; ++i)   // S = E St
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[i][c] *= E;
+      for (int c = 0; c < 4; ++c) S[i][c] *= E;
+  }
   {
     const int rg = t256 / CGN;
 #pragma unroll
@@ -431,9 +453,9 @@ hipError_t rec_launch(const void* q, const void* k, const void* v, int64_t qs, i
                       const float* g, const float* beta, const int32_t* cu, int n_seqs, int64_t T, int nk, int nv,
                       float scale, int l2, float* state, void* o, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(nv / G));
-  recurrent_kernel<TIn, TO, G><<<grid, 256 * G, 0, s>>>(
-      static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), qs, ks, vs, g, beta, cu, T,
-      nk, nv, scale, l2, state, static_cast<TO*>(o));
+  auto kern = cu ? recurrent_kernel<TIn, TO, G, true> : recurrent_kernel<TIn, TO, G, false>;
+  kern<<<grid, 256 * G, 0, s>>>(static_cast<const TIn*>(q), static_cast<const TIn*>(k), static_cast<const TIn*>(v), qs,
+                                ks, vs, g, beta, cu, T, nk, nv, scale, l2, state, static_cast<TO*>(o));
   return hipGetLastError();
 }
 
@@ -461,7 +483,8 @@ hipError_t fused_launch(const void* x, int64_t xs, void* cst, int state_len, con
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(nk));
   // snapshots are a separate instantiation: their stores inside the token
   // loop would otherwise cost the plain step about 30 spilled VGPRs
-  auto kern = snap ? decode_fused_kernel<T, TO, R, true> : decode_fused_kernel<T, TO, R, false>;
+  auto kern = snap ? (cu ? decode_fused_kernel<T, TO, R, true, true> : decode_fused_kernel<T, TO, R, true, false>)
+                   : (cu ? decode_fused_kernel<T, TO, R, false, true> : decode_fused_kernel<T, TO, R, false, false>);
   kern<<<grid, 256 * R, 0, s>>>(static_cast<const T*>(x), xs, static_cast<T*>(cst), state_len, cw, cb,
                                 static_cast<const T*>(a), static_cast<const T*>(b), A_log, dt_bias, cu, T_tot, nk, nv,
                                 scale, l2, state, slots, n_slots, snap, static_cast<TO*>(o));
