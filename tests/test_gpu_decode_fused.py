@@ -113,6 +113,7 @@ def test_fused_single_token(dtype, nk, nv):
     (2, 4, [4, 1, 0, 4, 2, 4, 3]),      # 1 + 3 draft tokens, ragged, one empty sequence
     (1, 4, [4, 4, 1]),
     (2, 2, [3, 0, 4, 5]),
+    (1, 2, [70, 130, 1, 64, 65]),       # the gating is formed 64 tokens at a time: block edges
 ])
 def test_fused_multi_token(dtype, nk, nv, lengths):
     _say("fused decode, several tokens per sequence", dtype, nk, nv, lengths)
