@@ -464,15 +464,16 @@ constexpr int EPI_SPIN = 1 << 20;
 // CV: q is the conv input x (channel 0 of the packed q | k | v) with token
 // stride qs; k and ks are unused. The K and Q tiles are then the conv + SiLU
 // outputs, rounded to bf16 as a stored conv output would be.
-template <typename TIn, int GM, bool CV>
-__global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_per_eu(4))) chunk_prep_kernel(
+template <typename TIn, int GM, bool CV, bool RG>
+__global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_per_eu(RG ? 3 : 4))) chunk_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, int64_t qs, int64_t ks,
     const void* __restrict__ ga, const void* __restrict__ gb, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, const int32_t* __restrict__ cu,
     int n_seqs, int64_t T, int nk, int nv, float scale, int l2, const int32_t* __restrict__ chunk_off,
     float* __restrict__ tp, float4* __restrict__ sc, float* __restrict__ egc, uint16_t* __restrict__ kf,
-    uint16_t* __restrict__ qf, ConvIn cv) {
+    uint16_t* __restrict__ qf, ConvIn cv, int hg_arg) {
   constexpr bool BF = sizeof(TIn) == 2;
+  const int hg = RG ? hg_arg : 1;
   constexpr int EP = prep_pitch<TIn>();
   constexpr size_t tiles = 2 * CH * EP * sizeof(TIn);
   constexpr size_t at = 2 * CH * AP * sizeof(float);
@@ -489,13 +490,17 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   float* rq_s = rk_s + CH;
   float* b_s = rq_s + CH;
 
-  // heads vary fastest: the value heads of one key head, and the per-token
-  // g and beta of all heads (one cache line per token), are read by
-  // neighbouring workgroups
-  // one-dimensional grid (its y dimension would cap the chunk count at 65536)
-  const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(nv));
-  const int c = static_cast<int>(blockIdx.x / static_cast<unsigned>(nv));
-  const int hk = h / (nv / nk);
+  // !RG: one workgroup per (chunk, value head), heads fastest (the value
+  // heads of one key head, and the per-token g and beta of all heads, are
+  // read by neighbouring workgroups); RG (hg = nv / nk): one workgroup per
+  // (chunk, key head), which forms the K and Q tiles (and their conv), the
+  // Grams and the norms once and then runs steps 5-9 for each of the key
+  // head's value heads in turn. One-dimensional grid (its y dimension would
+  // cap the chunk count at 65536).
+  const int nh = nv / hg;   // workgroups per chunk
+  const int h0 = static_cast<int>(blockIdx.x % static_cast<unsigned>(nh)) * hg;
+  const int c = static_cast<int>(blockIdx.x / static_cast<unsigned>(nh));
+  const int hk = h0 / (nv / nk);
   const int total = cu ? chunk_off[n_seqs] : static_cast<int>((T + CH - 1) / CH);
   if (c >= total) return;
   const int n = cu ? find_le(chunk_off, n_seqs, c) : 0;
@@ -508,9 +513,9 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   // per-token gating inputs (wave 0, lane = token), issued first so their
   // latency overlaps the tile loads and the Grams
   using TA = std::conditional_t<GM == 1, uint16_t, float>;
-  const int64_t gi = (t0 + min(lane, L - 1)) * nv + h;
-  const TA ga_ld = static_cast<const TA*>(ga)[gi];
-  const TA gb_ld = static_cast<const TA*>(gb)[gi];
+  const int64_t gi0 = (t0 + min(lane, L - 1)) * nv + h0;
+  TA ga_ld = static_cast<const TA*>(ga)[gi0];
+  TA gb_ld = static_cast<const TA*>(gb)[gi0];
 
   // 1. K and Q tiles into LDS; rows past the sequence end re-read the last
   //    valid row (or are zero after the conv): their norms are forced to 0
@@ -608,10 +613,10 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   //     per key head: K by its first value head, Q by its last; wave wv
   //     writes token tile wv
   if constexpr (BF) {
-    const int r = nv / nk, rho = h % r;
+    const int r = nv / nk, rho = h0 % r;
     const size_t kt = (static_cast<size_t>(c) * nk + hk) * TILE_ELEMS;
     if (rho == 0) write_row_blocks<EP>(Ks, L, kf + kt, lane, wv);
-    if (rho == r - 1) write_row_blocks<EP>(Qs, L, qf + kt, lane, wv);
+    if (rho + hg - 1 == r - 1) write_row_blocks<EP>(Qs, L, qf + kt, lane, wv);
   }
   // 4. |k_i|^2 and |q_i|^2 from the Gram diagonals (pairs 0, 2, 5, 9)
 #pragma unroll
@@ -624,6 +629,16 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
       const float skk = gkk[u][lr - 4 * lg], sqq = gqq[u][lr - 4 * lg];
       rk_s[row] = row < L ? (l2 ? rsqrtf(skk + kEps) : 1.0f) : 0.0f;
       rq_s[row] = row < L ? (l2 ? rsqrtf(sqq + kEps) : 1.0f) : 0.0f;
+    }
+  }
+  for (int hh = 0; hh < hg; ++hh) {
+  const int h = h0 + hh;
+  if (hh > 0) {
+    __syncthreads();   // the previous head's Aw, Tw, Gs and b_s are read
+    if (wv == 0) {
+      const int64_t gi = (t0 + min(lane, L - 1)) * nv + h;
+      ga_ld = static_cast<const TA*>(ga)[gi];
+      gb_ld = static_cast<const TA*>(gb)[gi];
     }
   }
   // 5. chunk-local cumulative decay in fp64 (wave 0, lane = token)
@@ -648,9 +663,10 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
   }
   __syncthreads();   // norms, G, beta visible; K/Q tiles no longer read
 
-  // 6. A (into LDS) and P (kept in registers, in place of the QK^T Gram);
-  //    per-token values are read before the first write to Aw (which could
-  //    alias them as far as the compiler knows)
+  // 6. A (into LDS) and P (kept in registers, the QK^T Gram kept for the
+  //    next head); per-token values are read before the first write to Aw
+  //    (which could alias them as far as the compiler knows)
+  f32x4 pq[NP];
   {
     double Gc[NP], Gr[NP][4];
     float rkc[NP], ar[NP][4], pr[NP][4];
@@ -679,7 +695,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
         const int i = 16 * mi + 4 * lg + ii;
         const float dec = (j <= i) ? exp_nonpos(Gr[u][ii] - Gc[u]) : 0.0f;
         Aw[i * AP + j] = (j < i) ? ar[u][ii] * rkc[u] * dec * gkk[u][ii] : 0.0f;
-        gqk[u][ii] = (j <= i) ? pr[u][ii] * rkc[u] * dec * gqk[u][ii] : 0.0f;
+        pq[u][ii] = (j <= i) ? pr[u][ii] * rkc[u] * dec * gqk[u][ii] : 0.0f;
       }
     }
   }
@@ -734,7 +750,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = 16 * mi + 4 * lg + ii;
-      if (j <= i) Tw[(63 - i) * AP + (63 - j)] = gqk[u][ii];
+      if (j <= i) Tw[(63 - i) * AP + (63 - j)] = pq[u][ii];
     }
   }
   __syncthreads();
@@ -767,6 +783,7 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) __attribute__((amdgpu_waves_p
     }
     if (lane == 0) egc[tile] = expf(static_cast<float>(GC));
   }
+  }   // value heads
 }
 
 // Workgroup -> (unit = sequence slot x nv + value head, 16-column slice) for
@@ -2394,6 +2411,17 @@ bool use_wide_state(int64_t slices) {
   return slices > static_cast<int64_t>(device_cus());
 }
 
+// Value heads per prep workgroup: all of a key head's (r) when a launch has
+// at least 4096 (chunk, key head) items, so that the grid still fills the
+// CUs many times over; else one. Grouped, the K and Q tiles (and their conv),
+// the Grams and the norms are formed once per key head. GDN_PREP_GROUP=0|1
+// in the environment forces either; both give the same bits.
+int prep_heads_per_group(int64_t nch, int nk, int nv) {
+  const int r = nv / nk;
+  if (const char* f = std::getenv("GDN_PREP_GROUP")) return std::atoi(f) ? r : 1;
+  return nch * nk >= 4096 ? r : 1;
+}
+
 // Segments of the segment-parallel prefill for this call (1 = not split).
 // The split triples the recurrence work (pass 1 forms a local state and a
 // transition per segment and 16-column slice, pass 2 reruns the segment), so
@@ -2454,18 +2482,24 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
     if (e != hipSuccess) return e;
   }
   {
-    auto kern = gm == 1 ? chunk_prep_kernel<TIn, 1, false>
-                : gm == 2 ? chunk_prep_kernel<TIn, 2, false> : chunk_prep_kernel<TIn, 0, false>;
+    const int hg = prep_heads_per_group(static_cast<int64_t>(nch), nk, nv);
+    auto kern = gm == 1 ? chunk_prep_kernel<TIn, 1, false, false>
+                : gm == 2 ? chunk_prep_kernel<TIn, 2, false, false> : chunk_prep_kernel<TIn, 0, false, false>;
+    if (hg > 1)
+      kern = gm == 1 ? chunk_prep_kernel<TIn, 1, false, true>
+             : gm == 2 ? chunk_prep_kernel<TIn, 2, false, true> : chunk_prep_kernel<TIn, 0, false, true>;
     if constexpr (BF) {
-      if (cvp) kern = gm == 1 ? chunk_prep_kernel<TIn, 1, true> : chunk_prep_kernel<TIn, 2, true>;
+      if (cvp)
+        kern = hg > 1 ? (gm == 1 ? chunk_prep_kernel<TIn, 1, true, true> : chunk_prep_kernel<TIn, 2, true, true>)
+                      : (gm == 1 ? chunk_prep_kernel<TIn, 1, true, false> : chunk_prep_kernel<TIn, 2, true, false>);
     }
     const size_t lds = prep_lds_bytes<TIn>();
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    kern<<<dim3(static_cast<unsigned>(nv * nch)), 64 * PREP_WAVES, lds, s>>>(
+    kern<<<dim3(static_cast<unsigned>((nv / hg) * nch)), 64 * PREP_WAVES, lds, s>>>(
         static_cast<const TIn*>(q), static_cast<const TIn*>(k), qs, ks, ga, gb, A_log, dt_bias, cu, n_seqs, T, nk, nv,
-        scale, l2, chunk_off, tp, sc, egc, kf, qf, cv);
+        scale, l2, chunk_off, tp, sc, egc, kf, qf, cv, hg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
