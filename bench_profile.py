@@ -46,7 +46,7 @@ BENCH_ARGS = ["--steps", "200", "--warmup", "100", "--skip-cpu-baseline", "--ski
 COPY_BYTES = 1 << 30
 KERNELS = {  # what one call of each measured entry point launches (bf16 in, fp32 out); the
     # chunk table kernel runs only with cu_seqlens, so it is counted when present
-    "chunk": ["chunk_offsets_kernel?", "chunk_prep_kernel<unsigned short, 1, false>",
+    "chunk": ["chunk_offsets_kernel?", "chunk_prep_kernel<unsigned short, 1, false, false>",
               "chunk_state_bf16_kernel<float, false, false>"],
     "recurrent": ["recurrent_kernel<unsigned short, float"],
     "fused": ["decode_fused_kernel<unsigned short, float"],
