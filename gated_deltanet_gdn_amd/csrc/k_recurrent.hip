@@ -190,13 +190,94 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], float& E, const f
   }
   E = uni(keep ? En : 1.0f);
 }
+// The direct forms, for launches of one token per sequence (no cu_seqlens):
+// k and q in LDS in natural row order, scaled by the norms row by row, and
+// S' = e S + k_hat delta^T in place (one multiply and one fma per element;
+// with a single token the scaled state saves nothing, and these measured
+// faster there).
+__device__ __forceinline__ RecNorms rec_pass_direct(const float (&S)[RPT][4], const float* ks, const float* qs, float* red,
+                                             int t256, float scale, int l2) {
+  const int lane = t256 & 63, wave = t256 >> 6, cg = t256 % CGN, rg = t256 / CGN;
+  // norms and k.q, redundantly per wave (no extra barrier)
+  const float k0 = ks[2 * lane], k1 = ks[2 * lane + 1];
+  const float q0 = qs[2 * lane], q1 = qs[2 * lane + 1];
+  const float skk = wave_sum(k0 * k0 + k1 * k1);
+  const float sqq = wave_sum(q0 * q0 + q1 * q1);
+  const float sqk = wave_sum(q0 * k0 + q1 * k1);
+  const float rk = l2 ? 1.0f / sqrtf(skk + 1e-6f) : 1.0f;
+  const float rq = (l2 ? 1.0f / sqrtf(sqq + 1e-6f) : 1.0f) * scale;
+  const float kq = sqk * rk * rq;
+
+  float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float kh = ks[rg + RGN * i] * rk;
+    const float qh = qs[rg + RGN * i] * rq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pa[c] = fmaf(S[i][c], kh, pa[c]);
+      pb[c] = fmaf(S[i][c], qh, pb[c]);
+    }
+  }
+  // the two row groups of a wave sit in lanes l and l ^ 32
+#pragma unroll
+  for (int x = CGN; x < 64; x <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pa[c] += __shfl_xor(pa[c], x, 64);
+      pb[c] += __shfl_xor(pb[c], x, 64);
+    }
+  }
+  if (lane < CGN) {
+    *reinterpret_cast<float4*>(red + (wave * 2 + 0) * D + 4 * cg) = make_float4(pa[0], pa[1], pa[2], pa[3]);
+    *reinterpret_cast<float4*>(red + (wave * 2 + 1) * D + 4 * cg) = make_float4(pb[0], pb[1], pb[2], pb[3]);
+  }
+  return {rk, rq, kq};
+}
+template <typename TO>
+__device__ __forceinline__ void rec_finish_direct(float (&S)[RPT][4], const float* ks, const float (&vv)[4], float gt,
+                                           float bt, const float* red, int t256, RecNorms nr, TO* __restrict__ o,
+                                           int64_t ob) {
+  const int cg = t256 % CGN, rg = t256 / CGN;
+  const float rk = nr.rk, kq = nr.kq;
+  const float e = expf(gt);
+  float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float4 ra = *reinterpret_cast<const float4*>(red + (w * 2 + 0) * D + 4 * cg);
+    const float4 rb = *reinterpret_cast<const float4*>(red + (w * 2 + 1) * D + 4 * cg);
+    a4[0] += ra.x; a4[1] += ra.y; a4[2] += ra.z; a4[3] += ra.w;
+    b4[0] += rb.x; b4[1] += rb.y; b4[2] += rb.z; b4[3] += rb.w;
+  }
+  float dl[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) dl[c] = bt * (vv[c] - e * a4[c]);
+  if (rg == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Elem<TO>::store(o, ob + c, fmaf(e, b4[c], kq * dl[c]));
+  }
+  // (k re-read from LDS rather than held across the barrier: fewer VGPRs,
+  // one more workgroup per CU)
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float kh = ks[rg + RGN * i] * rk;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[i][c] = fmaf(e, S[i][c], kh * dl[c]);
+  }
+}
 template <typename TO, bool DEFER>
 __device__ __forceinline__ void rec_token(float (&S)[RPT][4], float& E, const float* ks, const float* qs,
                                           const float (&vv)[4], float gt, float bt, float* red, int t256, float scale,
                                           int l2, TO* __restrict__ o, int64_t ob) {
-  const RecNorms nr = rec_pass(S, ks, qs, red, t256, scale, l2);
-  __syncthreads();
-  rec_finish<TO, DEFER>(S, E, ks, vv, gt, bt, red, t256, nr, o, ob);
+  if constexpr (DEFER) {
+    const RecNorms nr = rec_pass(S, ks, qs, red, t256, scale, l2);
+    __syncthreads();
+    rec_finish<TO, DEFER>(S, E, ks, vv, gt, bt, red, t256, nr, o, ob);
+  } else {
+    const RecNorms nr = rec_pass_direct(S, ks, qs, red, t256, scale, l2);
+    __syncthreads();
+    rec_finish_direct<TO>(S, ks, vv, gt, bt, red, t256, nr, o, ob);
+  }
 }
 
 // G consecutive (sequence, value head) states per workgroup, 256 threads
@@ -259,13 +340,13 @@ recurrent_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   float E = 1.0f;   // S = E St (see kStateScaleMin)
   int par = 0;
   for (int64_t t = t0; t < t1; ++t, par ^= 1) {
-    const float kqv = Elem<TIn>::cvt(kq_n), gt = uni(gt_n), bt = uni(bt_n);
+    const float kqv = Elem<TIn>::cvt(kq_n), gt = DEFER ? uni(gt_n) : gt_n, bt = DEFER ? uni(bt_n) : bt_n;
     float vv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) vv[c] = Elem<TIn>::cvt(vv_n[c]);
     if (t + 1 < t1) load_token(t + 1);   // the next token's inputs
     // stage k and q of this token's key head in LDS (fp32)
-    kq_s[par][rho][t256 < D ? 0 : 1][kq_slot(t256 & (D - 1))] = kqv;
+    kq_s[par][rho][t256 < D ? 0 : 1][DEFER ? kq_slot(t256 & (D - 1)) : t256 & (D - 1)] = kqv;
     __syncthreads();
     rec_token<TO, DEFER>(S, E, kq_s[par][rho][0], kq_s[par][rho][1], vv, gt, bt, &red[par][rho][0][0][0], t256, scale, l2,
                   o, t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
@@ -370,7 +451,7 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
 #pragma unroll
         for (int i = 0; i < KW - 1; ++i) acc = fmaf(cw[c * KW + i], hist[u][i], acc);
         acc = fmaf(cw[c * KW + KW - 1], xv, acc);
-        kqv_s[buf][j < 2 * D ? (j & ~(D - 1)) + kq_slot(j & (D - 1)) : j] = act_round(siluf_(acc), T{});
+        kqv_s[buf][DEFER && j < 2 * D ? (j & ~(D - 1)) + kq_slot(j & (D - 1)) : j] = act_round(siluf_(acc), T{});
 #pragma unroll
         for (int i = 0; i + 1 < KW - 1; ++i) hist[u][i] = hist[u][i + 1];
         hist[u][KW - 2] = xv;
@@ -389,17 +470,29 @@ decode_fused_kernel(const T* __restrict__ x, int64_t xs, T* __restrict__ cst, in
     // gating, as the separate gating kernel computes it
     const float av = Elem<T>::cvt(a_n), bv = Elem<T>::cvt(b_n);
     if (t + 1 < t1) { a_n = a[(t + 1) * nv + h]; b_n = b[(t + 1) * nv + h]; }
-    const float gt = uni(-exp_(alog) * softplusf_(av + dtb));
-    const float bt = uni(sigmoidf_(bv));
+    float gt = -exp_(alog) * softplusf_(av + dtb);
+    float bt = sigmoidf_(bv);
+    if constexpr (DEFER) {   // wave-uniform: scalar registers
+      gt = uni(gt);
+      bt = uni(bt);
+    }
     float* rd = &red[par][rho][0][0][0];
-    const RecNorms nr = rec_pass(S, &kqv_s[buf][D], &kqv_s[buf][0], rd, t256, scale, l2);
+    RecNorms nr;
+    if constexpr (DEFER)
+      nr = rec_pass(S, &kqv_s[buf][D], &kqv_s[buf][0], rd, t256, scale, l2);
+    else
+      nr = rec_pass_direct(S, &kqv_s[buf][D], &kqv_s[buf][0], rd, t256, scale, l2);
     const int nbuf = buf == 2 ? 0 : buf + 1;
     if (t + 1 < t1) conv_token(t + 1, nbuf);
     __syncthreads();
     const float4 v4 = *reinterpret_cast<const float4*>(&kqv_s[buf][2 * D + rho * D + col]);
     const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-    rec_finish<TO, DEFER>(S, E, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
-                   t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
+    if constexpr (DEFER)
+      rec_finish<TO, DEFER>(S, E, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
+                            t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
+    else
+      rec_finish_direct<TO>(S, &kqv_s[buf][D], vv, gt, bt, rd, t256, nr, o,
+                            t * static_cast<int64_t>(nv) * D + static_cast<int64_t>(h) * D + col);
     if constexpr (SNAP) {   // the state after this token, for rolling back rejected draft tokens
       // (buffer stores off one per-lane offset: the row addresses are not kept live)
       const rsrc_t rs = make_rsrc(snap + (t * nv + h) * static_cast<int64_t>(D) * D, D * D * 4);
