@@ -1466,7 +1466,9 @@ __global__ void __launch_bounds__(CV ? 512 : 256) chunk_state_wide_kernel(
   __shared__ __attribute__((aligned(16))) float SCS[2][4 * CH];   // planes a | b | c | beta
   __shared__ float EGS[2];               // exp(G_C)
   // epilogue: o of the last EPI_LAG + 1 chunks, [chunk % 3][token][the pair's 32 columns]
-  __shared__ __attribute__((aligned(16))) float ORX[EPI ? EPI_LAG + 1 : 1][EPI ? CH : 1][EPI ? 32 : 4];
+  // (rows padded to 36 floats: a 32-float pitch put the 16 rows an output
+  // wave writes at once on the same banks)
+  __shared__ __attribute__((aligned(16))) float ORX[EPI ? EPI_LAG + 1 : 1][EPI ? CH : 1][EPI ? 36 : 4];
 
   int slot, pair;
   wide_unit_pair(blockIdx.x, gridDim.x / 4, nv / nk, slot, pair);
