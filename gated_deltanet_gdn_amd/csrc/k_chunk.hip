@@ -2576,8 +2576,13 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
           void* args[] = {&a_v,   &a_vs,  &a_cu,    &a_n,  &a_T,  &a_nk, &a_nv, &a_off, &a_xf, &a_scp,
                           &a_egc, &a_kf,  &a_qf,    &a_order, &a_S0, &a_ST, &a_o, &a_cv, &a_ep};
           e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(wgrid), dim3(512), args, 0, s);
-          if (e == hipSuccess && normalized) *normalized = true;
-          return e;
+          if (e == hipSuccess) {
+            if (normalized) *normalized = true;
+            return e;
+          }
+          // refused (for instance under stream capture, or the device is
+          // shared): the plain launch below, and the caller normalizes
+          (void)hipGetLastError();
         }
       }
       auto launch_wide = [&](auto kern, auto* optr) {   // eight waves with the conv (conv waves), else four

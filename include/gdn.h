@@ -234,8 +234,13 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride,
  * workgroups fit the device at once, the norm runs inside the state kernel: o
  * never leaves the CU, and the four workgroups that hold a row's 128 columns
  * exchange their partial sums of squares through a small ring in the
- * workspace. Otherwise o is written to y and normalized there by a second
- * launch. The two routes differ by the order of the sum of squares only.
+ * workspace (a cooperative launch; each wait for a partner is bounded, and a
+ * row whose partners never arrive would come out NaN rather than hang).
+ * Otherwise (the four-wave form, a segment-parallel split, or a cooperative
+ * launch the runtime refuses, as under stream capture) o is written to y and
+ * normalized there by a second launch. The two routes differ by the order of
+ * the sum of squares only. Calls on one stream are ordered; concurrent calls
+ * on different streams need different workspaces, as for every call here.
  */
 int gdn_prefill_fused_norm(const void* x, int dtype, int64_t x_tok_stride,
                            const float* conv_weight, const float* conv_bias, int K,
