@@ -2580,8 +2580,7 @@ hipError_t chunk_dispatch(const void* q, const void* k, const void* v, int64_t q
             if (normalized) *normalized = true;
             return e;
           }
-          // refused (for instance under stream capture, or the device is
-          // shared): the plain launch below, and the caller normalizes
+          // refused: the plain launch below, and the caller normalizes
           (void)hipGetLastError();
         }
       }

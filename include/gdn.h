@@ -237,7 +237,7 @@ int gdn_prefill_fused(const void* x, int dtype, int64_t x_tok_stride,
  * workspace (a cooperative launch; each wait for a partner is bounded, and a
  * row whose partners never arrive would come out NaN rather than hang).
  * Otherwise (the four-wave form, a segment-parallel split, or a cooperative
- * launch the runtime refuses, as under stream capture) o is written to y and
+ * launch the runtime refuses) o is written to y and
  * normalized there by a second launch. The two routes differ by the order of
  * the sum of squares only. Calls on one stream are ordered; concurrent calls
  * on different streams need different workspaces, as for every call here.
