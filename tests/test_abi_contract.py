@@ -308,6 +308,36 @@ def test_prefill_fused_argument_errors(L, kw, status):
     assert gdn.gdn_last_error() != ""
 
 
+def _prefill_norm(L, **kw):
+    a = dict(x=P, dtype=1, xs=0, cw=P, cb=NULL, K=4, csi=NULL, cso=NULL, sl=3, a=P, b=P, ab_dtype=1, alog=P, dtb=P,
+             cu=NULL, n=1, T=256, nk=1, nv=2, dk=128, dv=128, scale=0.0, l2=1, s0=NULL, st=NULL, z=P, z_dtype=1,
+             nw=P, eps=1e-6, y=P, ws=P2, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return L.gdn_prefill_fused_norm(a["x"], a["dtype"], a["xs"], a["cw"], a["cb"], a["K"], a["csi"], a["cso"],
+                                    a["sl"], a["a"], a["b"], a["ab_dtype"], a["alog"], a["dtb"], a["cu"], a["n"],
+                                    a["T"], a["nk"], a["nv"], a["dk"], a["dv"], a["scale"], a["l2"], a["s0"],
+                                    a["st"], a["z"], a["z_dtype"], a["nw"], a["eps"], a["y"], a["ws"],
+                                    a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z_dtype=0), UNSUPPORTED),        # only bf16 z is built
+    (dict(z_dtype=7), INVALID),
+    (dict(z=NULL), INVALID),
+    (dict(z=MIS), UNSUPPORTED),
+    (dict(nw=NULL), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(y=NULL), INVALID),
+    (dict(dtype=0), UNSUPPORTED),          # the fused prefill's own checks apply as well
+    (dict(ws_bytes=16), WS_SMALL),
+    (dict(nk=3, nv=4), INVALID),
+])
+def test_prefill_fused_norm_argument_errors(L, kw, status):
+    assert _prefill_norm(L, **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
 def _declared_arg_counts():
     """Number of parameters of every function declared in gdn.h (comments stripped)."""
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
