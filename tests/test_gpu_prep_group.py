@@ -99,3 +99,33 @@ def test_grouped_prep_full_varlen_workload():
     (o0, s0), (o1, s1) = _both(run)
     _same(o1, o0, "o")
     _same(s1, s0, "final state")
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["chunk", "fused_prefill"])
+def test_grouped_prep_under_a_segment_split(fused):
+    """One sequence with few heads split into segments (GDN_SEGMENTS=3; the preparation then runs over the
+    segment table): grouped and per-head preparation give the same bits."""
+    old = os.environ.get("GDN_SEGMENTS")
+    os.environ["GDN_SEGMENTS"] = "3"
+    try:
+        if fused:
+            c = dict(name="segments_fused", T=5000, nk=1, nv=4, bias=True, conv_state=True, s0=True)
+            _say("prep grouping under segments", c)
+            d = PF._inputs(c, 970)
+            (o0, s0, cs0), (o1, s1, cs1) = _both(lambda: PF._fused(d, c["nk"], c["nv"]))
+            _same(cs1, cs0, "conv state out")
+        else:
+            _say("prep grouping under segments, chunk call, T=5000, 1->4 heads")
+            wl = W.Workload("t", 971, "chunk", "bf16", nk=1, nv=4, s0_std=0.3)
+            x = W.chunk_inputs(wl, lengths=[5000])
+            d = {k: (v.to(dev()) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+            run = lambda: gdn.gdn_chunk_fwd_gated(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                                  initial_state=d["S0"])
+            (o0, s0), (o1, s1) = _both(run)
+        _same(o1, o0, "o")
+        _same(s1, s0, "final state")
+    finally:
+        if old is None:
+            del os.environ["GDN_SEGMENTS"]
+        else:
+            os.environ["GDN_SEGMENTS"] = old
