@@ -171,3 +171,30 @@ def test_fused_norm_rejects_bad_arguments():
     with pytest.raises(gdn.GdnError):
         gdn.gdn_prefill_fused_norm(d["x"], d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], 2, 4,
                                    d["z"], d["norm_w"], eps=-1.0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fused_norm_random_shapes(seed):
+    """Seeded random shapes (sequence count and lengths, head grouping, conv history and bias, initial state,
+    gating dtype, x stride, state form): the final state and conv state bit for bit, y within the bound."""
+    import numpy as np
+    rng = np.random.RandomState(4000 + seed)
+    nk = int(rng.choice([1, 2]))
+    c = dict(name=f"random_{seed}", lengths=[int(v) for v in rng.randint(0, 260, size=int(rng.randint(1, 5)))],
+             nk=nk, nv=nk * int(rng.choice([1, 2, 4])), bias=bool(rng.randint(0, 2)),
+             conv_state=bool(rng.randint(0, 2)), s0=bool(rng.randint(0, 2)), ab=["bf16", "f32"][int(rng.randint(0, 2))],
+             pad=int(rng.choice([0, 8, 64])), state_len=int(rng.choice([3, 4])))
+    form = ["wide", "narrow"][seed % 2]
+    _say("prefill_fused_norm random", form, c)
+    d = _norm_inputs(c, 700 + seed)
+    with _Form(form):
+        y_r, st_r, cs_r = _reference(d, c["nk"], c["nv"])
+        y, st, cs = _fused_norm(d, c["nk"], c["nv"])
+    torch.cuda.synchronize()
+    PF._same(st, st_r, "final state")
+    if cs_r is not None:
+        PF._same(cs, cs_r, "conv state out")
+    if form == "narrow":
+        PF._same(y, y_r, "y")
+    else:
+        _close(y, y_r, "y")
