@@ -14,6 +14,8 @@ with tracing:
   6-8. --kernel-trace --stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE of
        bench.py --mtp-only: the 1 + 3 token fused decode step on its own (its
        kernel is the single-token step's, so it needs runs of its own)
+  9. --pmc TCP_TCC_READ_REQ_sum TCC_HIT_sum TCC_MISS_sum   L2 -> L1 read requests
+       (bytes per request from the copy, which reads each byte once) and L2 hits
 The copy gives the calibration factors: true bytes / counter reading for a
 copy of known size, applied to every kernel's reading.
 
@@ -67,6 +69,7 @@ PASSES = [  # name, rocprofv3 arguments
     ("mtp_ktrace", ["--kernel-trace", "--stats"]),   # bench.py --mtp-only
     ("mtp_fetch", ["--pmc", "FETCH_SIZE"]),
     ("mtp_write", ["--pmc", "WRITE_SIZE"]),
+    ("l2l1", ["--pmc", "TCP_TCC_READ_REQ_sum", "TCC_HIT_sum", "TCC_MISS_sum"]),   # L2 -> L1 reads, L2 hits
 ]
 ROWS_SUMMARY = os.path.join(ROOT, "profiles", "rows_long_prefill_t256k_decode_256seq_kernel_stats.md")
 
@@ -157,6 +160,24 @@ def summarize_rows(out):
     print("[profile] wrote", ROWS_SUMMARY, flush=True)
 
 
+def l2l1_lines(out):
+    """L2 -> L1 read traffic of the chunk call's kernels (the operand stream of the state kernel)."""
+    d = os.path.join(out, "l2l1")
+    if not os.path.isdir(d):
+        return []
+    c = counters(d)
+    copy_req = max(c[pick(c, "copyBuffer")]["TCP_TCC_READ_REQ_sum"])
+    bpr = COPY_BYTES / copy_req
+    lines = ["L2 -> L1 reads of the chunk call (one run: " + pass_command("l2l1", dict(PASSES)["l2l1"]) + "); the",
+             f"1 GiB copy made {copy_req:.0f} read requests, {bpr:.1f} bytes each:", "",
+             "| kernel | L2 -> L1 read requests | L2 -> L1 bytes | L2 hit rate |", "|---|---|---|---|"]
+    for k in launched(c, KERNELS["chunk"]):
+        r = c[pick(c, k)]
+        req, hit, miss = avg(r["TCP_TCC_READ_REQ_sum"]), avg(r["TCC_HIT_sum"]), avg(r["TCC_MISS_sum"])
+        lines.append(f"| `{k}` | {req:.3e} | {req * bpr / 1e6:.1f} MB | {100 * hit / max(1.0, hit + miss):.1f} % |")
+    return lines + [""]
+
+
 def summarize(out):
     d1, d2, d3, d4 = (os.path.join(out, n) for n, _ in PASSES[:4])
     cmd1, cmd2, cmd3, cmd4 = (pass_command(n, a) for n, a in PASSES[:4])
@@ -238,6 +259,7 @@ def summarize(out):
              f"(algorithmic {bench.fused_decode_bytes(1024, 256, 16, 32) / 1e6:.1f} MB); kernel trace average "
              f"{mtp_avg:.1f} us ({cmd_m[0]}), events {bm['roofline']['avg_ms'] * 1e3:.1f} us, "
              f"{100 * bm['roofline']['frac']:.1f} % of HBM peak", "",
+             *l2l1_lines(out),
              "Source hashes are of the kernel sources the counters were taken on; bench.py reports traffic",
              "only while they match.", "",
              "traffic_json: " + json.dumps(rec), ""]
