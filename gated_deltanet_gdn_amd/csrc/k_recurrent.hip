@@ -91,8 +91,10 @@ __device__ __forceinline__ RecNorms rec_pass(const float (&S)[RPT][4], const flo
   const float skk = wave_sum(k0 * k0 + k1 * k1);
   const float sqq = wave_sum(q0 * q0 + q1 * q1);
   const float sqk = wave_sum(q0 * k0 + q1 * k1);
-  const float rk = uni(l2 ? 1.0f / sqrtf(skk + 1e-6f) : 1.0f);
-  const float rq = uni((l2 ? 1.0f / sqrtf(sqq + 1e-6f) : 1.0f) * scale);
+  // (hardware reciprocal square root, about 1 ulp: a correctly rounded
+  // 1 / sqrt costs some twenty VALU operations per token and wave)
+  const float rk = uni(l2 ? __builtin_amdgcn_rsqf(skk + 1e-6f) : 1.0f);
+  const float rq = uni((l2 ? __builtin_amdgcn_rsqf(sqq + 1e-6f) : 1.0f) * scale);
   const float kq = uni(sqk * rk * rq);
 
   float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -169,7 +171,7 @@ __device__ __forceinline__ void rec_finish(float (&S)[RPT][4], float& E, const f
   }
   const float En = uni(e * E);
   const bool keep = En >= kStateScaleMin;
-  const float f = uni(keep ? nr.rk / En : nr.rk);
+  const float f = uni(keep ? nr.rk * __builtin_amdgcn_rcpf(En) : nr.rk);   // En >= 2^-64: a normal number
   float d2[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) d2[c] = dl[c] * f;
